@@ -1,0 +1,124 @@
+"""CPU oracle (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and shares no code with it.
+
+The arithmetic lives in ``oracle.cpp`` (plain single-threaded C++, g++); this
+module only loads it and marshals numpy arrays.  See that file for the
+definitions and the passages of the pages they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+SUM, MAX, MIN = 0, 1, 2
+
+
+def compile_oracle(src: str, so_path: str) -> str:
+    """g++ -> shared library (no HIP involved)."""
+    tmp = so_path + ".tmp%d" % os.getpid()
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC",
+                           src, "-o", tmp])
+    os.replace(tmp, so_path)
+    return so_path
+
+
+def compile_oracle_source(text: str, so_path: str) -> str:
+    """Compile C++ source text (tests use this for planted-mistake copies)."""
+    src = so_path + ".cpp"
+    with open(src, "w") as f:
+        f.write(text)
+    return compile_oracle(src, so_path)
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.cpp into liboracle.so if it is missing (or force)."""
+    if force or not os.path.exists(_SO):
+        compile_oracle(os.path.join(_HERE, "oracle.cpp"), _SO)
+    return _SO
+
+
+class Oracle:
+    """ctypes view of one build of oracle.cpp (the default build, or a
+    deliberately mutated copy used by the tests to show the pins bite)."""
+
+    def __init__(self, so_path: str):
+        lib = ctypes.CDLL(so_path)
+        p = ctypes.c_void_p
+        lib.oracle_topk_i32.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p]
+        lib.oracle_topk_i32.restype = ctypes.c_int
+        lib.oracle_reduce_i32.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p]
+        lib.oracle_reduce_i32.restype = ctypes.c_int
+        lib.oracle_check_topk.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p]
+        lib.oracle_check_topk.restype = ctypes.c_int
+        self.lib = lib
+
+    def topk(self, x, k: int) -> np.ndarray:
+        """The k largest values of x, descending (sort-based definition)."""
+        a = _as_i32(x)
+        out = np.empty(max(k, 0), dtype=np.int32)
+        rc = self.lib.oracle_topk_i32(a.ctypes.data, a.size, k,
+                                      out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_topk_i32: invalid arguments (n=%d, k=%d)"
+                             % (a.size, k))
+        return out
+
+    def reduce(self, x, op: int) -> int:
+        """Sum (int64), max or min of x; the identity when x is empty."""
+        a = _as_i32(x)
+        out = np.zeros(1, dtype=np.int64)
+        rc = self.lib.oracle_reduce_i32(a.ctypes.data if a.size else None,
+                                        a.size, op, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_reduce_i32: invalid arguments (op=%d)"
+                             % op)
+        return int(out[0])
+
+    def check_topk(self, x, k: int, cand) -> int:
+        """0 if cand is exactly the descending top-k of x, else 1/2/3."""
+        a = _as_i32(x)
+        c = _as_i32(cand)
+        if c.size != k:
+            return 1
+        rc = self.lib.oracle_check_topk(a.ctypes.data, a.size, k,
+                                        c.ctypes.data)
+        if rc < 0:
+            raise ValueError("oracle_check_topk: invalid arguments")
+        return rc
+
+
+def _as_i32(x) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError("expected a 1-D array")
+    return a
+
+
+def default() -> Oracle:
+    global _lib
+    if _lib is None:
+        build()
+        _lib = Oracle(_SO)
+    return _lib
+
+
+def topk(x, k: int) -> np.ndarray:
+    return default().topk(x, k)
+
+
+def reduce(x, op: int) -> int:
+    return default().reduce(x, op)
+
+
+def check_topk(x, k: int, cand) -> int:
+    return default().check_topk(x, k, cand)

@@ -1,0 +1,157 @@
+/*
+ * CPU oracle for the two-stage reduction / Top-K path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP library, and it is plain single-threaded C++ built by
+ * g++.
+ *
+ * Sources (the pages the method is taken from):
+ *   [TopK]   "CUDA并行优化实战：从TopK问题剖析共享内存与规约算法设计"
+ *            (CUDA optimisation in practice: shared memory and reduction
+ *            design through the TopK problem).
+ *   [Reduce] "CUDA归约优化完全指南：从入门到精通"
+ *            (A complete guide to CUDA reduction optimisation).
+ *
+ * Every result here has a plain definition, so the oracle is that definition
+ * written out, with a library sort as its one primitive:
+ *
+ *   oracle_topk_i32   the k largest values of the input in descending order,
+ *                     duplicates kept with their multiplicity ([TopK] §1: the
+ *                     20 largest of 1e8 values; §2.1: each thread keeps its
+ *                     list in descending order and thread 0 writes the
+ *                     block's list out in that order; §2.2: the GPU result
+ *                     must be identical to the CPU's; §5.2: duplicate
+ *                     elements must be handled).  Definition: sort a copy
+ *                     ascending, read the last k backwards.
+ *
+ *   oracle_reduce_i32 folding the array with a binary operator ([Reduce],
+ *                     "Basic concepts": a reduction combines all elements
+ *                     with one binary operation into a single result; the
+ *                     worked example sums [1..8] to 36).  Sum is accumulated
+ *                     in int64 so that it cannot overflow for n <= 2^32
+ *                     (the page's own int accumulator would); max and min
+ *                     start from the int32 extremes and are returned
+ *                     sign-extended to int64.
+ *
+ *   oracle_check_topk a second, sort-free characterisation of the top-k
+ *                     multiset, linear in n.  It is used to check results
+ *                     at sizes where sorting is too slow, and as an
+ *                     independent pin for oracle_topk_i32.  A candidate o of
+ *                     length k is the top-k of `in` iff
+ *                       (1) o is non-increasing;
+ *                       (2) every value occurs in o at most as often as in
+ *                           `in`;
+ *                       (3) #{x in in : x > o[k-1]} == #{i : o[i] > o[k-1]}.
+ *                     (1)-(3) force o's elements above t = o[k-1] to be
+ *                     exactly the input's elements above t, and the rest of
+ *                     o to be copies of t that the input holds.
+ *
+ * Values are compared as signed int32 throughout.
+ */
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+extern "C" {
+
+/* Returns 0 on success, -1 on invalid arguments (null pointers, n < 0,
+ * k < 1, k > n).  out receives k values, largest first. */
+int oracle_topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out)
+{
+    if (!in || !out || n < 0 || k < 1 || (int64_t)k > n)
+        return -1;
+    std::vector<int32_t> v(in, in + n);
+    std::sort(v.begin(), v.end());
+    for (int32_t i = 0; i < k; ++i)
+        out[i] = v[(size_t)(n - 1 - i)];
+    return 0;
+}
+
+/* op: 0 = sum (int64), 1 = max, 2 = min.  n == 0 yields the operator's
+ * identity: 0, INT32_MIN, INT32_MAX.  Returns 0, or -1 on invalid
+ * arguments. */
+int oracle_reduce_i32(const int32_t *in, int64_t n, int32_t op, int64_t *out)
+{
+    if (!out || n < 0 || (n > 0 && !in) || op < 0 || op > 2)
+        return -1;
+    if (op == 0) {
+        int64_t s = 0;
+        for (int64_t i = 0; i < n; ++i)
+            s += (int64_t)in[i];
+        *out = s;
+    } else if (op == 1) {
+        int32_t m = INT32_MIN;
+        for (int64_t i = 0; i < n; ++i)
+            if (in[i] > m)
+                m = in[i];
+        *out = (int64_t)m;
+    } else {
+        int32_t m = INT32_MAX;
+        for (int64_t i = 0; i < n; ++i)
+            if (in[i] < m)
+                m = in[i];
+        *out = (int64_t)m;
+    }
+    return 0;
+}
+
+/* Returns 0 if cand[0..k) is exactly the top-k of in[0..n) in descending
+ * order; 1, 2 or 3 naming the first condition above that fails; -1 on
+ * invalid arguments. */
+int oracle_check_topk(const int32_t *in, int64_t n, int32_t k,
+                      const int32_t *cand)
+{
+    if (!in || !cand || n < 0 || k < 1 || (int64_t)k > n)
+        return -1;
+    for (int32_t i = 1; i < k; ++i)
+        if (cand[i] > cand[i - 1])
+            return 1;
+    const int32_t t = cand[k - 1];
+
+    /* distinct values of cand (already sorted descending) and their counts */
+    std::vector<int32_t> val;
+    std::vector<int64_t> want;
+    for (int32_t i = 0; i < k; ++i) {
+        if (val.empty() || val.back() != cand[i]) {
+            val.push_back(cand[i]);
+            want.push_back(0);
+        }
+        ++want.back();
+    }
+    std::vector<int64_t> have(val.size(), 0);
+
+    int64_t above_in = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        const int32_t x = in[j];
+        if (x < t)
+            continue;
+        if (x > t)
+            ++above_in;
+        /* val is descending: find x by binary search */
+        size_t lo = 0, hi = val.size();
+        while (lo < hi) {
+            size_t mid = (lo + hi) / 2;
+            if (val[mid] > x)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        if (lo < val.size() && val[lo] == x)
+            ++have[lo];
+    }
+    for (size_t d = 0; d < val.size(); ++d)
+        if (want[d] > have[d])
+            return 2;
+    int64_t above_cand = 0;
+    for (int32_t i = 0; i < k; ++i)
+        if (cand[i] > t)
+            ++above_cand;
+    if (above_in != above_cand)
+        return 3;
+    return 0;
+}
+
+} /* extern "C" */

@@ -1,0 +1,252 @@
+"""Pins for the CPU oracle, each independent of the oracle's own code.
+
+The oracle's top-k is "sort, take the last k backwards"; its reductions are
+plain loops.  The pins below come from elsewhere: the worked example printed
+on the reduction page, closed forms, exhaustive brute force with a different
+algorithm (repeated max extraction, Python big-int sums), invariants of the
+top-k multiset, and a sort-free linear characterisation.  The last test
+compiles deliberately broken copies of oracle.cpp and checks that the same
+battery rejects every one of them.
+"""
+import itertools
+import os
+import re
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import MAX, MIN, SUM
+
+I32_MIN = -(2 ** 31)
+I32_MAX = 2 ** 31 - 1
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def brute_topk(xs, k):
+    """Repeated max extraction (O(nk)); shares nothing with a sort."""
+    pool = list(xs)
+    out = []
+    for _ in range(k):
+        j = max(range(len(pool)), key=lambda i: pool[i])
+        out.append(pool.pop(j))
+    return out
+
+
+def read_kv(name):
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            d[key] = vals
+    return d
+
+
+# ---------------------------------------------------------------- battery
+def pin_worked_example(o):
+    g = read_kv("reduce_worked_example.txt")
+    xs = np.array([int(v) for v in g["input"]], dtype=np.int32)
+    assert g["op"] == ["sum"]
+    assert o.reduce(xs, SUM) == int(g["output"][0]) == 36
+    # closed forms of the same input
+    assert o.reduce(xs, MAX) == 8
+    assert o.reduce(xs, MIN) == 1
+    assert list(o.topk(xs, 3)) == [8, 7, 6]
+    assert list(o.topk(xs, 8)) == [8, 7, 6, 5, 4, 3, 2, 1]
+
+
+def pin_all_ones(o):
+    g = read_kv("reduce_all_ones_2p24.txt")
+    n = int(g["n"][0])
+    xs = np.full(n, int(g["value"][0]), dtype=np.int32)
+    assert o.reduce(xs, SUM) == int(g["sum"][0]) == n
+    assert o.reduce(xs, MAX) == int(g["max"][0])
+    assert o.reduce(xs, MIN) == int(g["min"][0])
+    assert list(o.topk(xs, 20)) == [1] * 20
+
+
+def pin_exhaustive_small(o):
+    alphabet = [I32_MIN, -1, 0, 1, I32_MAX]
+    for n in range(1, 6):
+        for xs in itertools.product(alphabet, repeat=n):
+            a = np.array(xs, dtype=np.int32)
+            assert o.reduce(a, SUM) == sum(xs)
+            assert o.reduce(a, MAX) == max(xs)
+            assert o.reduce(a, MIN) == min(xs)
+            for k in range(1, n + 1):
+                assert list(o.topk(a, k)) == brute_topk(xs, k), (xs, k)
+
+
+def pin_empty_identities(o):
+    e = np.zeros(0, dtype=np.int32)
+    assert o.reduce(e, SUM) == 0
+    assert o.reduce(e, MAX) == I32_MIN
+    assert o.reduce(e, MIN) == I32_MAX
+
+
+def pin_int64_sum(o):
+    # sums far outside int32: an int32 accumulator would wrap
+    for v, n in [(I32_MAX, 1000), (I32_MIN, 1000), (I32_MAX, 3)]:
+        a = np.full(n, v, dtype=np.int32)
+        assert o.reduce(a, SUM) == v * n
+    a = np.array([I32_MAX, 1], dtype=np.int32)
+    assert o.reduce(a, SUM) == 2 ** 31
+
+
+def pin_closed_forms(o, rng):
+    for n in [1, 2, 7, 100, 1000, 4099]:
+        perm = rng.permutation(n).astype(np.int32)
+        assert o.reduce(perm, SUM) == n * (n - 1) // 2
+        assert o.reduce(perm, MAX) == n - 1
+        assert o.reduce(perm, MIN) == 0
+        for k in sorted({1, min(n, 3), min(n, 20), n}):
+            assert list(o.topk(perm, k)) == list(range(n - 1, n - 1 - k, -1))
+    # symmetric range sums to zero; all-negative input exercises max's start
+    sym = np.arange(-5000, 5001, dtype=np.int32)
+    rng.shuffle(sym)
+    assert o.reduce(sym, SUM) == 0
+    neg = np.arange(-100, -1, dtype=np.int32)
+    assert o.reduce(neg, MAX) == -2
+    assert list(o.topk(neg, 3)) == [-2, -3, -4]
+    pos = np.arange(5, 100, dtype=np.int32)
+    assert o.reduce(pos, MIN) == 5
+    # ascending input -> last k reversed; all-equal -> k copies
+    asc = np.arange(-50, 50, dtype=np.int32)
+    assert list(o.topk(asc, 10)) == list(range(49, 39, -1))
+    eq = np.full(77, -9, dtype=np.int32)
+    assert list(o.topk(eq, 40)) == [-9] * 40
+
+
+def pin_invariants(o, rng):
+    for trial in range(40):
+        n = int(rng.integers(1, 3000))
+        hi = int(rng.choice([3, 50, 2 ** 31]))
+        a = rng.integers(-hi, hi, size=n, dtype=np.int64).astype(np.int32)
+        k = int(rng.integers(1, min(n, 130) + 1))
+        t = o.topk(a, k)
+        assert t.size == k
+        assert all(t[i] >= t[i + 1] for i in range(k - 1))
+        # multiset containment, with multiplicity
+        vals, cnt = np.unique(a, return_counts=True)
+        have = dict(zip(vals.tolist(), cnt.tolist()))
+        tv, tc = np.unique(t, return_counts=True)
+        for v, c in zip(tv.tolist(), tc.tolist()):
+            assert have.get(v, 0) >= c
+        # every excluded element is <= the k-th output
+        assert int((a > t[-1]).sum()) == int((t > t[-1]).sum())
+        # duplicates kept with multiplicity
+        assert int((t == t[-1]).sum()) == min(have[int(t[-1])],
+                                                k - int((t > t[-1]).sum()))
+        # cross-op identities
+        assert t[0] == o.reduce(a, MAX)
+        full = o.topk(a, n)
+        assert int(full.astype(np.int64).sum()) == o.reduce(a, SUM)
+        assert full[-1] == o.reduce(a, MIN)
+        # permutation invariance
+        b = a.copy()
+        rng.shuffle(b)
+        assert list(o.topk(b, k)) == list(t)
+        assert o.reduce(b, SUM) == o.reduce(a, SUM)
+        # the linear characterisation accepts the result
+        assert o.check_topk(a, k, t) == 0
+
+
+def pin_checker_rejects(o, rng):
+    a = rng.integers(-1000, 1000, size=5000).astype(np.int32)
+    a[:7] = 999  # plant duplicates at the top
+    k = 12
+    t = o.topk(a, k)
+    assert o.check_topk(a, k, t) == 0
+    bad = t.copy()
+    bad[[0, 5]] = bad[[5, 0]]
+    if bad[0] != t[0]:
+        assert o.check_topk(a, k, bad) == 1           # order broken
+    bad = t.copy()
+    bad[-1] = t[-1] - 1                               # a smaller value
+    assert o.check_topk(a, k, bad) != 0
+    bad = t.copy()
+    bad[0] = 1000                                     # value not in input
+    assert o.check_topk(a, k, bad) != 0
+    dup = np.array([5, 5, 5, 1, 0], dtype=np.int32)
+    assert o.check_topk(dup, 3, [5, 5, 5]) == 0
+    assert o.check_topk(dup, 3, [5, 5, 1]) == 3       # a duplicate dropped
+    assert o.check_topk(dup, 4, [5, 5, 5, 5]) == 2    # multiplicity exceeded
+    assert o.check_topk(dup, 2, [5, 1]) != 0
+
+
+BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
+           pin_empty_identities, pin_int64_sum, pin_closed_forms,
+           pin_invariants, pin_checker_rejects]
+
+
+def run_battery(o, seed=7):
+    for pin in BATTERY:
+        args = (o,) if pin.__code__.co_argcount == 1 else (
+            o, np.random.default_rng(seed))
+        pin(*args)
+
+
+# ---------------------------------------------------------------- tests
+@pytest.mark.parametrize("pin", BATTERY, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    o = oracle.default()
+    if pin.__code__.co_argcount == 1:
+        pin(o)
+    else:
+        pin(o, np.random.default_rng(7))
+
+
+def test_oracle_rejects_bad_arguments():
+    o = oracle.default()
+    a = np.arange(5, dtype=np.int32)
+    for k in (0, -1, 6):
+        with pytest.raises(ValueError):
+            o.topk(a, k)
+    with pytest.raises(ValueError):
+        o.reduce(a, 3)
+
+
+# Plausible mistakes, each planted in a private copy of oracle.cpp.  The
+# battery must reject every mutant; if one survived, the pins would not be
+# able to tell that mistake from the correct oracle.
+MUTANTS = {
+    "int32_sum_accumulator": (r"int64_t s = 0;", "int32_t s = 0;"),
+    "ascending_output": (r"out\[i\] = v\[\(size_t\)\(n - 1 - i\)\];",
+                         "out[i] = v[(size_t)i];"),
+    "duplicates_dropped": (
+        r"std::sort\(v.begin\(\), v.end\(\)\);",
+        "std::sort(v.begin(), v.end()); v.erase(std::unique(v.begin(), "
+        "v.end()), v.end()); v.insert(v.begin(), (size_t)n - v.size(), "
+        "INT32_MIN);"),
+    "max_starts_at_zero": (r"int32_t m = INT32_MIN;", "int32_t m = 0;"),
+    "min_starts_at_zero": (r"int32_t m = INT32_MAX;", "int32_t m = 0;"),
+    "sum_skips_last": (r"for \(int64_t i = 0; i < n; \+\+i\)\n            s \+=",
+                       "for (int64_t i = 0; i + 1 < n; ++i)\n            s +="),
+    "wrong_identity_sum": (r"int64_t s = 0;", "int64_t s = 1;"),
+    "checker_counts_ties_as_above": (r"if \(x > t\)\n            \+\+above_in;",
+                                     "if (x >= t)\n            ++above_in;"),
+    "checker_ignores_multiplicity": (r"if \(want\[d\] > have\[d\]\)",
+                                     "if (have[d] == 0)"),
+    "topk_off_by_one": (r"out\[i\] = v\[\(size_t\)\(n - 1 - i\)\];",
+                        "out[i] = v[(size_t)(n - 1 - (i > 0 ? i - 1 : 0))];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_battery_rejects_mutant(name, tmp_path):
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    src = open(os.path.join(os.path.dirname(oracle.__file__),
+                            "oracle.cpp")).read()
+    pat, rep = MUTANTS[name]
+    mutated, count = re.subn(pat, rep, src, count=1)
+    assert count == 1, "mutation pattern %s no longer matches" % name
+    so = oracle.compile_oracle_source(mutated, str(tmp_path / "mut.so"))
+    o = oracle.Oracle(so)
+    with pytest.raises(AssertionError):
+        run_battery(o)
