@@ -1,0 +1,142 @@
+/*
+ * libtopk — two-stage parallel reduction and Top-K selection over int32
+ * arrays on AMD Instinct MI355X (gfx950).  C ABI, no C++ or PyTorch types.
+ *
+ * Sources (the pages the method is taken from):
+ *   [TopK]   "CUDA并行优化实战：从TopK问题剖析共享内存与规约算法设计"
+ *            (CUDA optimisation in practice: shared memory and reduction
+ *            design through the TopK problem)
+ *   [Reduce] "CUDA归约优化完全指南：从入门到精通"
+ *            (A complete guide to CUDA reduction optimisation)
+ *
+ * Common conventions
+ * ------------------
+ *  - `in`, `out` and `out_i64` are DEVICE pointers on the calling thread's
+ *    current HIP device.  They are owned by the caller; the library never
+ *    frees or retains them.  `in` must be 4-byte aligned (16-byte alignment
+ *    takes the fastest path; otherwise up to three leading elements are
+ *    peeled).  `in` and the output must not overlap.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Both calls are
+ *    asynchronous and stream-ordered: they return once the work is enqueued
+ *    and never synchronise the host.  The result is valid once the stream
+ *    reaches the call; `in` must stay alive and unmodified until then.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is launched and the output is untouched.  Launch and
+ *    allocation failures are reported as LIBTOPK_ERR_HIP / _NOMEM; a fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - The library owns a small scratch area per (device, stream): 512 KiB of
+ *    per-block candidates plus a few KiB of counters.  It is allocated by the
+ *    first call on that pair (so do that first call before capturing the
+ *    stream into a HIP graph), kept for reuse, and freed by
+ *    libtopk_release() or at process exit.  Every call leaves it ready for
+ *    the next one, so no per-call clearing is enqueued.
+ *  - Calls on different streams may run concurrently.  Thread-safe.
+ *  - No C++ exception crosses this interface.  The library prints nothing
+ *    unless LIBTOPK_DEBUG is set in the environment (then HIP failures are
+ *    described on stderr).
+ */
+#ifndef LIBTOPK_H
+#define LIBTOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layout-compatible with HIP's hipStream_t (a pointer to struct
+ * ihipStream_t); callers may pass a hipStream_t directly. */
+struct ihipStream_t;
+typedef struct ihipStream_t *libtopk_stream_t;
+
+/* Status codes returned by every entry point. */
+enum {
+    LIBTOPK_OK = 0,
+    LIBTOPK_ERR_INVALID = 1,     /* bad pointer, size, k or op            */
+    LIBTOPK_ERR_UNSUPPORTED = 2, /* k above libtopk_max_k()               */
+    LIBTOPK_ERR_NOMEM = 3,       /* scratch allocation failed             */
+    LIBTOPK_ERR_HIP = 4          /* no device, or a HIP call / launch failed */
+};
+
+/* Reduction operators for reduce_i32. */
+enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
+
+/* Largest supported k. */
+#define LIBTOPK_MAX_K 128
+
+/*
+ * topk_i32 — the k largest values of in[0..n), written to out[0..k) in
+ * descending order, duplicates kept with their multiplicity.
+ *
+ * Operation: [TopK] §1 (find the 20 largest of 1e8 values) and §2 (the
+ * two-stage design: §2.1 each thread keeps a descending local top-k list
+ * over a grid-stride share of the input, and the block merges the lists;
+ * §2.2 a second, single-block stage merges the per-block candidates; the
+ * result must be identical to the CPU's).  Here both stages run in one
+ * launch: the last workgroup to finish stage 1 performs stage 2.
+ *
+ *   in   device, int32[n], read once
+ *   n    number of elements, 1 <= n <= 2^32
+ *   k    1 <= k <= min(n, LIBTOPK_MAX_K)
+ *   out  device, int32[k], written in full
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, n out of
+ * range, k < 1 or k > n; LIBTOPK_ERR_UNSUPPORTED for k > LIBTOPK_MAX_K.
+ */
+int topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out,
+             libtopk_stream_t stream);
+
+/*
+ * reduce_i32 — fold in[0..n) with one operator into a single int64.
+ *
+ * Operation: [Reduce] "Basic concepts" (a reduction combines every element
+ * through one binary operation into one result; the worked example sums
+ * [1..8] to 36) and the "complete multi-level reduction" driver (a first
+ * pass leaves one partial per block, a further pass combines them).  Here
+ * exactly two stages run in one launch: per-block partials, then the last
+ * workgroup to finish combines them.
+ *
+ *   in       device, int32[n] (may be NULL when n == 0)
+ *   n        0 <= n <= 2^32
+ *   op       LIBTOPK_SUM: exact int64 sum (cannot overflow for n <= 2^32);
+ *            LIBTOPK_MAX / LIBTOPK_MIN: the extreme value, sign-extended.
+ *            n == 0 yields the identity: 0, INT32_MIN or INT32_MAX.
+ *   out_i64  device, int64[1]
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, n out of
+ * range or an unknown op.
+ */
+int reduce_i32(const int32_t *in, int64_t n, int32_t op, int64_t *out_i64,
+               libtopk_stream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *libtopk_strerror(int status);
+
+/* LIBTOPK_MAX_K. */
+int libtopk_max_k(void);
+
+/*
+ * Number of stage-1 workgroups for later calls in this process: 0 restores
+ * the automatic choice, otherwise 1..1024.  Results never depend on it (the
+ * tests sweep it); it exists for tuning.  Returns LIBTOPK_ERR_INVALID for a
+ * value outside 0..1024.
+ */
+int libtopk_set_grid(int32_t blocks);
+
+/*
+ * Workgroups that a call of size n would launch under the current setting
+ * (reporting and traffic accounting; no device work).  Returns 0 for n < 1.
+ */
+int32_t libtopk_grid_for(int64_t n);
+
+/*
+ * Free every cached scratch area after synchronising the devices that own
+ * them.  The next call allocates afresh.  Must not race with other calls.
+ */
+void libtopk_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBTOPK_H */

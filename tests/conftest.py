@@ -3,6 +3,10 @@ import sys
 
 import pytest
 
+# Load PyTorch (and its HIP runtime) before anything loads libtopk.so, so that
+# the process holds exactly one HIP runtime.
+import torch  # noqa: F401,E402
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

@@ -1,0 +1,121 @@
+"""The C-ABI library: it loads, exports every entry point include/libtopk.h
+declares, and rejects invalid arguments before touching the GPU.  Runs on the
+CPU; no compute call reaches a device here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_selection_two_amd as ltk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libtopk.h")
+FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def no_gpu():
+    if os.path.exists("/dev/kfd"):
+        return False
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert {"topk_i32", "reduce_i32", "libtopk_strerror", "libtopk_max_k",
+            "libtopk_set_grid", "libtopk_grid_for",
+            "libtopk_release"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ltk.LIBRARY_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(ltk.SIGNATURES)
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    for name, val in [("LIBTOPK_OK", 0), ("LIBTOPK_ERR_INVALID", 1),
+                      ("LIBTOPK_ERR_UNSUPPORTED", 2), ("LIBTOPK_ERR_NOMEM", 3),
+                      ("LIBTOPK_ERR_HIP", 4), ("LIBTOPK_SUM", 0),
+                      ("LIBTOPK_MAX", 1), ("LIBTOPK_MIN", 2)]:
+        assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text), name
+    assert re.search(r"#define LIBTOPK_MAX_K 128\b", text)
+    assert ltk.max_k() == 128
+
+
+def test_strerror():
+    for s in range(5):
+        assert ltk.strerror(s)
+    assert ltk.strerror(99) == "unknown status"
+    assert ltk.strerror(0) == "success"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 100, 5, FAKE), ltk.ERR_INVALID),                  # NULL input
+    ((FAKE, 100, 5, 0), ltk.ERR_INVALID),                  # NULL output
+    ((FAKE + 2, 100, 5, FAKE * 4), ltk.ERR_INVALID),       # misaligned input
+    ((FAKE, 100, 5, FAKE * 4 + 1), ltk.ERR_INVALID),       # misaligned output
+    ((FAKE, 0, 1, FAKE * 4), ltk.ERR_INVALID),             # n = 0
+    ((FAKE, -5, 1, FAKE * 4), ltk.ERR_INVALID),            # n < 0
+    ((FAKE, (1 << 32) + 1, 5, 1 << 40), ltk.ERR_INVALID),  # n > 2^32
+    ((FAKE, 100, 0, FAKE * 4), ltk.ERR_INVALID),           # k = 0
+    ((FAKE, 100, -3, FAKE * 4), ltk.ERR_INVALID),          # k < 0
+    ((FAKE, 10, 11, FAKE * 4), ltk.ERR_INVALID),           # k > n
+    ((FAKE, 1000, 129, FAKE * 4), ltk.ERR_UNSUPPORTED),    # k above max
+    ((FAKE, 1000, 20, FAKE + 400), ltk.ERR_INVALID),       # out inside in
+    ((FAKE, 1000, 20, FAKE - 40), ltk.ERR_INVALID),        # out overlaps in
+])
+def test_topk_rejects_invalid_arguments(args, status):
+    assert ltk.topk_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 10, 0, 0), ltk.ERR_INVALID),                   # NULL output
+    ((FAKE, 10, 0, FAKE * 4 + 4), ltk.ERR_INVALID),        # misaligned output
+    ((FAKE + 1, 10, 0, FAKE * 4), ltk.ERR_INVALID),        # misaligned input
+    ((0, 10, 0, FAKE * 4), ltk.ERR_INVALID),               # NULL input, n > 0
+    ((FAKE, -1, 0, FAKE * 4), ltk.ERR_INVALID),            # n < 0
+    ((FAKE, (1 << 32) + 1, 0, 1 << 40), ltk.ERR_INVALID),  # n > 2^32
+    ((FAKE, 10, 3, FAKE * 4), ltk.ERR_INVALID),            # unknown op
+    ((FAKE, 10, -1, FAKE * 4), ltk.ERR_INVALID),           # unknown op
+    ((FAKE, 10, 0, FAKE + 8), ltk.ERR_INVALID),            # out inside in
+])
+def test_reduce_rejects_invalid_arguments(args, status):
+    assert ltk.reduce_raw(*args) == status
+
+
+@pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
+def test_valid_call_without_device_reports_hip_error():
+    assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.reduce_raw(FAKE, 1000, 0, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.reduce_raw(0, 0, 1, FAKE * 4) == ltk.ERR_HIP
+
+
+def test_grid_setting():
+    for bad in (-1, 1025, 1 << 20):
+        with pytest.raises(ltk.LibtopkError):
+            ltk.set_grid(bad)
+    try:
+        assert ltk.grid_for(0) == 0
+        assert ltk.grid_for(1) == 1
+        assert ltk.grid_for(4096 * 3 + 5) == 3   # three full tiles
+        ltk.set_grid(7)
+        assert ltk.grid_for(10 ** 8) == 7
+        assert ltk.grid_for(4096 * 3) == 3       # never more than the tiles
+        ltk.set_grid(1024)
+        assert ltk.grid_for(10 ** 9) == 1024
+    finally:
+        ltk.set_grid(0)
+    g = ltk.grid_for(10 ** 8)
+    assert 1 <= g <= 1024

@@ -1,0 +1,153 @@
+"""Python binding for libtopk (two-stage reduction and Top-K on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libtopk.so, whose C interface is include/libtopk.h.  PyTorch
+supplies device memory and the current stream.  There is no CPU fallback:
+if the library is not built, importing this package raises.
+
+    topk(x, k)      -> int32 tensor [k], the k largest of x, descending
+    reduce(x, op)   -> int64 tensor [1]: SUM, MAX or MIN of x
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libtopk.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_NOMEM, ERR_HIP = 0, 1, 2, 3, 4
+SUM, MAX, MIN = 0, 1, 2
+OPS = {"sum": SUM, "max": MAX, "min": MIN}
+
+# Entry points of include/libtopk.h with their ctypes signatures.
+_VP = ctypes.c_void_p
+SIGNATURES = {
+    "topk_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
+                 ctypes.c_int),
+    "reduce_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
+                   ctypes.c_int),
+    "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "libtopk_max_k": ([], ctypes.c_int),
+    "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
+    "libtopk_grid_for": ([ctypes.c_int64], ctypes.c_int32),
+    "libtopk_release": ([], None),
+}
+
+
+class LibtopkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)"
+                         % (what, strerror(status), status))
+
+
+def _load() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime.  Tensors and streams handed to the
+    # library come from that runtime, so it must be the one libtopk.so binds
+    # to: loading torch first makes its libamdhip64 satisfy the library's
+    # dependency (same soname) instead of a second runtime from /opt/rocm.
+    import torch  # noqa: F401
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            "libtopk.so is not built (expected at %s); run "
+            "`python -c 'import __graft_entry__ as g; g.build()'` from the "
+            "repository root" % LIBRARY_PATH)
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.libtopk_strerror(status).decode()
+
+
+def max_k() -> int:
+    return lib.libtopk_max_k()
+
+
+def set_grid(blocks: int) -> None:
+    """Stage-1 workgroups for later calls (0 = automatic)."""
+    rc = lib.libtopk_set_grid(blocks)
+    if rc != OK:
+        raise LibtopkError(rc, "libtopk_set_grid")
+
+
+def grid_for(n: int) -> int:
+    return int(lib.libtopk_grid_for(n))
+
+
+def release() -> None:
+    lib.libtopk_release()
+
+
+# ---------------------------------------------------------------- raw calls
+def topk_raw(in_ptr: int, n: int, k: int, out_ptr: int, stream: int = 0) -> int:
+    """Call topk_i32 on raw device pointers; returns the status code."""
+    return lib.topk_i32(in_ptr or None, n, k, out_ptr or None, stream or None)
+
+
+def reduce_raw(in_ptr: int, n: int, op: int, out_ptr: int,
+               stream: int = 0) -> int:
+    """Call reduce_i32 on raw device pointers; returns the status code."""
+    return lib.reduce_i32(in_ptr or None, n, op, out_ptr or None,
+                          stream or None)
+
+
+# ---------------------------------------------------------------- tensors
+def _check_input(x):
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if x.dtype != torch.int32:
+        raise TypeError("expected int32, got %s" % x.dtype)
+    if x.device.type != "cuda":
+        raise ValueError("expected a device tensor, got %s" % x.device)
+    if x.dim() != 1 or not x.is_contiguous():
+        raise ValueError("expected a contiguous 1-D tensor")
+
+
+def topk(x, k: int, out=None):
+    """The k largest values of the int32 device tensor x, descending."""
+    import torch
+    _check_input(x)
+    if out is None:
+        out = torch.empty(max(int(k), 0), dtype=torch.int32, device=x.device)
+    elif (out.dtype != torch.int32 or out.device != x.device
+          or out.numel() != k or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [k] tensor on "
+                         "x's device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.topk_i32(x.data_ptr() if x.numel() else None, x.numel(), k,
+                          out.data_ptr() if out.numel() else None,
+                          stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "topk_i32")
+    return out
+
+
+def reduce(x, op, out=None):
+    """SUM (exact int64), MAX or MIN of the int32 device tensor x."""
+    import torch
+    _check_input(x)
+    if isinstance(op, str):
+        op = OPS[op]
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=x.device)
+    elif (out.dtype != torch.int64 or out.device != x.device
+          or out.numel() != 1):
+        raise ValueError("out must be an int64 [1] tensor on x's device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.reduce_i32(x.data_ptr() if x.numel() else None, x.numel(),
+                            op, out.data_ptr(), stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "reduce_i32")
+    return out

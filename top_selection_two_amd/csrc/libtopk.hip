@@ -1,0 +1,305 @@
+// libtopk host side: argument checks, launch geometry, per-(device, stream)
+// scratch, and the two C entry points declared in include/libtopk.h.
+//
+// The launch plan follows the two-stage design of
+//   [TopK]   "CUDA并行优化实战：从TopK问题剖析共享内存与规约算法设计", §2.2
+//            (a first launch over the data leaves k candidates per block, a
+//            single block merges them) and §4.2 (size the grid to the
+//            machine rather than fixing it),
+//   [Reduce] "CUDA归约优化完全指南：从入门到精通", "complete multi-level
+//            reduction" (one partial per block, then a pass over partials;
+//            check launch errors after each launch),
+// with both stages fused into a single launch (see the kernel headers).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "libtopk.h"
+#include "reduce_kernel.hpp"
+#include "topk_kernel.hpp"
+
+namespace {
+
+using namespace ltk;
+
+constexpr int kTileVec = 4;         // 16-byte loads per lane per tile (U)
+constexpr int kRefreshPeriod = 8;   // tiles between bound refreshes
+constexpr int64_t kMaxN = (int64_t)1 << 32;
+
+struct Scratch {
+  void* base = nullptr;
+  int* cand = nullptr;         // kMaxGrid * kMaxK
+  int* heads = nullptr;        // kMaxGrid
+  int* kths = nullptr;         // kMaxGrid
+  int64_t* partials = nullptr; // kMaxGrid
+  unsigned* ticket = nullptr;  // 1 word, kept at 0 between calls
+};
+
+constexpr size_t kCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(int);
+constexpr size_t kHeadBytes = (size_t)kMaxGrid * sizeof(int);
+constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
+constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes + 256;
+
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Scratch> g_cache;
+std::map<int, int> g_cus;          // device -> compute units
+std::atomic<int> g_grid_override{0};
+
+// With LIBTOPK_DEBUG set in the environment, HIP failures are described on
+// stderr; otherwise the library prints nothing.
+void debug_hip(const char* what, hipError_t e) {
+  static const bool on = getenv("LIBTOPK_DEBUG") != nullptr;
+  if (on) fprintf(stderr, "libtopk: %s: %s\n", what, hipGetErrorString(e));
+}
+
+__global__ void zero_words(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+int current_device(int* dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1)
+    return LIBTOPK_ERR_HIP;
+  if (hipGetDevice(dev) != hipSuccess) return LIBTOPK_ERR_HIP;
+  return LIBTOPK_OK;
+}
+
+// Caller holds g_mu.
+int compute_units(int dev) {
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess || cus < 1)
+    cus = 256;
+  g_cus[dev] = cus;
+  return cus;
+}
+
+int get_scratch(int dev, hipStream_t stream, Scratch* out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  const auto key = std::make_pair(dev, (void*)stream);
+  auto it = g_cache.find(key);
+  if (it != g_cache.end()) {
+    *out = it->second;
+    return LIBTOPK_OK;
+  }
+  Scratch s;
+  if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
+  hipError_t e = hipMalloc(&s.base, kScratchBytes);
+  if (e != hipSuccess) {
+    debug_hip("hipMalloc(scratch)", e);
+    (void)hipGetLastError();
+    return LIBTOPK_ERR_NOMEM;
+  }
+  char* b = (char*)s.base;
+  s.cand = (int*)b;
+  b += kCandBytes;
+  s.heads = (int*)b;
+  b += kHeadBytes;
+  s.kths = (int*)b;
+  b += kHeadBytes;
+  s.partials = (int64_t*)b;
+  b += kPartBytes;
+  s.ticket = (unsigned*)b;
+  // A kernel (not a memset) clears the counter, ordered on the caller's
+  // stream before the first real launch.
+  hipLaunchKernelGGL(zero_words, dim3(1), dim3(64), 0, stream, s.ticket, 64);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    debug_hip("zero_words launch", e);
+    (void)hipFree(s.base);
+    return LIBTOPK_ERR_HIP;
+  }
+  g_cache[key] = s;
+  *out = s;
+  return LIBTOPK_OK;
+}
+
+struct Plan {
+  int64_t head, ntiles, covered;
+  int grid;
+};
+
+Plan plan(const int32_t* in, int64_t n, int cus) {
+  Plan pl;
+  const uintptr_t a = (uintptr_t)in;
+  int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
+  if (head > n) head = n;
+  const int64_t vecs = (n - head) / 4;
+  pl.head = head;
+  pl.ntiles = vecs / (kBlock * kTileVec);
+  pl.covered = pl.ntiles * kBlock * kTileVec * 4;
+  int g = g_grid_override.load();
+  if (g <= 0) g = 2 * cus;
+  if (g > kMaxGrid) g = kMaxGrid;
+  int64_t cap = pl.ntiles > 0 ? pl.ntiles : 1;
+  if (g > cap) g = (int)cap;
+  pl.grid = g;
+  return pl;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bn && y < x + an;
+}
+
+template <class P>
+int launch(const void* fn, int grid, P params, hipStream_t stream) {
+  void* args[] = {&params};
+  const hipError_t e =
+      hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+  if (e != hipSuccess) {
+    debug_hip("kernel launch", e);
+    (void)hipGetLastError();
+    return LIBTOPK_ERR_HIP;
+  }
+  return LIBTOPK_OK;
+}
+
+const void* topk_fn(int k) {
+  if (k <= 16) return (const void*)&topk_kernel<16, kTileVec>;
+  if (k <= 32) return (const void*)&topk_kernel<32, kTileVec>;
+  if (k <= 64) return (const void*)&topk_kernel<64, kTileVec>;
+  return (const void*)&topk_kernel<128, kTileVec>;
+}
+
+const void* reduce_fn(int op) {
+  if (op == kOpSum) return (const void*)&reduce_kernel<kOpSum, kTileVec>;
+  if (op == kOpMax) return (const void*)&reduce_kernel<kOpMax, kTileVec>;
+  return (const void*)&reduce_kernel<kOpMin, kTileVec>;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
+             libtopk_stream_t stream) {
+  if (!in || !out) return LIBTOPK_ERR_INVALID;
+  if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return LIBTOPK_ERR_INVALID;
+  if (n < 1 || n > kMaxN) return LIBTOPK_ERR_INVALID;
+  if (k < 1 || (int64_t)k > n) return LIBTOPK_ERR_INVALID;
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (overlaps(in, (size_t)n * 4, out, (size_t)k * 4))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  const Plan pl = plan(in, n, cus);
+  TopkParams p;
+  p.in = in;
+  p.n = n;
+  p.head = pl.head;
+  p.ntiles = pl.ntiles;
+  p.covered = pl.covered;
+  p.k = k;
+  p.grid = pl.grid;
+  p.refresh = kRefreshPeriod;
+  p.cand = sc.cand;
+  p.heads = sc.heads;
+  p.kths = sc.kths;
+  p.ticket = sc.ticket;
+  p.out = out;
+  return launch(topk_fn(k), pl.grid, p, s);
+}
+
+int reduce_i32(const int32_t* in, int64_t n, int32_t op, int64_t* out_i64,
+               libtopk_stream_t stream) {
+  if (!out_i64 || ((uintptr_t)out_i64 & 7u)) return LIBTOPK_ERR_INVALID;
+  if (n < 0 || n > kMaxN) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && (!in || ((uintptr_t)in & 3u))) return LIBTOPK_ERR_INVALID;
+  if (op < LIBTOPK_SUM || op > LIBTOPK_MIN) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && overlaps(in, (size_t)n * 4, out_i64, 8))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  // n == 0: a one-block launch with nothing to read writes the identity.
+  static const int32_t kDummy = 0;
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  ReduceParams p;
+  p.in = in;
+  p.n = n;
+  p.head = pl.head;
+  p.ntiles = pl.ntiles;
+  p.covered = pl.covered;
+  p.grid = pl.grid;
+  p.partials = sc.partials;
+  p.ticket = sc.ticket;
+  p.out = out_i64;
+  return launch(reduce_fn(op), pl.grid, p, s);
+}
+
+const char* libtopk_strerror(int status) {
+  switch (status) {
+    case LIBTOPK_OK: return "success";
+    case LIBTOPK_ERR_INVALID: return "invalid argument";
+    case LIBTOPK_ERR_UNSUPPORTED: return "k above the supported maximum";
+    case LIBTOPK_ERR_NOMEM: return "scratch allocation failed";
+    case LIBTOPK_ERR_HIP: return "no HIP device, or a HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int libtopk_max_k(void) { return LIBTOPK_MAX_K; }
+
+int libtopk_set_grid(int32_t blocks) {
+  if (blocks < 0 || blocks > kMaxGrid) return LIBTOPK_ERR_INVALID;
+  g_grid_override.store(blocks);
+  return LIBTOPK_OK;
+}
+
+int32_t libtopk_grid_for(int64_t n) {
+  if (n < 1) return 0;
+  int cus = 256;
+  int dev = 0;
+  if (current_device(&dev) == LIBTOPK_OK) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  // The grid depends on the alignment only through the head peel (< 4
+  // elements); report it for a 16-byte-aligned input.
+  return plan((const int32_t*)(uintptr_t)0x1000, n, cus).grid;
+}
+
+void libtopk_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  for (auto& kv : g_cache) {
+    if (hipSetDevice(kv.first.first) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.base);
+    }
+  }
+  g_cache.clear();
+  if (prev >= 0) (void)hipSetDevice(prev);
+  (void)hipGetLastError();
+}
+
+}  // extern "C"
