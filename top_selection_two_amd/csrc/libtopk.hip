@@ -163,11 +163,15 @@ int launch(const void* fn, int grid, P params, hipStream_t stream) {
   return LIBTOPK_OK;
 }
 
+// List capacity: exactly k rounded up to 8 while that is small (the list
+// then needs no guards), otherwise 64 or 128 slots with chunk guards.
 const void* topk_fn(int k) {
-  if (k <= 16) return (const void*)&topk_kernel<16, kTileVec>;
-  if (k <= 32) return (const void*)&topk_kernel<32, kTileVec>;
-  if (k <= 64) return (const void*)&topk_kernel<64, kTileVec>;
-  return (const void*)&topk_kernel<128, kTileVec>;
+  if (k <= 8) return (const void*)&topk_kernel<8, true, kTileVec>;
+  if (k <= 16) return (const void*)&topk_kernel<16, true, kTileVec>;
+  if (k <= 24) return (const void*)&topk_kernel<24, true, kTileVec>;
+  if (k <= 32) return (const void*)&topk_kernel<32, true, kTileVec>;
+  if (k <= 64) return (const void*)&topk_kernel<64, false, kTileVec>;
+  return (const void*)&topk_kernel<128, false, kTileVec>;
 }
 
 const void* reduce_fn(int op) {

@@ -9,12 +9,13 @@
 //            with the identity) and the "complete multi-level reduction"
 //            driver (one partial per block, then a pass over the partials).
 //
-// gfx950 design: 16-byte loads, U per lane per tile, a workgroup owns a
-// contiguous run of tiles; lanes accumulate in registers (int64 for the sum,
+// gfx950 design: non-temporal 16-byte loads, U per lane per tile, tiles
+// dealt round-robin to the workgroups and double-buffered in registers;
+// lanes accumulate in registers (int64 for the sum,
 // so it cannot overflow for n <= 2^32), the wave combines with cross-lane
 // shuffles, four wave partials meet in LDS, and the last workgroup to
-// finish (ticket counter, release/acquire fences) folds the per-block
-// partials instead of a second launch.  No MFMA: nothing here is a dense
+// finish (ticket counter; see last_to_finish) folds the per-block partials
+// instead of a second launch.  No MFMA: nothing here is a dense
 // contraction.
 #pragma once
 
@@ -104,16 +105,41 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
   const int w = threadIdx.x / kWave;
 
   typename F::acc_t acc = F::identity();
+  // Round-robin tiles, two alternating register buffers (see load_tile).
   const v4i* __restrict__ body = reinterpret_cast<const v4i*>(p.in + p.head);
-  const int64_t t0 = p.ntiles * blk / p.grid;
-  const int64_t t1 = p.ntiles * (blk + 1) / p.grid;
-  for (int64_t t = t0; t < t1; ++t) {
-    const int64_t base = t * (int64_t)(kBlock * U) + threadIdx.x;
-    v4i d[U];
+  const int64_t count = tiles_of(p.ntiles, blk, p.grid);
+  if (count > 0) {
+    // Both buffers are filled unconditionally (the second load re-reads the
+    // only tile when there is one), so every path into the loop has the
+    // same loads pending in the same order, and the wait before each tile
+    // is for that tile alone.
+    v4i A[U], B[U];
+    load_tile<U>(body, blk, p.grid, count, 0, A);
+    sched_fence();
+    load_tile<U>(body, blk, p.grid, count, 1, B);
+    sched_fence();
+    int64_t i = 0;
+#pragma nounroll
+    for (; i + 2 <= count; i += 2) {
+      ready(A);
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = body[base + u * kBlock];
+      for (int u = 0; u < U; ++u) acc = F::add4(acc, A[u]);
+      pin(acc);
+      sched_fence();
+      load_tile<U>(body, blk, p.grid, count, i + 2, A);
+      sched_fence();
+      ready(B);
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = F::add4(acc, d[u]);
+      for (int u = 0; u < U; ++u) acc = F::add4(acc, B[u]);
+      pin(acc);
+      sched_fence();
+      load_tile<U>(body, blk, p.grid, count, i + 3, B);
+      sched_fence();
+    }
+    if (i < count) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc = F::add4(acc, A[u]);
+    }
   }
   if (blk == p.grid - 1) {
     const int64_t left = p.n - p.covered;
@@ -127,20 +153,14 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
     int64_t b = red[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) b = F::combine(b, red[i]);
-    p.partials[blk] = b;
+    st_agent(p.partials + blk, b);
   }
 
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = atomicAdd(p.ticket, 1u) == (unsigned)(p.grid - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
 
   int64_t v = F::widen(F::identity());
   for (int i = threadIdx.x; i < p.grid; i += kBlock)
-    v = F::combine(v, p.partials[i]);
+    v = F::combine(v, ld_agent(p.partials + i));
   v = wave_combine64<OP>(v);
   if (lane() == 0) red[w] = v;
   __syncthreads();
@@ -149,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) r = F::combine(r, red[i]);
     *p.out = r;
-    *p.ticket = 0u;
+    st_agent(p.ticket, 0u);
   }
 }
 

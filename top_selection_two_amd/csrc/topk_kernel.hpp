@@ -12,8 +12,10 @@
 //          memory for the final steps).
 //
 // What differs from the pages, and why (gfx950, wave64):
-//  * Each lane streams 16-byte loads (global_load_dwordx4), U of them per
-//    tile; a workgroup owns a contiguous run of tiles.
+//  * Each lane streams non-temporal 16-byte loads (global_load_dwordx4), U
+//    of them per tile; tiles are dealt round-robin to the workgroups and
+//    double-buffered in registers so the next tile is in flight while the
+//    current one is examined.
 //  * The insertion test uses a shared, *certified* lower bound T besides the
 //    lane's own k-th entry.  T is certified when the lists of this workgroup
 //    jointly hold at least k entries >= T; then every element x <= T can be
@@ -29,8 +31,9 @@
 //    over ballots), keeps the entries > g and pads with copies of g; wave 0
 //    then does the same over the four wave results.  The result of a block
 //    is its exact top-k as a multiset (unordered), plus its max and k-th.
-//  * Stage 2 runs in the last workgroup to finish (ticket counter, release/
-//    acquire fences), not in a second launch.  It first derives a certified
+//  * Stage 2 runs in the last workgroup to finish (ticket counter and
+//    agent-coherent stores and loads, see last_to_finish), not in a second
+//    launch.  It first derives a certified
 //    bound T2 from the block maxima (k-th largest of them) and the block
 //    k-th values (their max), keeps only candidates >= T2, selects the k-th
 //    largest g among them, and writes the < k values above g in descending
@@ -58,35 +61,55 @@ struct TopkParams {
 };
 
 constexpr int kSurvCap = 4096;  // stage-2 survivors staged in LDS
+constexpr int kRing = 4;        // tiles in flight per wave (power of 2)
+template <int U>
+constexpr int64_t kTileBytes = (int64_t)kBlock * U * 16;  // one tile
+
+// Stage-2 scratch in LDS.  It lives in the memory of the last workgroup's
+// streaming ring (declared separately, see topk_kernel), which is idle by
+// then.
+struct Stage2Lds {
+  int surv[kSurvCap];
+  int gt[kMaxK];
+  int blocks[kMaxGrid];  // blocks whose maximum reaches T2
+};
 
 template <int KCAP>
 struct TopkShared {
-  unsigned heads[2][kBlock];
+  unsigned heads[kBlock];  // snapshot of the lane heads (biased)
   int wave_out[kWaves][KCAP];
   int wave_cnt[kWaves];
   int red[2][kWaves];
   int bcast[8];
   int is_last;
-  int surv[kSurvCap];
-  int gt[kMaxK];
 };
 
-// Insert x into the descending list L[0..k); returns the new L[k-1].
-// Lanes whose x does not exceed L[k-1] leave their list unchanged.
-template <int KCAP>
+// Insert x into the descending list; returns the evicted value.  The
+// bubble (min into a temporary, max in place: two instructions per slot)
+// runs over the slots up to k8, the first multiple of 8 that is >= k, so
+// the list holds the top-k8 >= k of the elements admitted to it.  Every
+// entry left in the list is >= the evicted value, so that value is a valid
+// lane threshold.  Lanes whose x does not exceed L[k8-1] leave their list
+// unchanged (and return x).
+//
+// FIT: the capacity is exactly k8, so every slot is used and the bubble has
+// no branches at all.  Otherwise (large k) the slots beyond k8 stay INT_MIN
+// and whole chunks of 8 are skipped with one wave-uniform branch each.
+template <int KCAP, bool FIT>
 __device__ __forceinline__ int list_insert(int (&L)[KCAP], int x, int k) {
-  int hi = x;
-  // Constant trip count so the loop unrolls fully and L stays in VGPRs;
-  // the guard is a wave-uniform scalar branch.
+  static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
 #pragma unroll
-  for (int i = 0; i < KCAP; ++i) {
-    if (i < k) {
-      hi = max(L[i], x);
-      x = min(L[i], x);
-      L[i] = hi;
+  for (int c = 0; c < KCAP; c += 8) {
+    if (FIT || c < k) {
+#pragma unroll
+      for (int i = c; i < c + 8; ++i) {
+        const int lo = min(L[i], x);
+        L[i] = max(L[i], x);
+        x = lo;
+      }
     }
   }
-  return hi;
+  return x;
 }
 
 // Wave-uniform count of list entries >= s (lists are descending, so the
@@ -139,18 +162,19 @@ struct ListCount {
   }
 };
 
-template <int KCAP>
+template <int KCAP, bool FIT>
 __device__ __forceinline__ void admit(int (&L)[KCAP], int x, int k, int tsh,
                                       int& thr) {
   if (ballot(x > thr)) {
-    const int last = list_insert<KCAP>(L, x, k);
-    thr = max(last, tsh);
+    const int evicted = list_insert<KCAP, FIT>(L, x, k);
+    thr = max(thr, max(evicted, tsh));
   }
 }
 
 // One tile's worth of values (U x 4 per lane): a max-of-16 and one vote
-// reject the whole group in the common case.
-template <int KCAP, int U>
+// reject the whole group in the common case; otherwise each 4-element
+// vector, then each element, is tested the same way before insertion.
+template <int KCAP, bool FIT, int U>
 __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
                                         int k, int tsh, int& thr) {
   int mu[U];
@@ -164,50 +188,62 @@ __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!ballot(mu[u] > thr)) continue;
-    admit<KCAP>(L, d[u].x, k, tsh, thr);
-    admit<KCAP>(L, d[u].y, k, tsh, thr);
-    admit<KCAP>(L, d[u].z, k, tsh, thr);
-    admit<KCAP>(L, d[u].w, k, tsh, thr);
+    admit<KCAP, FIT>(L, d[u].x, k, tsh, thr);
+    admit<KCAP, FIT>(L, d[u].y, k, tsh, thr);
+    admit<KCAP, FIT>(L, d[u].z, k, tsh, thr);
+    admit<KCAP, FIT>(L, d[u].w, k, tsh, thr);
   }
 }
 
-// Raise the workgroup's certified bound to the k-th largest of its 256 lane
-// heads (k <= 128 < 256).  Every wave computes the same value from the same
-// LDS snapshot.  Contains one barrier: call uniformly across the block.
-template <int KCAP>
+// Raise a certified bound to the k-th largest of the workgroup's 256 lane
+// heads (k <= 128 < 256).
+//
+// Every lane keeps its current head (list maximum) in an LDS snapshot.  A
+// list's head never decreases, so any value that was ever a lane's head is
+// still <= that lane's current head: the k-th largest of ANY mix of current
+// and older snapshot entries is <= the k-th largest current head, hence
+// certified.  During streaming (SYNC = false) a wave therefore publishes its
+// own heads and reads the snapshot without waiting for the other waves: no
+// barrier, and each wave keeps its own bound.  The final refresh (SYNC =
+// true) waits for all four waves, so every wave computes the same value, the
+// exact k-th largest head, which is >= every earlier wave bound.
+template <bool SYNC, int KCAP, class SH>
 __device__ __forceinline__ void refresh_bound(const int (&L)[KCAP], int k,
                                               int& tsh, int& thr,
-                                              TopkShared<KCAP>& sh, int& buf) {
-  sh.heads[buf][threadIdx.x] = bias(L[0]);
-  __syncthreads();
+                                              SH& sh) {
+  __hip_atomic_store(&sh.heads[threadIdx.x], bias(L[0]), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (SYNC) __syncthreads();
   unsigned u[kWaves];
   int mx = kI32Min;
 #pragma unroll
   for (int j = 0; j < kWaves; ++j) {
-    u[j] = sh.heads[buf][lane() + kWave * j];
+    u[j] = __hip_atomic_load(&sh.heads[lane() + kWave * j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
     mx = max(mx, unbias(u[j]));
   }
-  buf ^= 1;
   const RegCount<kWaves> cnt{u};
   const unsigned lo = bias(tsh);
   if (cnt(lo) >= k) {
     mx = wave_max(mx);
-    tsh = unbias(radix_select(lo, bias(mx), k, cnt));
+    // While streaming, the top 6 undecided bits are enough: the bound lands
+    // within 1/64 of the gap between the old bound and the largest head
+    // below the exact k-th head, for a fraction of the steps.
+    tsh = unbias(SYNC ? radix_select(lo, bias(mx), k, cnt)
+                      : radix_lower_bound(lo, bias(mx), k, 6, cnt));
   }
   thr = max(thr, tsh);
 }
 
-template <int U>
-__device__ __forceinline__ void load_tile(const v4i* __restrict__ body,
-                                          int64_t t, v4i (&d)[U]) {
-  const int64_t base = t * (int64_t)(kBlock * U) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < U; ++u) d[u] = body[base + u * kBlock];
+// Refresh after local tiles 0, 1, 3 (while the bound improves fastest), then
+// after every R-th tile.
+__device__ __forceinline__ bool refresh_due(int64_t j, int R) {
+  return (j < R && (j & (j + 1)) == 0) || (j & (R - 1)) == R - 1;
 }
 
 // Block-wide sum of one int per thread (barrier inside; call uniformly).
-template <int KCAP>
-__device__ __forceinline__ int block_sum(int v, TopkShared<KCAP>& sh,
+template <class SH>
+__device__ __forceinline__ int block_sum(int v, SH& sh,
                                          int& parity) {
   const int64_t ws = wave_sum((int64_t)v);
   if (lane() == 0) sh.red[parity][threadIdx.x / kWave] = (int)ws;
@@ -231,15 +267,46 @@ __device__ __forceinline__ void wave_append(bool p, int v, int* counter,
   if (p && pos < cap) dst[pos] = v;
 }
 
+// Visit the candidates of the flagged blocks (blocks[0..nb), k each): 16
+// independent agent-coherent loads per thread are in flight before any is
+// used.  f(valid, value) is called uniformly across the block.
+template <class F>
+__device__ __forceinline__ void scan_flagged(const TopkParams& p,
+                                             const int* blocks, int total,
+                                             F&& f) {
+  const int k = p.k;
+  constexpr int B = 16;
+  for (int base = 0; base < total; base += kBlock * B) {
+    int v[B];
+    bool ok[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      int idx = base + j * kBlock + (int)threadIdx.x;
+      ok[j] = idx < total;
+      idx = ok[j] ? idx : total - 1;
+      const int fb = idx / k;
+      const int e = idx - fb * k;
+      v[j] = ld_agent(p.cand + (int64_t)blocks[fb] * k + e);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) f(ok[j], v[j]);
+  }
+}
+
 // Stage 2, run by the last workgroup: merge grid*k candidates into out[0..k).
-template <int KCAP>
-__device__ __forceinline__ void topk_stage2(const TopkParams& p,
-                                            TopkShared<KCAP>& sh) {
+template <class SH>
+__device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
+                                            Stage2Lds& s2) {
   const int G = p.grid, k = p.k;
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
 
-  // (A) certified bound from the block summaries (wave 0).
+  // (A) wave 0: a certified bound T2 from the block summaries, and the list
+  // of blocks whose maximum reaches it (no other block can contribute).
+  //   T2b = max over blocks of their k-th candidate (that block alone holds
+  //         k candidates >= it);
+  //   T2a = k-th largest block maximum (k distinct candidates >= it);
+  //   T2  = max(T2a, T2b).
   if (w == 0) {
     constexpr int VH = kMaxGrid / kWave;
     unsigned uh[VH];
@@ -247,37 +314,99 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p,
 #pragma unroll
     for (int j = 0; j < VH; ++j) {
       const int b = lane() + kWave * j;
-      int h = kI32Min;
-      if (b < G) {
-        h = p.heads[b];
-        kt = max(kt, p.kths[b]);
-      }
+      const int bb = b < G ? b : G - 1;
+      int h = ld_agent(p.heads + bb);
+      int t = ld_agent(p.kths + bb);
+      if (b >= G) h = t = kI32Min;
       uh[j] = bias(h);
       mx = max(mx, h);
+      kt = max(kt, t);
     }
     mx = wave_max(mx);
     kt = wave_max(kt);
-    int ta = kI32Min;
-    if (G >= k) ta = unbias(radix_select(0u, bias(mx), k, RegCount<VH>{uh}));
+    const RegCount<VH> cnt{uh};
+    int t2 = kt;
+    // A lower bound within 1/256 of the range of the exact T2a suffices:
+    // it only admits a few more survivors.
+    if (cnt(bias(kt)) >= k)
+      t2 = unbias(radix_lower_bound(bias(kt), bias(mx), k, 8, cnt));
+    int nb = 0;  // flagged blocks, compacted in block order
+#pragma unroll
+    for (int j = 0; j < VH; ++j) {
+      const int b = lane() + kWave * j;
+      const bool f = b < G && unbias(uh[j]) >= t2;
+      const uint64_t m = ballot(f);
+      if (f) s2.blocks[nb + lanes_below(m)] = b;
+      nb += popc(m);
+    }
+    const int total = nb * k;  // candidates of the flagged blocks
+    int done = 1;
+    if (t2 == mx) {
+      // At least k candidates are >= T2 and none exceeds mx: k copies of mx.
+      for (int j = lane(); j < k; j += kWave) p.out[j] = mx;
+    } else if (total <= 8 * kWave) {
+      // Few survivors: this wave finishes alone, in registers.
+      constexpr int V = 8;
+      unsigned u[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int q = lane() + kWave * j;
+        const int qq = q < total ? q : total - 1;
+        const int fb = qq / k;
+        const int v = ld_agent(p.cand + (int64_t)s2.blocks[fb] * k + (qq - fb * k));
+        u[j] = (q < total && v >= t2) ? bias(v) : 0u;
+      }
+      const unsigned g = radix_select(bias(t2), bias(mx), k, RegCount<V>{u});
+      const int gs = unbias(g);
+      int ngt = 0;  // values above g, compacted into gt[]
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const bool a = u[j] > g;
+        const uint64_t m = ballot(a);
+        if (a) s2.gt[ngt + lanes_below(m)] = unbias(u[j]);
+        ngt += popc(m);
+      }
+      for (int i = lane(); i < k; i += kWave) {
+        if (i < ngt) {
+          const int v = s2.gt[i];
+          int r = 0;
+          for (int j = 0; j < ngt; ++j) {
+            const int o = s2.gt[j];
+            r += (o > v) | ((o == v) & (j < i));
+          }
+          p.out[r] = v;
+        } else {
+          p.out[i] = gs;
+        }
+      }
+    } else {
+      done = 0;
+    }
     if (lane() == 0) {
-      sh.bcast[0] = max(ta, kt);  // T2
-      sh.bcast[1] = mx;           // largest candidate
-      sh.bcast[2] = 0;            // survivor count
-      sh.bcast[3] = 0;            // count of values above g
+      sh.bcast[6] = done;
+      sh.bcast[5] = nb;
+      sh.bcast[0] = t2;  // T2
+      sh.bcast[1] = mx;  // largest candidate
+      sh.bcast[2] = 0;   // survivor count
+      sh.bcast[3] = 0;   // count of values above g
     }
   }
   __syncthreads();
-  const int T2 = sh.bcast[0], mx = sh.bcast[1];
-
-  // (B) survivors >= T2 into LDS.
-  const int64_t nc = (int64_t)G * k;
-  for (int64_t base = 0; base < nc; base += kBlock) {
-    const int64_t i = base + tid;
-    const int c = (i < nc) ? p.cand[i] : kI32Min;
-    wave_append(i < nc && c >= T2, c, &sh.bcast[2], sh.surv, kSurvCap);
+  if (sh.bcast[6]) {
+    if (tid == 0) st_agent(p.ticket, 0u);
+    return;
   }
+  // General path: many flagged candidates (heavy ties near the top).
+  const int T2 = sh.bcast[0], mx = sh.bcast[1];
+  const int total = sh.bcast[5] * k;
+
+  // (B) survivors >= T2 into LDS (only the first kSurvCap are kept).
+  scan_flagged(p, s2.blocks, total, [&](bool ok, int c) {
+    wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv, kSurvCap);
+  });
   __syncthreads();
   const int m = sh.bcast[2];
+  const bool in_lds = m <= kSurvCap;
 
   // (C) g = k-th largest survivor (there are >= k: T2 is certified).
   unsigned g;
@@ -287,7 +416,7 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int q = lane() + kWave * j;
-        u[j] = q < m ? bias(sh.surv[q]) : 0u;
+        u[j] = q < m ? bias(s2.surv[q]) : 0u;
       }
       g = radix_select(bias(T2), bias(mx), k, RegCount<8>{u});
       if (lane() == 0) sh.bcast[4] = (int)g;
@@ -296,17 +425,15 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p,
     g = (unsigned)sh.bcast[4];
   } else {
     int parity = 0;
-    const bool in_lds = m <= kSurvCap;
     auto count_ge = [&](unsigned c) __attribute__((always_inline)) -> int {
       const int s = unbias(c);
       int mine = 0;
       if (in_lds) {
-        for (int i = tid; i < m; i += kBlock) mine += sh.surv[i] >= s;
+        for (int i = tid; i < m; i += kBlock) mine += s2.surv[i] >= s;
       } else {
-        for (int64_t i = tid; i < nc; i += kBlock) {
-          const int v = p.cand[i];
-          mine += (v >= s) & (v >= T2);
-        }
+        scan_flagged(p, s2.blocks, total, [&](bool ok, int v) {
+          mine += ok & (v >= s) & (v >= T2);
+        });
       }
       return block_sum(mine, sh, parity);
     };
@@ -315,38 +442,41 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p,
   const int gs = unbias(g);
 
   // (D) values above g (fewer than k), ranked; then copies of g.
-  if (m <= kSurvCap) {
+  if (in_lds) {
     for (int base = 0; base < m; base += kBlock) {
       const int i = base + tid;
-      const int c = i < m ? sh.surv[i] : kI32Min;
-      wave_append(i < m && c > gs, c, &sh.bcast[3], sh.gt, kMaxK);
+      const int c = i < m ? s2.surv[i] : kI32Min;
+      wave_append(i < m && c > gs, c, &sh.bcast[3], s2.gt, kMaxK);
     }
   } else {
-    for (int64_t base = 0; base < nc; base += kBlock) {
-      const int64_t i = base + tid;
-      const int c = (i < nc) ? p.cand[i] : kI32Min;
-      wave_append(i < nc && c > gs, c, &sh.bcast[3], sh.gt, kMaxK);
-    }
+    scan_flagged(p, s2.blocks, total, [&](bool ok, int c) {
+      wave_append(ok && c > gs, c, &sh.bcast[3], s2.gt, kMaxK);
+    });
   }
   __syncthreads();
   const int ngt = sh.bcast[3];
   if (tid < ngt) {
-    const int v = sh.gt[tid];
+    const int v = s2.gt[tid];
     int r = 0;
     for (int j = 0; j < ngt; ++j) {
-      const int o = sh.gt[j];
+      const int o = s2.gt[j];
       r += (o > v) | ((o == v) & (j < tid));
     }
     p.out[r] = v;
   } else if (tid < k) {
     p.out[tid] = gs;
   }
-  if (tid == 0) *p.ticket = 0u;
+  if (tid == 0) st_agent(p.ticket, 0u);
 }
 
-template <int KCAP, int U>
+template <int KCAP, bool FIT, int U>
 __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   __shared__ TopkShared<KCAP> sh;
+  // Each wave's ring of kRing tiles (its quarter of each tile).  A separate
+  // LDS object from `sh`, so that the compiler can tell LDS accesses to
+  // `sh` apart from the in-flight ring loads and does not wait for those.
+  __shared__ v4i ring_lds[kWaves][kRing][U][kWave];
+  static_assert(sizeof(ring_lds) >= sizeof(Stage2Lds), "ring too small");
   const int blk = blockIdx.x;
   const int k = p.k;
   const int w = threadIdx.x / kWave;
@@ -354,25 +484,47 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   int L[KCAP];
 #pragma unroll
   for (int i = 0; i < KCAP; ++i) L[i] = kI32Min;
-  int tsh = kI32Min;  // certified bound shared by the workgroup
-  int thr = kI32Min;  // this lane's test: max(L[k-1], tsh)
-  int buf = 0;
+  int tsh = kI32Min;  // this wave's certified bound
+  int thr = kI32Min;  // this lane's test: max(its list's last entry, tsh)
+  sh.heads[threadIdx.x] = 0u;  // biased INT_MIN: the weakest valid head
+  __syncthreads();
 
   // ---- stage 1: stream this workgroup's tiles ---------------------------
+  // Tiles are dealt round-robin (tile blk, blk+grid, ...), so at any moment
+  // the grid reads one compact window of HBM.  Each wave streams its
+  // quarter of every tile straight into its own LDS ring (global_load_lds,
+  // 16 B per lane, no VGPRs), kRing tiles ahead of the one it examines, so
+  // the time spent inserting never leaves the memory pipe empty.
   const v4i* __restrict__ body = reinterpret_cast<const v4i*>(p.in + p.head);
-  const int64_t t0 = p.ntiles * blk / p.grid;
-  const int64_t t1 = p.ntiles * (blk + 1) / p.grid;
+  const int64_t count = tiles_of(p.ntiles, blk, p.grid);
   const int R = p.refresh;
-  v4i cur[U], nxt[U];
-  if (t0 < t1) load_tile<U>(body, t0, cur);
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t + 1 < t1) load_tile<U>(body, t + 1, nxt);
-    consume<KCAP, U>(L, cur, k, tsh, thr);
-    const int j = (int)(t - t0);
-    if ((j < R && (j & (j + 1)) == 0) || (j & (R - 1)) == R - 1)
-      refresh_bound<KCAP>(L, k, tsh, thr, sh, buf);
+  if (count > 0) {
+    v4i(*ring)[U][kWave] = ring_lds[w];
+    // Byte offsets of this lane's loads within a tile, and the byte
+    // distance between consecutive tiles of this workgroup.
+    uint32_t voff[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < U; ++u)
+      voff[u] = (uint32_t)((u * kBlock + threadIdx.x) * sizeof(v4i));
+    const char* first = reinterpret_cast<const char*>(body) +
+                        (int64_t)blk * kTileBytes<U>;
+    const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+      if (j < count) issue_tile_lds<U>(first + j * stride, voff, ring[j]);
+    for (int64_t i = 0; i < count; ++i) {
+      // Steady state: the kRing - 1 tiles after this one stay in flight.
+      wait_tile_loads<U, kRing>(i + kRing - 1 < count);
+      const int slot = (int)(i & (kRing - 1));
+      v4i d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = ring[slot][u][lane()];
+      wait_lds_reads();  // the slot is free once its data is in registers
+      if (i + kRing < count)
+        issue_tile_lds<U>(first + (i + kRing) * stride, voff, ring[slot]);
+      consume<KCAP, FIT, U>(L, d, k, tsh, thr);
+      if (refresh_due(i, R)) refresh_bound<false>(L, k, tsh, thr, sh);
+    }
   }
   // Elements outside the full tiles: the unaligned head and the tail.
   if (blk == p.grid - 1) {
@@ -381,11 +533,11 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       const int64_t i = base + threadIdx.x;
       int x = kI32Min;
       if (i < left) x = p.in[i < p.head ? i : p.covered + i];
-      admit<KCAP>(L, x, k, tsh, thr);
+      admit<KCAP, FIT>(L, x, k, tsh, thr);
     }
   }
-  refresh_bound<KCAP>(L, k, tsh, thr, sh, buf);
-  const int T = tsh;
+  refresh_bound<true>(L, k, tsh, thr, sh);
+  const int T = tsh;  // the same in every wave of the workgroup
 
   // ---- wave merge: each wave's top-k of its entries >= T ----------------
   {
@@ -410,14 +562,16 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
 
   // ---- block merge (wave 0): top-k of the four wave results -------------
   if (w == 0) {
-    constexpr int V = kWaves * KCAP / kWave;
+    constexpr int V = (kWaves * KCAP + kWave - 1) / kWave;
     unsigned u[V];
     int mx = kI32Min;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const int q = lane() + kWave * j;
       const int ww = q / KCAP, o = q % KCAP;
-      const int v = o < sh.wave_cnt[ww] ? sh.wave_out[ww][o] : kI32Min;
+      const int v = (ww < kWaves && o < sh.wave_cnt[ww < kWaves ? ww : 0])
+                        ? sh.wave_out[ww][o]
+                        : kI32Min;
       u[j] = bias(v);
       mx = max(mx, v);
     }
@@ -429,25 +583,20 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     for (int j = 0; j < V; ++j) {
       const bool q = u[j] > g;
       const uint64_t b = ballot(q);
-      if (q) dst[base + lanes_below(b)] = unbias(u[j]);
+      if (q) st_agent(dst + base + lanes_below(b), unbias(u[j]));
       base += popc(b);
     }
-    for (int j = lane(); j < k - base; j += kWave) dst[base + j] = unbias(g);
+    for (int j = lane(); j < k - base; j += kWave)
+      st_agent(dst + base + j, unbias(g));
     if (lane() == 0) {
-      p.heads[blk] = mx;
-      p.kths[blk] = unbias(g);
+      st_agent(p.heads + blk, mx);
+      st_agent(p.kths + blk, unbias(g));
     }
   }
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    sh.is_last = atomicAdd(p.ticket, 1u) == (unsigned)(p.grid - 1);
-  __syncthreads();
-  if (!sh.is_last) return;
-  __threadfence();
-  topk_stage2<KCAP>(p, sh);
+  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
+  topk_stage2(p, sh, *reinterpret_cast<Stage2Lds*>(&ring_lds[0][0][0][0]));
 }
 
 }  // namespace ltk

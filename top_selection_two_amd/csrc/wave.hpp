@@ -51,16 +51,32 @@ __device__ __forceinline__ int unbias(unsigned u) {
   return (int)(u ^ 0x80000000u);
 }
 
+// Wave-wide max / min with DPP row shifts and row broadcasts: after the
+// four row_shr steps lane 15 of every 16-lane row holds that row's
+// reduction, the two broadcasts carry it across rows, and lane 63 ends with
+// the result of the whole wave.  Lanes without a source keep their own value
+// (old = v), which max and min ignore.
+#define LTK_DPP(v, ctrl, rows) \
+  __builtin_amdgcn_update_dpp((v), (v), (ctrl), (rows), 0xf, false)
+
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return uni(v);
+  v = max(v, LTK_DPP(v, 0x111, 0xf));  // row_shr:1
+  v = max(v, LTK_DPP(v, 0x112, 0xf));  // row_shr:2
+  v = max(v, LTK_DPP(v, 0x114, 0xf));  // row_shr:4
+  v = max(v, LTK_DPP(v, 0x118, 0xf));  // row_shr:8
+  v = max(v, LTK_DPP(v, 0x142, 0xa));  // row_bcast:15 into rows 1, 3
+  v = max(v, LTK_DPP(v, 0x143, 0xc));  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return uni(v);
+  v = min(v, LTK_DPP(v, 0x111, 0xf));
+  v = min(v, LTK_DPP(v, 0x112, 0xf));
+  v = min(v, LTK_DPP(v, 0x114, 0xf));
+  v = min(v, LTK_DPP(v, 0x118, 0xf));
+  v = min(v, LTK_DPP(v, 0x142, 0xa));
+  v = min(v, LTK_DPP(v, 0x143, 0xc));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ int64_t wave_sum(int64_t v) {
@@ -71,6 +87,157 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
     v += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
   }
   return v;
+}
+
+// Keep the compiler (IR passes and the machine scheduler) from moving
+// memory operations or any instruction across this point.
+// The streaming loops use it so that the loads of the next tile are not
+// hoisted above the use of the current one: hoisting would leave both
+// buffers live at once, force register copies at the loop latch, and the
+// copies would wait for the loads that were meant to stay in flight.
+__device__ __forceinline__ void sched_fence() {
+  asm volatile("" ::: "memory");  // loads stay on their side at IR level
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Optimisation barriers on values.  ready(d) marks the point where the
+// loaded tile d is first needed: every use of d comes after it, so the
+// wait for d's loads is placed there and not earlier.  pin(x) keeps the
+// compiler from reassociating work on x across this point (for example
+// folding two tiles into one expression tree, which would make the first
+// tile wait for the second tile's loads).
+template <int U>
+__device__ __forceinline__ void ready(v4i (&d)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) asm volatile("" : "+v"(d[u]));
+}
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// The tiles of one workgroup: tile i of workgroup blk is global tile
+// blk + i * grid of the 16-byte-aligned body; a tile is kBlock lanes x U
+// 16-byte vectors, lane-contiguous per vector (each wave instruction reads
+// 1 KiB of consecutive bytes).  Plain scalars rather than a struct, so that
+// nothing about the stream ever lives in private memory.
+__device__ __forceinline__ int64_t tiles_of(int64_t ntiles, int blk,
+                                            int grid) {
+  return blk < ntiles ? (ntiles - blk + grid - 1) / grid : 0;
+}
+
+// Load local tile i (clamped to the last one, count - 1, so that a prefetch
+// past the end re-reads a tile just read, an L2 hit, instead of branching).
+// Non-temporal: every byte is read exactly once.
+template <int U>
+__device__ __forceinline__ void load_tile(const v4i* __restrict__ body,
+                                          int blk, int grid, int64_t count,
+                                          int64_t i, v4i (&d)[U]) {
+  if (i > count - 1) i = count - 1;
+  const int64_t base = (blk + i * grid) * (int64_t)(kBlock * U) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    d[u] = __builtin_nontemporal_load(body + base + u * kBlock);
+}
+
+// Cross-workgroup hand-off without an agent-scope fence.
+//
+// The last workgroup to finish reads what every other workgroup published.
+// An agent-scope release fence would make that legal for plain stores, but
+// on this chip it writes back the whole L2 of the XCD, and a fence per
+// workgroup costs about 0.2 us each, serialised (it more than doubles the
+// time of a 400 MB streaming pass at 1024 workgroups).  Instead, published
+// values are written with agent-scope atomic stores, which are coherent at
+// device level (write-through, sc1), every wave waits for its own memory
+// operations to complete before the workgroup takes its ticket, and the
+// reader uses agent-scope atomic loads (sc1), which do not hit stale lines.
+template <class T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void drain_memory_ops() {
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Take the workgroup's completion ticket after its published stores have
+// completed; true in exactly one workgroup, the last one.  Barriers inside:
+// call uniformly.  `flag` is an LDS word.
+__device__ __forceinline__ bool last_to_finish(unsigned* ticket, int grid,
+                                               int* flag) {
+  drain_memory_ops();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = atomicAdd(ticket, 1u) == (unsigned)(grid - 1);
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Direct global -> LDS streaming (gfx950 global_load_lds_dwordx4).  Each
+// lane's 16 bytes land at M0 + 16 * lane, so one instruction moves 1 KiB
+// of consecutive HBM bytes into 1 KiB of consecutive LDS without passing
+// through VGPRs.  Issued non-temporal: every byte is read exactly once.
+//
+// The loads are written as inline assembly on purpose.  The compiler's own
+// tracking of LDS-targeting loads makes it wait for ALL of them (vmcnt(0))
+// before any LDS access that might alias, which would drain the ring at
+// every tile.  Hidden in asm, they are ordered by hand instead:
+// wait_tile_loads() (an explicit vmcnt wait) before a tile's slot is read,
+// and wait_lds_reads() before a slot that was just read is refilled.  All
+// of these carry a memory clobber, so the compiler moves no memory access
+// across them and keeps the reads of the ring (whose address escapes into
+// the asm).  M0 is saved and restored around each load, so the compiler's
+// view of M0 is unchanged.  The streaming loop issues no other vector-memory
+// instruction, so vmcnt counts exactly the outstanding tile loads.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(
+      (const __attribute__((address_space(3))) void*)p);
+}
+
+// Issue the U loads of one tile: `tile` is the tile's first byte (a
+// wave-uniform address, kept in SGPRs), `voff[u]` this lane's byte offset
+// within it for load u, and `lds` the wave's slot in LDS.  No per-tile
+// vector address arithmetic.
+template <int U>
+__device__ __forceinline__ void issue_tile_lds(const char* tile,
+                                               const uint32_t (&voff)[U],
+                                               v4i (*slot)[kWave]) {
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)lds_offset(&slot[0][0]));
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[lds]\n\t"
+        "global_load_lds_dwordx4 %[vo], %[base] nt\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved)
+        : [lds] "s"(lds + u * kWave * 16u), [vo] "v"(voff[u]),
+          [base] "s"(tile)
+        : "memory");
+  }
+}
+
+// Before a tile's slot is read: wait until at most the loads of the tiles
+// issued after it are pending.  In the steady state that is kRing - 1
+// tiles of U loads; near the end of the stream everything is drained.
+template <int U, int RING>
+__device__ __forceinline__ void wait_tile_loads(bool steady) {
+  static_assert(U * (RING - 1) <= 63, "vmcnt is a 6-bit counter");
+  if (steady)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(U * (RING - 1)) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lds_reads() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Bitwise radix selection.  Given a wave-uniform range [lo, hi] (biased
@@ -93,6 +260,31 @@ __device__ __forceinline__ unsigned radix_select(unsigned lo, unsigned hi,
     if (count_ge(c) >= k) prefix = c;
   }
   return prefix;
+}
+
+// The same search cut short after `steps` bits: the result is a value v
+// with count_ge(v) >= k that is <= the exact answer, and close to it (the
+// undecided low bits are zero).  Every prefix kept along the way satisfies
+// the count, and lo itself does (precondition), so max(prefix, lo) does.
+template <class CountGe>
+__device__ __forceinline__ unsigned radix_lower_bound(unsigned lo, unsigned hi,
+                                                      int k, int steps,
+                                                      CountGe count_ge) {
+  lo = uni(lo);
+  hi = uni(hi);
+  const unsigned diff = lo ^ hi;
+  if (diff == 0u) return lo;
+  const int top = 31 - __clz((int)diff);
+  unsigned prefix = lo & ~((2u << top) - 1u);
+  // Ties at the top (for example an input of equal values): if the largest
+  // value already has k values at or above it, it is the exact answer.
+  if (count_ge(hi) >= k) return hi;
+  const int last = top - steps + 1 > 0 ? top - steps + 1 : 0;
+  for (int b = top; b >= last; --b) {
+    const unsigned c = prefix | (1u << b);
+    if (count_ge(c) >= k) prefix = c;
+  }
+  return prefix > lo ? prefix : lo;
 }
 
 // Count over V biased values per lane held in registers.
