@@ -5,10 +5,10 @@
 One step is one full topk_i32 call (both stages; a single kernel launch) over
 the resident 1e8-element input.  The input is synthetic (seeded SplitMix64,
 uniform over the full int32 range, seed 3) and sits in HBM before timing
-starts.  W untimed calls, then K timed calls bracketed by device
-synchronisation; every timed call is also bracketed by its own pair of HIP
-events on the stream it is launched on, which gives the kernel's average
-launch duration for the roofline.  The result is checked against the CPU
+starts.  W untimed calls, then K timed back-to-back calls bracketed by device
+synchronisation and by a pair of HIP events on the stream they are launched
+on; each call is one kernel launch, so the event time over K is the kernel's
+average launch duration for the roofline.  The result is checked against the CPU
 oracle before timing, and the oracle itself is timed on the host cores as a
 reported baseline.
 
@@ -66,6 +66,122 @@ def measured_traffic():
     return c.get("traffic_bytes_per_launch")
 
 
+def summarize(run_dir: str, out_dir: str) -> None:
+    """Turn rocprofv3 CSV output into the committed summaries.
+
+    run_dir holds the three profiler runs made by the commands printed in
+    the summaries: trace/ (--kernel-trace --stats over a timed bench run),
+    fetch/ and write/ (--pmc FETCH_SIZE, --pmc WRITE_SIZE over --mode
+    counters).  The counter values (KiB per dispatch) are scaled by what the
+    same counter reads for the plain 400 MB device copy that --mode counters
+    runs first (torch's copy kernel), so that traffic is in bytes.
+    """
+    import csv
+    import glob
+
+    def rows(pattern):
+        files = glob.glob(os.path.join(run_dir, pattern), recursive=True)
+        if not files:
+            raise SystemExit("missing %s under %s" % (pattern, run_dir))
+        with open(files[0]) as f:
+            return list(csv.DictReader(f))
+
+    n = 100_000_000
+    copy_bytes = 4 * n
+
+    def counter(pattern, name):
+        per = {}
+        for r in rows(pattern):
+            if r["Counter_Name"] != name:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        topk = [v for kname, v in per.items() if "topk_kernel" in kname]
+        copy = [v for kname, v in per.items() if "copyBuffer" in kname]
+        if not topk or not copy:
+            raise SystemExit("counter %s: kernels not found" % name)
+        return (sum(topk[0]) / len(topk[0]), sum(copy[0]) / len(copy[0]),
+                [kname for kname in per if "topk_kernel" in kname][0])
+
+    fetch_topk, fetch_copy, kname = counter("fetch/**/*counter_collection.csv",
+                                            "FETCH_SIZE")
+    write_topk, write_copy, _ = counter("write/**/*counter_collection.csv",
+                                        "WRITE_SIZE")
+    f_scale = copy_bytes / fetch_copy   # bytes per counted unit (read side)
+    w_scale = copy_bytes / write_copy   # bytes per counted unit (write side)
+    traffic = fetch_topk * f_scale + write_topk * w_scale
+
+    stats = rows("trace/**/*kernel_stats.csv")
+    krow = [r for r in stats if "topk_kernel" in r["Name"]][0]
+    cmd_trace = ("rocprofv3 --kernel-trace --stats -d <run>/trace -o trace "
+                 "--output-format csv -- python3 bench.py --steps 200 "
+                 "--warmup 20 --no-cpu-baseline")
+    cmd_fetch = ("rocprofv3 --pmc FETCH_SIZE -d <run>/fetch -o fetch "
+                 "--output-format csv -- python3 bench.py --mode counters")
+    cmd_write = ("rocprofv3 --pmc WRITE_SIZE -d <run>/write -o write "
+                 "--output-format csv -- python3 bench.py --mode counters")
+    os.makedirs(out_dir, exist_ok=True)
+    data = {
+        "kernel": kname,
+        "workload": "top-20 of 1e8 int32, uniform full range, seed 3",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_size_kib_per_dispatch": fetch_topk,
+        "write_size_kib_per_dispatch": write_topk,
+        "copy_calibration": {
+            "bytes_read_and_written": copy_bytes,
+            "fetch_size_kib": fetch_copy, "write_size_kib": write_copy,
+            "bytes_per_fetch_unit": f_scale, "bytes_per_write_unit": w_scale},
+        "traffic_bytes_per_launch": round(traffic),
+        "algorithmic_bytes_per_launch": 4 * n + 4 * K,
+        "commands": [cmd_fetch, cmd_write],
+    }
+    with open(os.path.join(out_dir, "topk_counters_full_1e8_k20.json"),
+              "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    lines = [
+        "# topk_kernel on top-20 of 1e8 int32 (uniform full range, seed 3)",
+        "",
+        "Kernel trace (rocprofv3 --kernel-trace --stats), from the repository "
+        "root:",
+        "",
+        "    " + cmd_trace,
+        "",
+        "| kernel | calls | average ns | min ns | max ns | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in stats:
+        lines.append("| %s | %s | %s | %s | %s | %s |" % (
+            r["Name"][:60], r["Calls"], r["AverageNs"], r["MinNs"],
+            r["MaxNs"], r.get("Percentage", "")))
+    avg_ns = float(krow["AverageNs"])
+    lines += [
+        "",
+        "topk_kernel average: %.2f us -> algorithmic %.0f GB/s (%.1f %% of "
+        "8 TB/s)." % (avg_ns / 1e3, (4 * n + 4 * K) / avg_ns,
+                      100 * (4 * n + 4 * K) / avg_ns / 8000.0),
+        "",
+        "HBM traffic (rocprofv3 --pmc, one counter per run):",
+        "",
+        "    " + cmd_fetch,
+        "    " + cmd_write,
+        "",
+        "| counter | topk_kernel (KiB/dispatch) | 400 MB copy (KiB) | bytes per "
+        "unit | topk bytes |",
+        "|---|---|---|---|---|",
+        "| FETCH_SIZE | %.1f | %.1f | %.4f | %.0f |" % (
+            fetch_topk, fetch_copy, f_scale, fetch_topk * f_scale),
+        "| WRITE_SIZE | %.1f | %.1f | %.4f | %.0f |" % (
+            write_topk, write_copy, w_scale, write_topk * w_scale),
+        "",
+        "Traffic per launch: %.0f bytes = %.4f x the 4N + 4k algorithmic "
+        "bytes." % (traffic, traffic / (4 * n + 4 * K)),
+        "",
+    ]
+    with open(os.path.join(out_dir, "topk_full_1e8_k20.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("wrote summaries to", out_dir)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -100,7 +216,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grid", type=int, default=0,
                     help="stage-1 workgroups (0 = library default)")
+    ap.add_argument("--summarize", metavar="RUN_DIR",
+                    help="write profiles/ summaries from rocprofv3 output "
+                         "(CPU only)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (requested --gpus %d)" % args.gpus, file=sys.stderr)
@@ -150,18 +272,22 @@ def main():
         ltk.topk(xd, K, out=out)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: K back-to-back calls on the stream, bracketed by device
+    # synchronisation (wall clock) and by a pair of HIP events recorded on
+    # the same stream.  Each call is exactly one kernel launch, so the event
+    # time divided by K is the kernel's average launch duration (including
+    # the short gaps between back-to-back launches).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    ev0.record(stream)
+    for _ in range(args.steps):
         ltk.topk(xd, K, out=out)
-        ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    avg_launch_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = n * args.steps / wall
 
@@ -210,7 +336,6 @@ def main():
             "k": K,
             "grid": ltk.grid_for(n),
             "kernel_ms_avg": round(avg_launch_ms, 5),
-            "kernel_ms_min": round(min(launch_ms), 5),
             "hbm_gbps_per_step": round(algo_bytes / (ms_per_step * 1e-3) / 1e9,
                                        1),
         },
