@@ -146,6 +146,22 @@ def test_special_values(ltk, pattern):
     check_reduce(ltk, x)
 
 
+@pytest.mark.parametrize("copies", [300, 2_000, 20_000])
+@pytest.mark.parametrize("k", [20, 32])
+def test_ties_below_a_unique_maximum(ltk, copies, k):
+    # One maximum, then `copies` equal values just below it, scattered over
+    # the whole input: the certified bound lands on the tied value, so the
+    # merge of the block candidates sees about `copies` survivors (a few
+    # hundred, a few thousand, or more than fit on chip).
+    n = 4_000_037
+    x = synth.fill(600 + copies, n, -10**6, 10**6)
+    idx = np.unique(synth.fill(700 + copies, copies, 0, n).astype(np.int64))
+    x[idx] = 10**6 + 3
+    x[n // 3] = 10**6 + 9
+    check_topk(ltk, x, k)
+    check_topk(ltk, x, 100)
+
+
 def test_sum_exceeds_int32(ltk):
     x = np.full(3_000_000, I32_MAX, np.int32)
     check_reduce(ltk, x)

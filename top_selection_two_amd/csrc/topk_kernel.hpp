@@ -12,10 +12,11 @@
 //          memory for the final steps).
 //
 // What differs from the pages, and why (gfx950, wave64):
-//  * Each lane streams non-temporal 16-byte loads (global_load_dwordx4), U
-//    of them per tile; tiles are dealt round-robin to the workgroups and
-//    double-buffered in registers so the next tile is in flight while the
-//    current one is examined.
+//  * Tiles (256 lanes x U x 16 bytes) are dealt round-robin to the
+//    workgroups; each wave streams its quarter of every tile straight into
+//    its own LDS ring (global-to-LDS loads, non-temporal) kRing tiles ahead
+//    of the one it examines, so inserting never leaves the memory pipe
+//    empty.  A lane's first tile fills its list through a sorting network.
 //  * The insertion test uses a shared, *certified* lower bound T besides the
 //    lane's own k-th entry.  T is certified when the lists of this workgroup
 //    jointly hold at least k entries >= T; then every element x <= T can be
@@ -26,18 +27,17 @@
 //    16-element group is rejected by one max-of-16 and one wave vote.
 //  * Per-lane lists stay in VGPRs (static indexing, capacity KCAP >= k);
 //    insertion is a branch-free max/min bubble that stops at k.
-//  * Merges drop everything below T and select by counting rather than by
-//    sorting: the wave finds the k-th largest live value g (radix select
-//    over ballots), keeps the entries > g and pads with copies of g; wave 0
-//    then does the same over the four wave results.  The result of a block
-//    is its exact top-k as a multiset (unordered), plus its max and k-th.
+//  * The workgroup's candidates are its exact top-k: the list entries that
+//    reach the final bound T (usually about k of them) are gathered in LDS
+//    and each is ranked by counting, which also orders them; only under
+//    heavy ties do the waves fall back to selection (radix select over
+//    ballots).  Each workgroup also publishes its largest candidate and its
+//    k-th.
 //  * Stage 2 runs in the last workgroup to finish (ticket counter and
 //    agent-coherent stores and loads, see last_to_finish), not in a second
-//    launch.  It first derives a certified
-//    bound T2 from the block maxima (k-th largest of them) and the block
-//    k-th values (their max), keeps only candidates >= T2, selects the k-th
-//    largest g among them, and writes the < k values above g in descending
-//    order followed by copies of g.
+//    launch.  It keeps only candidates >= a certified bound T2 (k
+//    candidates are known to reach it) and ranks the survivors by counting;
+//    see topk_stage2.
 #pragma once
 
 #include "wave.hpp"
@@ -53,30 +53,42 @@ struct TopkParams {
   int k;
   int grid;          // stage-1 workgroups
   int refresh;       // certificate refresh period, in tiles (power of 2)
-  int* cand;         // [grid * k]  per-block candidates (unordered)
+  int* cand;         // [grid * k]  per-block candidates
   int* heads;        // [grid]      max of each block's candidates
   int* kths;         // [grid]      k-th largest of each block's candidates
   unsigned* ticket;  // completion counter; 0 between calls
   int* out;          // [k]         result, descending
 };
 
-constexpr int kSurvCap = 4096;  // stage-2 survivors staged in LDS
+constexpr int kSurvCap = 1024;  // stage-2 survivors staged in LDS
 constexpr int kRing = 4;        // tiles in flight per wave (power of 2)
 template <int U>
 constexpr int64_t kTileBytes = (int64_t)kBlock * U * 16;  // one tile
 
 // Stage-2 scratch in LDS.  It lives in the memory of the last workgroup's
 // streaming ring (declared separately, see topk_kernel), which is idle by
-// then.
+// then.  `heads` and `cand` receive every block summary and candidate when
+// grid*k <= kDirectCand.
+constexpr int kDirectCand = 12288;
 struct Stage2Lds {
   int surv[kSurvCap];
   int gt[kMaxK];
   int blocks[kMaxGrid];  // blocks whose maximum reaches T2
+  int heads[kMaxGrid];
+  int cand[kDirectCand];
+  alignas(16) int gmax[kWave];  // group maxima of the block maxima
+  int gmax_rank[kWave];
+  int surv_rank[kWave];
 };
 
 template <int KCAP>
 struct TopkShared {
   unsigned heads[kBlock];  // snapshot of the lane heads (biased)
+  // List entries >= the final bound, gathered from all waves, and their
+  // ranks (see block_rank64).
+  alignas(16) int blist[kBlock];
+  int ranks[kWave];
+  int bcnt;
   int wave_out[kWaves][KCAP];
   int wave_cnt[kWaves];
   int red[2][kWaves];
@@ -195,6 +207,46 @@ __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
   }
 }
 
+// The first tile of a lane's stream goes straight into its (empty) list:
+// a bitonic sorting network orders the 4U values (descending, no branches,
+// 2 instructions per compare-exchange), and the list keeps the largest
+// min(KCAP, 4U) of them -- the same list that inserting them one by one
+// would build.
+template <int KCAP, int U>
+__device__ __forceinline__ void init_list(int (&L)[KCAP], const v4i (&d)[U],
+                                          int& thr) {
+  constexpr int M = 4 * U;
+  static_assert((M & (M - 1)) == 0, "the network needs a power of two");
+  int v[M];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    v[4 * u + 0] = d[u].x;
+    v[4 * u + 1] = d[u].y;
+    v[4 * u + 2] = d[u].z;
+    v[4 * u + 3] = d[u].w;
+  }
+#pragma unroll
+  for (int size = 2; size <= M; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const int hi = max(v[i], v[j]);
+          const int lo = min(v[i], v[j]);
+          const bool desc = (i & size) == 0;
+          v[i] = desc ? hi : lo;
+          v[j] = desc ? lo : hi;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) L[i] = i < M ? v[i] : kI32Min;
+  thr = KCAP <= M ? L[KCAP - 1] : kI32Min;
+}
+
 // Raise a certified bound to the k-th largest of the workgroup's 256 lane
 // heads (k <= 128 < 256).
 //
@@ -293,20 +345,188 @@ __device__ __forceinline__ void scan_flagged(const TopkParams& p,
   }
 }
 
-// Stage 2, run by the last workgroup: merge grid*k candidates into out[0..k).
+// ---- stage 2, run by the last workgroup ---------------------------------
+// Merge grid*k candidates into out[0..k).  First a gather leaves the
+// survivors -- every candidate >= a certified bound T2 -- in LDS, then the
+// result is written from them.
+//
+// Two gathers:
+//  * direct (grid*k <= kDirectCand, k <= 64): every block maximum and
+//    candidate is copied into LDS at once (device-coherent global-to-LDS
+//    loads, one round trip to memory).  T2 is the k-th largest of 64 group
+//    maxima over disjoint groups of blocks: k distinct candidates reach it.
+//  * flagged: wave 0 reads the block summaries first (T2 from the k-th
+//    largest block maximum and the largest block k-th value), then only the
+//    candidates of the blocks whose maximum reaches T2 are read.
+// If more than kSurvCap candidates survive the direct gather (heavy ties
+// just below the maximum), the flagged gather runs instead; it can count
+// survivors that do not fit in LDS by rescanning the flagged blocks.
+//
+// This code runs once per call, in one workgroup, mostly from a cold
+// instruction cache, so it is written as short loops over LDS rather than
+// long unrolled sequences.
+
+struct Stage2Bound {
+  int t2;     // certified: at least k candidates are >= t2
+  int mx;     // the largest candidate
+  int m;      // survivors (>= t2); those beyond kSurvCap were not stored
+  int total;  // candidates of the flagged blocks (flagged gather only)
+};
+
+// Copy 1 KiB of device memory that other workgroups published (with
+// agent-scope stores, before their ticket) into LDS: 16 bytes per lane,
+// lane-contiguous, a device-coherent load (sc1) like ld_agent.
+__device__ __forceinline__ void copy_1k_to_lds(const char* src, void* dst) {
+  const uint32_t lds =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(dst));
+  const uint32_t voff = (uint32_t)lane() * 16u;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lds]\n\t"
+      "global_load_lds_dwordx4 %[vo], %[base] sc1\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [lds] "s"(lds), [vo] "v"(voff), [base] "s"(src)
+      : "memory");
+}
+
+// Ranks by counting, with the whole workgroup: the rank of vals[i] among
+// vals[0..n) (n <= 64) is how many of them are larger, or equal at a lower
+// index, so the ranks of vals[0..n) are 0..n-1 in descending order.
+// Thread t compares value t % 64 with the 16 values 16 * (t / 64) ..
+// 16 * (t / 64) + 15; the four partial counts meet in ranks[] by LDS
+// atomics.  vals: 16-byte aligned, 64 readable slots (those past n are
+// ignored); ranks: 64 slots, zero on entry (set before an earlier
+// barrier).  One barrier inside: call uniformly.  Returns this thread's
+// value (valid for threads < n); rank_of(i) is then ranks[i].
+// Every step is independent vector work: no scalar round trips per
+// comparison, which is what a serial loop over lanes would cost.
+__device__ __forceinline__ int block_rank64(const int* vals, int n,
+                                            int* ranks) {
+  const int i = threadIdx.x & (kWave - 1);
+  const int g = threadIdx.x / kWave;
+  const int v = vals[i];
+  const v4i* q = reinterpret_cast<const v4i*>(vals + 16 * g);
+  int r = 0;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const v4i o4 = q[qq];
+    const int o[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 16 * g + 4 * qq + e;
+      r += (j < n) & ((o[e] > v) | ((o[e] == v) & (j < i)));
+    }
+  }
+  if (i < n && r > 0) atomicAdd(&ranks[i], r);
+  __syncthreads();
+  return v;
+}
+
 template <class SH>
-__device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
-                                            Stage2Lds& s2) {
+__device__ __forceinline__ Stage2Bound gather_direct(const TopkParams& p,
+                                                     SH& sh, Stage2Lds& s2) {
+  const int G = p.grid, k = p.k, tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int total = G * k;
+  // Block maxima and candidates into LDS, in whole KiB chunks: the source
+  // areas hold kMaxGrid and more than kDirectCand ints, so the last chunk
+  // of each stays inside them; ints past G or `total` are ignored.
+  constexpr int kChunkInts = 1024 / 4;
+  const int hchunks = (G + kChunkInts - 1) / kChunkInts;
+  const int chunks = hchunks + (total + kChunkInts - 1) / kChunkInts;
+  for (int c = w; c < chunks; c += kWaves) {
+    const bool h = c < hchunks;
+    const int o = (h ? c : c - hchunks) * kChunkInts;
+    const int* src = h ? p.heads + o : p.cand + o;
+    copy_1k_to_lds(uni_ptr(reinterpret_cast<const char*>(src)),
+                   h ? s2.heads + o : s2.cand + o);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // T2 = the k-th largest of 64 group maxima over disjoint groups of blocks
+  // (distinct blocks, so k candidates reach T2).  Wave 0 forms the groups:
+  // lane l takes blocks l*per .. l*per + per - 1, per being G/64 rounded up
+  // to a multiple of 4 (16-byte LDS loads; slots past those, or past G, are
+  // not its blocks).  Empty groups hold INT_MIN, the trivial bound.
+  if (w == 0) {
+    constexpr int VH = kMaxGrid / kWave;
+    const int per = (((G + kWave - 1) / kWave) + 3) & ~3;
+    const v4i* h4 = reinterpret_cast<const v4i*>(s2.heads + lane() * per);
+    int gm = kI32Min;
+#pragma unroll
+    for (int q = 0; q < VH / 4; ++q) {
+      if (4 * q < per) {
+        const v4i t = h4[q];
+        const int b = lane() * per + 4 * q;
+        gm = max(gm, b < G ? t.x : kI32Min);
+        gm = max(gm, b + 1 < G ? t.y : kI32Min);
+        gm = max(gm, b + 2 < G ? t.z : kI32Min);
+        gm = max(gm, b + 3 < G ? t.w : kI32Min);
+      }
+    }
+    s2.gmax[lane()] = gm;
+    const int mx = wave_max(gm);
+    if (lane() == 0) {
+      sh.bcast[1] = mx;
+      sh.bcast[2] = 0;  // survivor count
+      sh.bcast[5] = 0;  // flagged blocks
+    }
+  }
+  __syncthreads();
+  {
+    const int gv = block_rank64(s2.gmax, kWave, s2.gmax_rank);
+    if (tid < kWave && s2.gmax_rank[tid] == k - 1) sh.bcast[0] = gv;
+  }
+  __syncthreads();
+  const int T2 = sh.bcast[0];
+  // The blocks whose maximum reaches T2 (no other block can contribute).
+  for (int b0 = 0; b0 < G; b0 += kBlock) {
+    const int b = b0 + tid;
+    const bool f = b < G && s2.heads[b] >= T2;
+    wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
+  }
+  __syncthreads();
+  Stage2Bound r;
+  r.t2 = sh.bcast[0];
+  r.mx = sh.bcast[1];
+  r.total = 0;
+  r.m = 0;
+  if (r.t2 == r.mx) return r;  // the caller writes k copies of mx
+
+  // Survivors: the candidates >= T2 of the flagged blocks.  Candidates
+  // equal to INT_MIN are left out: if T2 is INT_MIN and fewer than k
+  // candidates exceed it, the result is padded with INT_MIN, which is the
+  // same.
+  const int tf = r.t2 == kI32Min ? kI32Min + 1 : r.t2;
+  const int nf = sh.bcast[5] * k;
+  for (int i0 = 0; i0 < nf; i0 += kBlock) {
+    const int i = i0 + tid;
+    int v = kI32Min;
+    if (i < nf) {
+      const int fb = i / k;
+      v = s2.cand[s2.blocks[fb] * k + (i - fb * k)];
+    }
+    wave_append(v >= tf, v, &sh.bcast[2], s2.surv, kSurvCap);
+  }
+  __syncthreads();
+  r.m = sh.bcast[2];
+  return r;
+}
+
+template <class SH>
+__device__ __forceinline__ Stage2Bound gather_flagged(const TopkParams& p,
+                                                      SH& sh, Stage2Lds& s2) {
   const int G = p.grid, k = p.k;
   const int w = threadIdx.x / kWave;
-  const int tid = threadIdx.x;
-
-  // (A) wave 0: a certified bound T2 from the block summaries, and the list
-  // of blocks whose maximum reaches it (no other block can contribute).
+  // Wave 0: the bound from the block summaries.
   //   T2b = max over blocks of their k-th candidate (that block alone holds
   //         k candidates >= it);
   //   T2a = k-th largest block maximum (k distinct candidates >= it);
   //   T2  = max(T2a, T2b).
+  // Only blocks whose maximum reaches T2 can contribute.
   if (w == 0) {
     constexpr int VH = kMaxGrid / kWave;
     unsigned uh[VH];
@@ -339,76 +559,92 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
       if (f) s2.blocks[nb + lanes_below(m)] = b;
       nb += popc(m);
     }
-    const int total = nb * k;  // candidates of the flagged blocks
-    int done = 1;
-    if (t2 == mx) {
-      // At least k candidates are >= T2 and none exceeds mx: k copies of mx.
-      for (int j = lane(); j < k; j += kWave) p.out[j] = mx;
-    } else if (total <= 8 * kWave) {
-      // Few survivors: this wave finishes alone, in registers.
-      constexpr int V = 8;
-      unsigned u[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const int q = lane() + kWave * j;
-        const int qq = q < total ? q : total - 1;
-        const int fb = qq / k;
-        const int v = ld_agent(p.cand + (int64_t)s2.blocks[fb] * k + (qq - fb * k));
-        u[j] = (q < total && v >= t2) ? bias(v) : 0u;
-      }
-      const unsigned g = radix_select(bias(t2), bias(mx), k, RegCount<V>{u});
-      const int gs = unbias(g);
-      int ngt = 0;  // values above g, compacted into gt[]
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const bool a = u[j] > g;
-        const uint64_t m = ballot(a);
-        if (a) s2.gt[ngt + lanes_below(m)] = unbias(u[j]);
-        ngt += popc(m);
-      }
-      for (int i = lane(); i < k; i += kWave) {
-        if (i < ngt) {
-          const int v = s2.gt[i];
-          int r = 0;
-          for (int j = 0; j < ngt; ++j) {
-            const int o = s2.gt[j];
-            r += (o > v) | ((o == v) & (j < i));
-          }
-          p.out[r] = v;
-        } else {
-          p.out[i] = gs;
-        }
-      }
-    } else {
-      done = 0;
-    }
     if (lane() == 0) {
-      sh.bcast[6] = done;
+      sh.bcast[0] = t2;
+      sh.bcast[1] = mx;
+      sh.bcast[2] = 0;  // survivor count
       sh.bcast[5] = nb;
-      sh.bcast[0] = t2;  // T2
-      sh.bcast[1] = mx;  // largest candidate
-      sh.bcast[2] = 0;   // survivor count
-      sh.bcast[3] = 0;   // count of values above g
     }
   }
   __syncthreads();
-  if (sh.bcast[6]) {
-    if (tid == 0) st_agent(p.ticket, 0u);
-    return;
-  }
-  // General path: many flagged candidates (heavy ties near the top).
-  const int T2 = sh.bcast[0], mx = sh.bcast[1];
-  const int total = sh.bcast[5] * k;
-
-  // (B) survivors >= T2 into LDS (only the first kSurvCap are kept).
-  scan_flagged(p, s2.blocks, total, [&](bool ok, int c) {
+  Stage2Bound r;
+  r.t2 = sh.bcast[0];
+  r.mx = sh.bcast[1];
+  r.total = sh.bcast[5] * k;
+  r.m = 0;
+  if (r.t2 == r.mx) return r;
+  // Survivors >= T2 into LDS (only the first kSurvCap are kept).
+  const int T2 = r.t2;
+  scan_flagged(p, s2.blocks, r.total, [&](bool ok, int c) {
     wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv, kSurvCap);
   });
   __syncthreads();
-  const int m = sh.bcast[2];
-  const bool in_lds = m <= kSurvCap;
+  r.m = sh.bcast[2];
+  return r;
+}
 
-  // (C) g = k-th largest survivor (there are >= k: T2 is certified).
+// Stage 2 proper: gather, select g, write the result, re-arm the ticket.
+template <class SH>
+__device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
+                                            Stage2Lds& s2) {
+  const int k = p.k;
+  const int w = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+
+  if (tid < kWave) {  // rank counters (a barrier follows in either gather)
+    s2.gmax_rank[tid] = 0;
+    s2.surv_rank[tid] = 0;
+  }
+  Stage2Bound r;
+  // The direct gather certifies T2 from 64 group maxima: it needs k <= 64.
+  bool direct = (int64_t)p.grid * k <= kDirectCand && k <= kWave;
+  if (direct) {
+    r = gather_direct(p, sh, s2);
+    if (r.t2 != r.mx && r.m > kSurvCap) {
+      direct = false;
+      __syncthreads();  // LDS reuse by the second gather
+    }
+  }
+  if (!direct) r = gather_flagged(p, sh, s2);
+  const int T2 = r.t2, mx = r.mx, m = r.m, total = r.total;
+
+  if (T2 == mx) {
+    // At least k candidates are >= T2 and none exceeds mx: k copies of mx.
+    for (int j = tid; j < k; j += kBlock) p.out[j] = mx;
+    if (tid == 0) st_agent(p.ticket, 0u);
+    return;
+  }
+  // Few survivors (the usual case): each is ranked by counting, so the
+  // result comes out in order with no selection step.  Equal values get
+  // consecutive ranks.  If T2 was INT_MIN, fewer than k may have survived:
+  // the rest of the result is INT_MIN.
+  if (m <= kWave) {
+    const int v = block_rank64(s2.surv, m, s2.surv_rank);
+    if (tid < m) {
+      const int rk = s2.surv_rank[tid];
+      if (rk < k) p.out[rk] = v;
+    }
+    for (int j = m + tid; j < k; j += kBlock) p.out[j] = kI32Min;
+    if (tid == 0) st_agent(p.ticket, 0u);
+    return;
+  }
+  if (m <= kBlock) {
+    const int v = tid < m ? s2.surv[tid] : kI32Min;
+    int rk = 0;
+    for (int j = 0; j < m; ++j) {
+      const int o = s2.surv[j];
+      rk += (o > v) | ((o == v) & (j < tid));
+    }
+    if (tid < m && rk < k) p.out[rk] = v;
+    for (int j = m + tid; j < k; j += kBlock) p.out[j] = kI32Min;
+    if (tid == 0) st_agent(p.ticket, 0u);
+    return;
+  }
+
+  // Many survivors (heavy ties near the top): select g, the k-th largest
+  // survivor (there are >= k: T2 is certified), by counting.
+  const bool in_lds = m <= kSurvCap;
+  if (tid == 0) sh.bcast[3] = 0;  // count of values above g
   unsigned g;
   if (m <= 8 * kWave) {
     if (w == 0) {
@@ -441,7 +677,7 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
   }
   const int gs = unbias(g);
 
-  // (D) values above g (fewer than k), ranked; then copies of g.
+  // Values above g (fewer than k), ranked; then copies of g.
   if (in_lds) {
     for (int base = 0; base < m; base += kBlock) {
       const int i = base + tid;
@@ -457,12 +693,12 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
   const int ngt = sh.bcast[3];
   if (tid < ngt) {
     const int v = s2.gt[tid];
-    int r = 0;
+    int rk = 0;
     for (int j = 0; j < ngt; ++j) {
       const int o = s2.gt[j];
-      r += (o > v) | ((o == v) & (j < tid));
+      rk += (o > v) | ((o == v) & (j < tid));
     }
-    p.out[r] = v;
+    p.out[rk] = v;
   } else if (tid < k) {
     p.out[tid] = gs;
   }
@@ -487,6 +723,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   int tsh = kI32Min;  // this wave's certified bound
   int thr = kI32Min;  // this lane's test: max(its list's last entry, tsh)
   sh.heads[threadIdx.x] = 0u;  // biased INT_MIN: the weakest valid head
+  if (threadIdx.x == 0) sh.bcnt = 0;
+  if (threadIdx.x < kWave) sh.ranks[threadIdx.x] = 0;
   __syncthreads();
 
   // ---- stage 1: stream this workgroup's tiles ---------------------------
@@ -522,7 +760,10 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       wait_lds_reads();  // the slot is free once its data is in registers
       if (i + kRing < count)
         issue_tile_lds<U>(first + (i + kRing) * stride, voff, ring[slot]);
-      consume<KCAP, FIT, U>(L, d, k, tsh, thr);
+      if (i == 0)
+        init_list<KCAP, U>(L, d, thr);
+      else
+        consume<KCAP, FIT, U>(L, d, k, tsh, thr);
       if (refresh_due(i, R)) refresh_bound<false>(L, k, tsh, thr, sh);
     }
   }
@@ -536,61 +777,118 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       admit<KCAP, FIT>(L, x, k, tsh, thr);
     }
   }
-  refresh_bound<true>(L, k, tsh, thr, sh);
-  const int T = tsh;  // the same in every wave of the workgroup
+  // One more refresh of this wave's bound from the lane-head snapshot (no
+  // barrier: the bound is certified whatever the other waves are doing).
+  refresh_bound<false>(L, k, tsh, thr, sh);
+  const int T = tsh;  // certified for the workgroup; may differ per wave
+  int* dst = p.cand + (int64_t)blk * k;
 
-  // ---- wave merge: each wave's top-k of its entries >= T ----------------
+  // ---- block candidates: the workgroup's exact top-k ---------------------
+  // The entries >= T among the first k of every list include the
+  // workgroup's top-k (T is at most its k-th largest value, and no list
+  // entry past position k can be among them), and there are at least k of
+  // them.  Usually they are few (about k): they are gathered in LDS and
+  // each thread ranks one by counting, which writes the top-k in
+  // descending order.  With heavy ties there can be more than fit; then
+  // the waves select instead.
   {
-    const int live = list_count_ge<KCAP>(L, k, T);
-    int cnt;
-    if (live <= k) {
-      list_emit<KCAP>(L, k, T, false, sh.wave_out[w], KCAP);
-      cnt = live;
-    } else {
-      const int hi = wave_max(L[0]);
-      const unsigned g =
-          radix_select(bias(T), bias(hi), k, ListCount<KCAP>{L, k});
-      const int gs = unbias(g);
-      const int above = list_emit<KCAP>(L, k, gs, true, sh.wave_out[w], KCAP);
-      for (int j = lane(); j < k - above; j += kWave)
-        sh.wave_out[w][above + j] = gs;
-      cnt = k;
+    // Level by level while some lane reaches T, and only until the LDS
+    // list has overflowed (the count keeps growing past kBlock then, which
+    // is all the fallback needs to know).
+    bool more = true;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) {
+      if (more) {
+        const bool q = i < k && L[i] >= T;
+        const uint64_t b = ballot(q);
+        more = b != 0;
+        if (more) {
+          int base = 0;
+          if (lane() == 0) base = atomicAdd(&sh.bcnt, popc(b));
+          base = uni(base);
+          const int pos = base + lanes_below(b);
+          if (q && pos < kBlock) sh.blist[pos] = L[i];
+          more = base + popc(b) < kBlock;
+        }
+      }
     }
-    if (lane() == 0) sh.wave_cnt[w] = cnt;
   }
   __syncthreads();
+  const int lb = sh.bcnt;
+  if (lb <= kBlock) {
+    int v, rk = kBlock;
+    if (lb <= kWave) {  // the usual case
+      v = block_rank64(sh.blist, lb, sh.ranks);
+      if ((int)threadIdx.x < lb) rk = sh.ranks[threadIdx.x];
+    } else {
+      v = threadIdx.x < lb ? sh.blist[threadIdx.x] : kI32Min;
+      rk = 0;
+      for (int j = 0; j < lb; ++j) {
+        const int o = sh.blist[j];
+        rk += (o > v) | ((o == v) & (j < (int)threadIdx.x));
+      }
+    }
+    if ((int)threadIdx.x < lb && rk < k) {
+      st_agent(dst + rk, v);
+      if (rk == 0) st_agent(p.heads + blk, v);
+      if (rk == k - 1) st_agent(p.kths + blk, v);
+    }
+  } else {
+    // Wave merge: each wave's top-k of its entries >= T.
+    {
+      const int live = list_count_ge<KCAP>(L, k, T);
+      int cnt;
+      if (live <= k) {
+        list_emit<KCAP>(L, k, T, false, sh.wave_out[w], KCAP);
+        cnt = live;
+      } else {
+        const int hi = wave_max(L[0]);
+        const unsigned g =
+            radix_select(bias(T), bias(hi), k, ListCount<KCAP>{L, k});
+        const int gs = unbias(g);
+        const int above =
+            list_emit<KCAP>(L, k, gs, true, sh.wave_out[w], KCAP);
+        for (int j = lane(); j < k - above; j += kWave)
+          sh.wave_out[w][above + j] = gs;
+        cnt = k;
+      }
+      if (lane() == 0) sh.wave_cnt[w] = cnt;
+    }
+    __syncthreads();
 
-  // ---- block merge (wave 0): top-k of the four wave results -------------
-  if (w == 0) {
-    constexpr int V = (kWaves * KCAP + kWave - 1) / kWave;
-    unsigned u[V];
-    int mx = kI32Min;
+    // Block merge (wave 0): top-k of the four wave results.  T of wave 0 is
+    // a valid lower end for the search: the workgroup's k-th largest value
+    // is >= it, and each wave result holds that wave's share of the top-k.
+    if (w == 0) {
+      constexpr int V = (kWaves * KCAP + kWave - 1) / kWave;
+      unsigned u[V];
+      int mx = kI32Min;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int q = lane() + kWave * j;
-      const int ww = q / KCAP, o = q % KCAP;
-      const int v = (ww < kWaves && o < sh.wave_cnt[ww < kWaves ? ww : 0])
-                        ? sh.wave_out[ww][o]
-                        : kI32Min;
-      u[j] = bias(v);
-      mx = max(mx, v);
-    }
-    mx = wave_max(mx);
-    const unsigned g = radix_select(bias(T), bias(mx), k, RegCount<V>{u});
-    int* dst = p.cand + (int64_t)blk * k;
-    int base = 0;
+      for (int j = 0; j < V; ++j) {
+        const int q = lane() + kWave * j;
+        const int ww = q / KCAP, o = q % KCAP;
+        const int v = (ww < kWaves && o < sh.wave_cnt[ww < kWaves ? ww : 0])
+                          ? sh.wave_out[ww][o]
+                          : kI32Min;
+        u[j] = bias(v);
+        mx = max(mx, v);
+      }
+      mx = wave_max(mx);
+      const unsigned g = radix_select(bias(T), bias(mx), k, RegCount<V>{u});
+      int base = 0;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const bool q = u[j] > g;
-      const uint64_t b = ballot(q);
-      if (q) st_agent(dst + base + lanes_below(b), unbias(u[j]));
-      base += popc(b);
-    }
-    for (int j = lane(); j < k - base; j += kWave)
-      st_agent(dst + base + j, unbias(g));
-    if (lane() == 0) {
-      st_agent(p.heads + blk, mx);
-      st_agent(p.kths + blk, unbias(g));
+      for (int j = 0; j < V; ++j) {
+        const bool q = u[j] > g;
+        const uint64_t b = ballot(q);
+        if (q) st_agent(dst + base + lanes_below(b), unbias(u[j]));
+        base += popc(b);
+      }
+      for (int j = lane(); j < k - base; j += kWave)
+        st_agent(dst + base + j, unbias(g));
+      if (lane() == 0) {
+        st_agent(p.heads + blk, mx);
+        st_agent(p.kths + blk, unbias(g));
+      }
     }
   }
 

@@ -44,6 +44,16 @@ __device__ __forceinline__ unsigned uni(unsigned v) {
 
 // Order-preserving map int32 -> uint32 (and back): signed order becomes
 // unsigned order, so bitwise radix selection works on plain unsigned values.
+// A pointer known to be the same in every lane, moved to scalar registers.
+template <class T>
+__device__ __forceinline__ T* uni_ptr(T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ unsigned bias(int x) {
   return (unsigned)x ^ 0x80000000u;
 }
