@@ -5,7 +5,9 @@ includes the kernel headers.  The flags disable packed-FP32 instruction
 selection (nothing here uses floating point, but every HIP build in this
 project carries the flag), emit code for gfx950 only, and pin code object
 version 5, which both the ROCm runtime in /opt/rocm and the one bundled with
-PyTorch load.
+PyTorch load.  They also turn off the compiler's atomic optimizer: every
+atomic here is issued by one lane or targets a distinct address per lane,
+and the optimizer's wave-wide combining would only add a scalar loop.
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ HIPCC_FLAGS = [
     "-shared",
     "-mcode-object-version=5",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 

@@ -67,16 +67,15 @@ constexpr int64_t kTileBytes = (int64_t)kBlock * U * 16;  // one tile
 
 // Stage-2 scratch in LDS.  It lives in the memory of the last workgroup's
 // streaming ring (declared separately, see topk_kernel), which is idle by
-// then.  `heads` and `cand` receive every block summary and candidate when
-// grid*k <= kDirectCand.
+// then.  `cand` receives every candidate when grid*k <= kDirectCand.
 constexpr int kDirectCand = 12288;
 struct Stage2Lds {
   int surv[kSurvCap];
   int gt[kMaxK];
   int blocks[kMaxGrid];  // blocks whose maximum reaches T2
-  int heads[kMaxGrid];
+  int heads[kMaxGrid];   // block maxima
   int cand[kDirectCand];
-  alignas(16) int gmax[kWave];  // group maxima of the block maxima
+  alignas(16) int gmax[kBlock + 16];  // group maxima of the block maxima
   int gmax_rank[kWave];
   int surv_rank[kWave];
 };
@@ -86,7 +85,7 @@ struct TopkShared {
   unsigned heads[kBlock];  // snapshot of the lane heads (biased)
   // List entries >= the final bound, gathered from all waves, and their
   // ranks (see block_rank64).
-  alignas(16) int blist[kBlock];
+  alignas(16) int blist[kBlock + 16];
   int ranks[kWave];
   int bcnt;
   int wave_out[kWaves][KCAP];
@@ -247,25 +246,23 @@ __device__ __forceinline__ void init_list(int (&L)[KCAP], const v4i (&d)[U],
   thr = KCAP <= M ? L[KCAP - 1] : kI32Min;
 }
 
-// Raise a certified bound to the k-th largest of the workgroup's 256 lane
-// heads (k <= 128 < 256).
+// Raise this wave's certified bound towards the k-th largest of the
+// workgroup's 256 lane heads (k <= 128 < 256).
 //
 // Every lane keeps its current head (list maximum) in an LDS snapshot.  A
 // list's head never decreases, so any value that was ever a lane's head is
 // still <= that lane's current head: the k-th largest of ANY mix of current
 // and older snapshot entries is <= the k-th largest current head, hence
-// certified.  During streaming (SYNC = false) a wave therefore publishes its
-// own heads and reads the snapshot without waiting for the other waves: no
-// barrier, and each wave keeps its own bound.  The final refresh (SYNC =
-// true) waits for all four waves, so every wave computes the same value, the
-// exact k-th largest head, which is >= every earlier wave bound.
-template <bool SYNC, int KCAP, class SH>
+// certified.  A wave therefore publishes its own heads and reads the
+// snapshot without waiting for the other waves: no barrier, and each wave
+// keeps its own bound.  The top 6 undecided bits of the search are enough:
+// the bound lands within 1/64 of the gap between the old bound and the
+// k-th head, for a fraction of the steps.
+template <int KCAP, class SH>
 __device__ __forceinline__ void refresh_bound(const int (&L)[KCAP], int k,
-                                              int& tsh, int& thr,
-                                              SH& sh) {
+                                              int& tsh, int& thr, SH& sh) {
   __hip_atomic_store(&sh.heads[threadIdx.x], bias(L[0]), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_WORKGROUP);
-  if (SYNC) __syncthreads();
   unsigned u[kWaves];
   int mx = kI32Min;
 #pragma unroll
@@ -278,11 +275,7 @@ __device__ __forceinline__ void refresh_bound(const int (&L)[KCAP], int k,
   const unsigned lo = bias(tsh);
   if (cnt(lo) >= k) {
     mx = wave_max(mx);
-    // While streaming, the top 6 undecided bits are enough: the bound lands
-    // within 1/64 of the gap between the old bound and the largest head
-    // below the exact k-th head, for a fraction of the steps.
-    tsh = unbias(SYNC ? radix_select(lo, bias(mx), k, cnt)
-                      : radix_lower_bound(lo, bias(mx), k, 6, cnt));
+    tsh = unbias(radix_lower_bound(lo, bias(mx), k, 6, cnt));
   }
   thr = max(thr, tsh);
 }
@@ -346,40 +339,39 @@ __device__ __forceinline__ void scan_flagged(const TopkParams& p,
 }
 
 // ---- stage 2, run by the last workgroup ---------------------------------
-// Merge grid*k candidates into out[0..k).  First a gather leaves the
-// survivors -- every candidate >= a certified bound T2 -- in LDS, then the
-// result is written from them.
-//
-// Two gathers:
-//  * direct (grid*k <= kDirectCand, k <= 64): every block maximum and
-//    candidate is copied into LDS at once (device-coherent global-to-LDS
-//    loads, one round trip to memory).  T2 is the k-th largest of 64 group
-//    maxima over disjoint groups of blocks: k distinct candidates reach it.
-//  * flagged: wave 0 reads the block summaries first (T2 from the k-th
-//    largest block maximum and the largest block k-th value), then only the
-//    candidates of the blocks whose maximum reaches T2 are read.
-// If more than kSurvCap candidates survive the direct gather (heavy ties
-// just below the maximum), the flagged gather runs instead; it can count
-// survivors that do not fit in LDS by rescanning the flagged blocks.
-//
-// This code runs once per call, in one workgroup, mostly from a cold
-// instruction cache, so it is written as short loops over LDS rather than
-// long unrolled sequences.
+// Merge grid*k candidates into out[0..k):
+//  1. One round trip to memory copies every block maximum into LDS
+//     (device-coherent global-to-LDS loads), and every candidate too when
+//     grid*k <= kDirectCand; the largest block k-th value T2b is read on
+//     the way.
+//  2. T2a = the k-th largest of group maxima over disjoint groups of blocks
+//     (64 groups for k <= 64, else 256): k distinct candidates reach it.
+//     T2 = max(T2a, T2b) is certified: at least k candidates are >= T2.
+//  3. Only blocks whose maximum reaches T2 can contribute; their candidates
+//     >= T2 (the survivors) go to LDS, read from LDS or, when they were not
+//     copied, from memory.
+//  4. Few survivors (the usual case) are ranked by counting, which writes
+//     the result in order.  Many (heavy ties near the top) go through
+//     selection of the k-th largest by counting; if more than kSurvCap
+//     survive, the counting rescans the flagged blocks in memory.
+// Each step is spread over the whole workgroup with barriers between: a
+// serial loop in one wave would cost a round trip between the vector and
+// scalar units per element.
 
 struct Stage2Bound {
   int t2;     // certified: at least k candidates are >= t2
   int mx;     // the largest candidate
   int m;      // survivors (>= t2); those beyond kSurvCap were not stored
-  int total;  // candidates of the flagged blocks (flagged gather only)
+  int total;  // candidates of the flagged blocks
 };
 
 // Copy 1 KiB of device memory that other workgroups published (with
 // agent-scope stores, before their ticket) into LDS: 16 bytes per lane,
-// lane-contiguous, a device-coherent load (sc1) like ld_agent.
-__device__ __forceinline__ void copy_1k_to_lds(const char* src, void* dst) {
-  const uint32_t lds =
-      (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(dst));
-  const uint32_t voff = (uint32_t)lane() * 16u;
+// lane-contiguous, a device-coherent load (sc1) like ld_agent.  `src` and
+// `lds` (an LDS byte address) must be wave-uniform values in scalar
+// registers; `voff` is lane() * 16.
+__device__ __forceinline__ void copy_1k_to_lds(const char* src, uint32_t lds,
+                                               uint32_t voff) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %[sv], m0\n\t"
@@ -391,22 +383,30 @@ __device__ __forceinline__ void copy_1k_to_lds(const char* src, void* dst) {
       : "memory");
 }
 
-// Ranks by counting, with the whole workgroup: the rank of vals[i] among
-// vals[0..n) (n <= 64) is how many of them are larger, or equal at a lower
-// index, so the ranks of vals[0..n) are 0..n-1 in descending order.
-// Thread t compares value t % 64 with the 16 values 16 * (t / 64) ..
-// 16 * (t / 64) + 15; the four partial counts meet in ranks[] by LDS
-// atomics.  vals: 16-byte aligned, 64 readable slots (those past n are
-// ignored); ranks: 64 slots, zero on entry (set before an earlier
-// barrier).  One barrier inside: call uniformly.  Returns this thread's
-// value (valid for threads < n); rank_of(i) is then ranks[i].
-// Every step is independent vector work: no scalar round trips per
-// comparison, which is what a serial loop over lanes would cost.
-__device__ __forceinline__ int block_rank64(const int* vals, int n,
-                                            int* ranks) {
+// Ranking by counting.  The rank of vals[i] among vals[0..n) is how many
+// of them are larger, or equal at a lower index, so the ranks of
+// vals[0..n) are 0..n-1 in descending order of value.  Each comparison is
+// one unsigned 64-bit compare of keys (biased value, then the complement
+// of the index), so it stays in the vector unit; slots past n are first
+// set to INT_MIN, whose keys never exceed a real one (a real INT_MIN has a
+// lower index).
+__device__ __forceinline__ uint64_t rank_key(int v, int i) {
+  return ((uint64_t)bias(v) << 32) | (uint32_t)~i;
+}
+
+// n <= 64, with the whole workgroup: thread t compares value t % 64 with
+// the 16 values 16 * (t / 64) .. + 15; the four partial counts meet in
+// ranks[] by LDS atomics.  vals: 16-byte aligned, 64 slots; ranks: 64
+// slots, zero on entry (set before an earlier barrier).  Barriers inside:
+// call uniformly.  Returns this thread's value (meaningful for threads
+// < n); its rank is then ranks[threadIdx.x].
+__device__ __forceinline__ int block_rank64(int* vals, int n, int* ranks) {
   const int i = threadIdx.x & (kWave - 1);
   const int g = threadIdx.x / kWave;
+  if ((int)threadIdx.x >= n && threadIdx.x < kWave) vals[threadIdx.x] = kI32Min;
+  __syncthreads();
   const int v = vals[i];
+  const uint64_t ki = rank_key(v, i);
   const v4i* q = reinterpret_cast<const v4i*>(vals + 16 * g);
   int r = 0;
 #pragma unroll
@@ -414,198 +414,198 @@ __device__ __forceinline__ int block_rank64(const int* vals, int n,
     const v4i o4 = q[qq];
     const int o[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 16 * g + 4 * qq + e;
-      r += (j < n) & ((o[e] > v) | ((o[e] == v) & (j < i)));
-    }
+    for (int e = 0; e < 4; ++e)
+      r += rank_key(o[e], 16 * g + 4 * qq + e) > ki;
   }
   if (i < n && r > 0) atomicAdd(&ranks[i], r);
   __syncthreads();
   return v;
 }
 
+// n <= kBlock, one value per thread: thread t ranks vals[t] against all n,
+// 16 values per step, all read before any is used.  vals: 16-byte
+// aligned, kBlock + 16 slots.  A barrier inside: call uniformly.  Threads
+// t >= n get a meaningless result.
+__device__ __forceinline__ int rank_all(int* vals, int n, int& v) {
+  const int t = threadIdx.x;
+  const int n16 = (n + 15) & ~15;
+  for (int j = n + t; j < n16; j += kBlock) vals[j] = kI32Min;
+  __syncthreads();
+  v = vals[t];
+  const uint64_t kt = rank_key(v, t);
+  const v4i* q = reinterpret_cast<const v4i*>(vals);
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    v4i o4[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) o4[qq] = q[j0 / 4 + qq];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int o[4] = {o4[qq].x, o4[qq].y, o4[qq].z, o4[qq].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r += rank_key(o[e], j0 + 4 * qq + e) > kt;
+    }
+  }
+  return r;
+}
+
 template <class SH>
-__device__ __forceinline__ Stage2Bound gather_direct(const TopkParams& p,
-                                                     SH& sh, Stage2Lds& s2) {
+__device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
+                                                     SH& sh, Stage2Lds& s2,
+                                                     bool all_in_lds) {
   const int G = p.grid, k = p.k, tid = threadIdx.x;
   const int w = tid / kWave;
   const int total = G * k;
-  // Block maxima and candidates into LDS, in whole KiB chunks: the source
-  // areas hold kMaxGrid and more than kDirectCand ints, so the last chunk
-  // of each stays inside them; ints past G or `total` are ignored.
+  if (tid < kWave) s2.gmax_rank[tid] = 0;
+  if (tid == 0) {
+    sh.bcast[1] = kI32Min;  // largest block maximum
+    sh.bcast[2] = 0;        // survivors
+    sh.bcast[5] = 0;        // flagged blocks
+    sh.bcast[6] = kI32Min;  // T2b
+  }
+
+  // (1) Whole KiB chunks: the source areas hold kMaxGrid and more than
+  // kDirectCand ints, so the last chunk of each stays inside them; ints
+  // past G or `total` are ignored.
   constexpr int kChunkInts = 1024 / 4;
   const int hchunks = (G + kChunkInts - 1) / kChunkInts;
-  const int chunks = hchunks + (total + kChunkInts - 1) / kChunkInts;
-  for (int c = w; c < chunks; c += kWaves) {
-    const bool h = c < hchunks;
-    const int o = (h ? c : c - hchunks) * kChunkInts;
-    const int* src = h ? p.heads + o : p.cand + o;
-    copy_1k_to_lds(uni_ptr(reinterpret_cast<const char*>(src)),
-                   h ? s2.heads + o : s2.cand + o);
+  const int chunks =
+      hchunks + (all_in_lds ? (total + kChunkInts - 1) / kChunkInts : 0);
+  {
+    // Scalar bookkeeping: the wave index as a scalar, so that every
+    // address below is computed once per wave, not per lane.
+    const int ws = __builtin_amdgcn_readfirstlane(w);
+    const char* hsrc = reinterpret_cast<const char*>(uni_ptr(p.heads));
+    const char* csrc = reinterpret_cast<const char*>(uni_ptr(p.cand));
+    const uint32_t hlds = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)lds_offset(s2.heads));
+    const uint32_t clds = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)lds_offset(s2.cand));
+    const uint32_t voff = (uint32_t)lane() * 16u;
+    for (int c = ws; c < chunks; c += kWaves) {
+      if (c < hchunks)
+        copy_1k_to_lds(hsrc + c * 1024, hlds + c * 1024u, voff);
+      else
+        copy_1k_to_lds(csrc + (c - hchunks) * 1024,
+                       clds + (c - hchunks) * 1024u, voff);
+    }
   }
+  int kt = kI32Min;
+  for (int b = tid; b < G; b += kBlock) kt = max(kt, ld_agent(p.kths + b));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  kt = wave_max(kt);
+  if (lane() == 0) atomicMax(&sh.bcast[6], kt);
 
-  // T2 = the k-th largest of 64 group maxima over disjoint groups of blocks
-  // (distinct blocks, so k candidates reach T2).  Wave 0 forms the groups:
-  // lane l takes blocks l*per .. l*per + per - 1, per being G/64 rounded up
-  // to a multiple of 4 (16-byte LDS loads; slots past those, or past G, are
-  // not its blocks).  Empty groups hold INT_MIN, the trivial bound.
-  if (w == 0) {
-    constexpr int VH = kMaxGrid / kWave;
-    const int per = (((G + kWave - 1) / kWave) + 3) & ~3;
-    const v4i* h4 = reinterpret_cast<const v4i*>(s2.heads + lane() * per);
-    int gm = kI32Min;
+  // (2) Group maxima into s2.gmax.  k <= 64: wave 0 forms 64 groups, lane
+  // l taking blocks l*per .. l*per + per - 1 (per = G/64 rounded up to a
+  // multiple of 4, read as 16-byte LDS loads).  Otherwise every thread
+  // forms one group of G/256 (rounded up) blocks.  Empty groups hold
+  // INT_MIN, which certifies nothing beyond the trivial bound.
+  const bool narrow = k <= kWave;
+  int gm = kI32Min;
+  if (narrow) {
+    if (w == 0) {
+      constexpr int VH = kMaxGrid / kWave;
+      const int per = (((G + kWave - 1) / kWave) + 3) & ~3;
+      const v4i* h4 = reinterpret_cast<const v4i*>(s2.heads + lane() * per);
 #pragma unroll
-    for (int q = 0; q < VH / 4; ++q) {
-      if (4 * q < per) {
-        const v4i t = h4[q];
-        const int b = lane() * per + 4 * q;
-        gm = max(gm, b < G ? t.x : kI32Min);
-        gm = max(gm, b + 1 < G ? t.y : kI32Min);
-        gm = max(gm, b + 2 < G ? t.z : kI32Min);
-        gm = max(gm, b + 3 < G ? t.w : kI32Min);
+      for (int q = 0; q < VH / 4; ++q) {
+        if (4 * q < per) {
+          const v4i t = h4[q];
+          const int b = lane() * per + 4 * q;
+          gm = max(gm, b < G ? t.x : kI32Min);
+          gm = max(gm, b + 1 < G ? t.y : kI32Min);
+          gm = max(gm, b + 2 < G ? t.z : kI32Min);
+          gm = max(gm, b + 3 < G ? t.w : kI32Min);
+        }
       }
+      s2.gmax[lane()] = gm;
     }
-    s2.gmax[lane()] = gm;
-    const int mx = wave_max(gm);
-    if (lane() == 0) {
-      sh.bcast[1] = mx;
-      sh.bcast[2] = 0;  // survivor count
-      sh.bcast[5] = 0;  // flagged blocks
+  } else {
+    const int per = (G + kBlock - 1) / kBlock;
+    for (int j = 0; j < per; ++j) {
+      const int b = tid * per + j;
+      if (b < G) gm = max(gm, s2.heads[b]);
     }
+    s2.gmax[tid] = gm;
   }
+  gm = wave_max(gm);
+  if (lane() == 0 && gm > kI32Min) atomicMax(&sh.bcast[1], gm);
   __syncthreads();
-  {
+  if (narrow) {
     const int gv = block_rank64(s2.gmax, kWave, s2.gmax_rank);
     if (tid < kWave && s2.gmax_rank[tid] == k - 1) sh.bcast[0] = gv;
+  } else if (w == 0) {
+    // 256 group maxima, 4 per lane: a lower bound on the k-th largest,
+    // within 1/256 of its range (certified all the same; see
+    // radix_lower_bound).
+    unsigned u[kWaves];
+    int lo = kI32Max;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) {
+      const int x = s2.gmax[lane() + kWave * j];
+      u[j] = bias(x);
+      lo = min(lo, x);
+    }
+    const unsigned t = radix_lower_bound(bias(wave_min(lo)),
+                                         bias(sh.bcast[1]), k, 8,
+                                         RegCount<kWaves>{u});
+    if (lane() == 0) sh.bcast[0] = unbias(t);
   }
   __syncthreads();
-  const int T2 = sh.bcast[0];
-  // The blocks whose maximum reaches T2 (no other block can contribute).
+  Stage2Bound r;
+  r.t2 = max(sh.bcast[0], sh.bcast[6]);
+  r.mx = sh.bcast[1];
+  r.m = 0;
+  r.total = 0;
+
+  // (3) The blocks whose maximum reaches T2.
   for (int b0 = 0; b0 < G; b0 += kBlock) {
     const int b = b0 + tid;
-    const bool f = b < G && s2.heads[b] >= T2;
+    const bool f = b < G && s2.heads[b] >= r.t2;
     wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
   }
   __syncthreads();
-  Stage2Bound r;
-  r.t2 = sh.bcast[0];
-  r.mx = sh.bcast[1];
-  r.total = 0;
-  r.m = 0;
+  r.total = sh.bcast[5] * k;
   if (r.t2 == r.mx) return r;  // the caller writes k copies of mx
 
-  // Survivors: the candidates >= T2 of the flagged blocks.  Candidates
-  // equal to INT_MIN are left out: if T2 is INT_MIN and fewer than k
-  // candidates exceed it, the result is padded with INT_MIN, which is the
-  // same.
+  // Survivors.  Candidates equal to INT_MIN are left out: if T2 is INT_MIN
+  // and fewer than k candidates exceed it, the result is padded with
+  // INT_MIN, which is the same.
   const int tf = r.t2 == kI32Min ? kI32Min + 1 : r.t2;
-  const int nf = sh.bcast[5] * k;
-  for (int i0 = 0; i0 < nf; i0 += kBlock) {
-    const int i = i0 + tid;
-    int v = kI32Min;
-    if (i < nf) {
-      const int fb = i / k;
-      v = s2.cand[s2.blocks[fb] * k + (i - fb * k)];
+  if (all_in_lds) {
+    for (int i0 = 0; i0 < r.total; i0 += kBlock) {
+      const int i = i0 + tid;
+      int v = kI32Min;
+      if (i < r.total) {
+        const int fb = i / k;
+        v = s2.cand[s2.blocks[fb] * k + (i - fb * k)];
+      }
+      wave_append(v >= tf, v, &sh.bcast[2], s2.surv, kSurvCap);
     }
-    wave_append(v >= tf, v, &sh.bcast[2], s2.surv, kSurvCap);
+  } else {
+    scan_flagged(p, s2.blocks, r.total, [&](bool ok, int c) {
+      wave_append(ok && c >= tf, c, &sh.bcast[2], s2.surv, kSurvCap);
+    });
   }
   __syncthreads();
   r.m = sh.bcast[2];
   return r;
 }
 
-template <class SH>
-__device__ __forceinline__ Stage2Bound gather_flagged(const TopkParams& p,
-                                                      SH& sh, Stage2Lds& s2) {
-  const int G = p.grid, k = p.k;
-  const int w = threadIdx.x / kWave;
-  // Wave 0: the bound from the block summaries.
-  //   T2b = max over blocks of their k-th candidate (that block alone holds
-  //         k candidates >= it);
-  //   T2a = k-th largest block maximum (k distinct candidates >= it);
-  //   T2  = max(T2a, T2b).
-  // Only blocks whose maximum reaches T2 can contribute.
-  if (w == 0) {
-    constexpr int VH = kMaxGrid / kWave;
-    unsigned uh[VH];
-    int mx = kI32Min, kt = kI32Min;
-#pragma unroll
-    for (int j = 0; j < VH; ++j) {
-      const int b = lane() + kWave * j;
-      const int bb = b < G ? b : G - 1;
-      int h = ld_agent(p.heads + bb);
-      int t = ld_agent(p.kths + bb);
-      if (b >= G) h = t = kI32Min;
-      uh[j] = bias(h);
-      mx = max(mx, h);
-      kt = max(kt, t);
-    }
-    mx = wave_max(mx);
-    kt = wave_max(kt);
-    const RegCount<VH> cnt{uh};
-    int t2 = kt;
-    // A lower bound within 1/256 of the range of the exact T2a suffices:
-    // it only admits a few more survivors.
-    if (cnt(bias(kt)) >= k)
-      t2 = unbias(radix_lower_bound(bias(kt), bias(mx), k, 8, cnt));
-    int nb = 0;  // flagged blocks, compacted in block order
-#pragma unroll
-    for (int j = 0; j < VH; ++j) {
-      const int b = lane() + kWave * j;
-      const bool f = b < G && unbias(uh[j]) >= t2;
-      const uint64_t m = ballot(f);
-      if (f) s2.blocks[nb + lanes_below(m)] = b;
-      nb += popc(m);
-    }
-    if (lane() == 0) {
-      sh.bcast[0] = t2;
-      sh.bcast[1] = mx;
-      sh.bcast[2] = 0;  // survivor count
-      sh.bcast[5] = nb;
-    }
-  }
-  __syncthreads();
-  Stage2Bound r;
-  r.t2 = sh.bcast[0];
-  r.mx = sh.bcast[1];
-  r.total = sh.bcast[5] * k;
-  r.m = 0;
-  if (r.t2 == r.mx) return r;
-  // Survivors >= T2 into LDS (only the first kSurvCap are kept).
-  const int T2 = r.t2;
-  scan_flagged(p, s2.blocks, r.total, [&](bool ok, int c) {
-    wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv, kSurvCap);
-  });
-  __syncthreads();
-  r.m = sh.bcast[2];
-  return r;
-}
-
-// Stage 2 proper: gather, select g, write the result, re-arm the ticket.
+// Stage 2 proper: gather, rank or select, write the result, re-arm the
+// ticket.
 template <class SH>
 __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
                                             Stage2Lds& s2) {
   const int k = p.k;
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
+  if (tid < kWave) s2.surv_rank[tid] = 0;  // barriers follow in the gather
 
-  if (tid < kWave) {  // rank counters (a barrier follows in either gather)
-    s2.gmax_rank[tid] = 0;
-    s2.surv_rank[tid] = 0;
-  }
-  Stage2Bound r;
-  // The direct gather certifies T2 from 64 group maxima: it needs k <= 64.
-  bool direct = (int64_t)p.grid * k <= kDirectCand && k <= kWave;
-  if (direct) {
-    r = gather_direct(p, sh, s2);
-    if (r.t2 != r.mx && r.m > kSurvCap) {
-      direct = false;
-      __syncthreads();  // LDS reuse by the second gather
-    }
-  }
-  if (!direct) r = gather_flagged(p, sh, s2);
+  const Stage2Bound r =
+      stage2_gather(p, sh, s2, (int64_t)p.grid * k <= kDirectCand);
   const int T2 = r.t2, mx = r.mx, m = r.m, total = r.total;
 
   if (T2 == mx) {
@@ -614,26 +614,18 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
     if (tid == 0) st_agent(p.ticket, 0u);
     return;
   }
+
   // Few survivors (the usual case): each is ranked by counting, so the
   // result comes out in order with no selection step.  Equal values get
   // consecutive ranks.  If T2 was INT_MIN, fewer than k may have survived:
   // the rest of the result is INT_MIN.
-  if (m <= kWave) {
-    const int v = block_rank64(s2.surv, m, s2.surv_rank);
-    if (tid < m) {
-      const int rk = s2.surv_rank[tid];
-      if (rk < k) p.out[rk] = v;
-    }
-    for (int j = m + tid; j < k; j += kBlock) p.out[j] = kI32Min;
-    if (tid == 0) st_agent(p.ticket, 0u);
-    return;
-  }
   if (m <= kBlock) {
-    const int v = tid < m ? s2.surv[tid] : kI32Min;
-    int rk = 0;
-    for (int j = 0; j < m; ++j) {
-      const int o = s2.surv[j];
-      rk += (o > v) | ((o == v) & (j < tid));
+    int v, rk = kBlock;
+    if (m <= kWave) {
+      v = block_rank64(s2.surv, m, s2.surv_rank);
+      if (tid < m) rk = s2.surv_rank[tid];
+    } else {
+      rk = rank_all(s2.surv, m, v);
     }
     if (tid < m && rk < k) p.out[rk] = v;
     for (int j = m + tid; j < k; j += kBlock) p.out[j] = kI32Min;
@@ -764,7 +756,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
         init_list<KCAP, U>(L, d, thr);
       else
         consume<KCAP, FIT, U>(L, d, k, tsh, thr);
-      if (refresh_due(i, R)) refresh_bound<false>(L, k, tsh, thr, sh);
+      if (refresh_due(i, R)) refresh_bound(L, k, tsh, thr, sh);
     }
   }
   // Elements outside the full tiles: the unaligned head and the tail.
@@ -779,7 +771,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   }
   // One more refresh of this wave's bound from the lane-head snapshot (no
   // barrier: the bound is certified whatever the other waves are doing).
-  refresh_bound<false>(L, k, tsh, thr, sh);
+  refresh_bound(L, k, tsh, thr, sh);
   const int T = tsh;  // certified for the workgroup; may differ per wave
   int* dst = p.cand + (int64_t)blk * k;
 
@@ -821,12 +813,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       v = block_rank64(sh.blist, lb, sh.ranks);
       if ((int)threadIdx.x < lb) rk = sh.ranks[threadIdx.x];
     } else {
-      v = threadIdx.x < lb ? sh.blist[threadIdx.x] : kI32Min;
-      rk = 0;
-      for (int j = 0; j < lb; ++j) {
-        const int o = sh.blist[j];
-        rk += (o > v) | ((o == v) & (j < (int)threadIdx.x));
-      }
+      rk = rank_all(sh.blist, lb, v);
     }
     if ((int)threadIdx.x < lb && rk < k) {
       st_agent(dst + rk, v);
