@@ -60,6 +60,8 @@ class Oracle:
         lib.oracle_reduce_i32.restype = ctypes.c_int
         lib.oracle_check_topk.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p]
         lib.oracle_check_topk.restype = ctypes.c_int
+        lib.oracle_stats_i32.argtypes = [p, ctypes.c_int64, p]
+        lib.oracle_stats_i32.restype = ctypes.c_int
         self.lib = lib
 
     def topk(self, x, k: int) -> np.ndarray:
@@ -83,6 +85,19 @@ class Oracle:
             raise ValueError("oracle_reduce_i32: invalid arguments (op=%d)"
                              % op)
         return int(out[0])
+
+    def stats(self, x) -> dict:
+        """count, sum, max, min and sum of squares of x, as Python ints
+        (the sum of squares exact beyond 64 bits)."""
+        a = _as_i32(x)
+        out = np.zeros(6, dtype=np.int64)
+        rc = self.lib.oracle_stats_i32(a.ctypes.data if a.size else None,
+                                       a.size, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_stats_i32: invalid arguments")
+        u = out.view(np.uint64)
+        return {"count": int(out[0]), "sum": int(out[1]), "max": int(out[2]),
+                "min": int(out[3]), "sumsq": int(u[4]) | (int(u[5]) << 64)}
 
     def check_topk(self, x, k: int, cand) -> int:
         """0 if cand is exactly the descending top-k of x, else 1/2/3."""
@@ -122,3 +137,7 @@ def reduce(x, op: int) -> int:
 
 def check_topk(x, k: int, cand) -> int:
     return default().check_topk(x, k, cand)
+
+
+def stats(x) -> dict:
+    return default().stats(x)

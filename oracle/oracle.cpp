@@ -35,6 +35,17 @@
  *                     start from the int32 extremes and are returned
  *                     sign-extended to int64.
  *
+ *   oracle_stats_i32  the statistics of one array in one call: count, sum,
+ *                     max, min and the sum of squares, from which mean and
+ *                     (population) variance follow ([TopK] §6: the same
+ *                     two-stage reduction serves large-scale statistics
+ *                     such as the mean and the variance; [Reduce], "Basic
+ *                     concepts": each of these is a fold of the array with
+ *                     one binary operator).  Definition: four independent
+ *                     folds, each written out; the sum of squares is
+ *                     accumulated exactly in unsigned 128-bit arithmetic
+ *                     (x^2 <= 2^62, so n <= 2^32 elements stay below 2^94).
+ *
  *   oracle_check_topk a second, sort-free characterisation of the top-k
  *                     multiset, linear in n.  It is used to check results
  *                     at sizes where sorting is too slow, and as an
@@ -95,6 +106,35 @@ int oracle_reduce_i32(const int32_t *in, int64_t n, int32_t op, int64_t *out)
                 m = in[i];
         *out = (int64_t)m;
     }
+    return 0;
+}
+
+/* out[0] = n; out[1] = sum (int64); out[2] = max and out[3] = min,
+ * sign-extended (INT32_MIN and INT32_MAX when n == 0); out[4] and out[5] =
+ * the low and high 64 bits of the sum of squares, an unsigned 128-bit
+ * integer.  Returns 0, or -1 on invalid arguments. */
+int oracle_stats_i32(const int32_t *in, int64_t n, int64_t *out)
+{
+    if (!out || n < 0 || (n > 0 && !in))
+        return -1;
+    int64_t s = 0;
+    int32_t mx = INT32_MIN, mn = INT32_MAX;
+    unsigned __int128 sq = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t x = in[i];
+        s += x;
+        if (in[i] > mx)
+            mx = in[i];
+        if (in[i] < mn)
+            mn = in[i];
+        sq += (unsigned __int128)(uint64_t)(x * x);
+    }
+    out[0] = n;
+    out[1] = s;
+    out[2] = (int64_t)mx;
+    out[3] = (int64_t)mn;
+    out[4] = (int64_t)(uint64_t)sq;
+    out[5] = (int64_t)(uint64_t)(sq >> 64);
     return 0;
 }
 

@@ -179,9 +179,60 @@ def pin_checker_rejects(o, rng):
     assert o.check_topk(dup, 2, [5, 1]) != 0
 
 
+def pin_stats(o, rng):
+    """Statistics (count, sum, max, min, sum of squares), pinned by the
+    page's worked example, closed forms, Python big-int brute force, values
+    beyond 64 bits, and invariants."""
+    g = read_kv("reduce_worked_example.txt")
+    xs = np.array([int(v) for v in g["input"]], dtype=np.int32)
+    st = o.stats(xs)
+    # [1..8]: sum from the page; sum of squares n(n+1)(2n+1)/6 = 204
+    assert st == {"count": 8, "sum": int(g["output"][0]), "max": 8, "min": 1,
+                  "sumsq": 204}
+    e = o.stats(np.zeros(0, dtype=np.int32))
+    assert e == {"count": 0, "sum": 0, "max": I32_MIN, "min": I32_MAX,
+                 "sumsq": 0}
+    alphabet = [I32_MIN, -1, 0, 1, I32_MAX]
+    for n in range(1, 5):
+        for t in itertools.product(alphabet, repeat=n):
+            st = o.stats(np.array(t, dtype=np.int32))
+            assert st == {"count": n, "sum": sum(t), "max": max(t),
+                          "min": min(t), "sumsq": sum(v * v for v in t)}, t
+    for n in [1, 2, 10, 1000, 4099]:
+        perm = rng.permutation(n).astype(np.int32)
+        st = o.stats(perm)
+        assert st["sumsq"] == (n - 1) * n * (2 * n - 1) // 6
+        assert st["sum"] == n * (n - 1) // 2
+    # beyond 64 bits: (-2^31)^2 = 2^62, so four of them already overflow
+    assert o.stats(np.full(1000, I32_MIN, np.int32))["sumsq"] == 1000 * 2 ** 62
+    assert o.stats(np.full(7, I32_MAX, np.int32))["sumsq"] == 7 * I32_MAX ** 2
+    for trial in range(20):
+        n = int(rng.integers(1, 5000))
+        a = rng.integers(I32_MIN + 1, I32_MAX, size=n, dtype=np.int64)
+        a = a.astype(np.int32)
+        st = o.stats(a)
+        ref = [int(v) for v in a.tolist()]
+        assert st["sumsq"] == sum(v * v for v in ref)
+        # cross-op with the single reductions
+        assert st["sum"] == o.reduce(a, SUM)
+        assert st["max"] == o.reduce(a, MAX)
+        assert st["min"] == o.reduce(a, MIN)
+        # permutation and negation invariance (no INT_MIN in a)
+        b = a.copy()
+        rng.shuffle(b)
+        assert o.stats(b) == st
+        neg = o.stats(-a)
+        assert neg["sumsq"] == st["sumsq"] and neg["sum"] == -st["sum"]
+        assert neg["max"] == -st["min"] and neg["min"] == -st["max"]
+        # population variance is non-negative: n * sumsq >= sum^2
+        assert n * st["sumsq"] >= st["sum"] ** 2
+    eq = o.stats(np.full(50, -12345, np.int32))
+    assert 50 * eq["sumsq"] == eq["sum"] ** 2   # zero variance
+
+
 BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
            pin_empty_identities, pin_int64_sum, pin_closed_forms,
-           pin_invariants, pin_checker_rejects]
+           pin_invariants, pin_checker_rejects, pin_stats]
 
 
 def run_battery(o, seed=7):
@@ -234,6 +285,15 @@ MUTANTS = {
                                      "if (have[d] == 0)"),
     "topk_off_by_one": (r"out\[i\] = v\[\(size_t\)\(n - 1 - i\)\];",
                         "out[i] = v[(size_t)(n - 1 - (i > 0 ? i - 1 : 0))];"),
+    "sumsq_in_64_bits": (r"unsigned __int128 sq = 0;", "uint64_t sq = 0;"),
+    "sumsq_of_abs": (r"sq \+= \(unsigned __int128\)\(uint64_t\)\(x \* x\);",
+                     "sq += (unsigned __int128)(uint64_t)(x < 0 ? -x : x);"),
+    "sumsq_skips_first": (r"sq \+= \(unsigned __int128\)",
+                          "if (i > 0) sq += (unsigned __int128)"),
+    "stats_max_starts_at_zero": (r"int32_t mx = INT32_MIN, mn = INT32_MAX;",
+                                 "int32_t mx = 0, mn = INT32_MAX;"),
+    "stats_min_starts_at_zero": (r"int32_t mx = INT32_MIN, mn = INT32_MAX;",
+                                 "int32_t mx = INT32_MIN, mn = 0;"),
 }
 
 
