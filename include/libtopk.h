@@ -109,6 +109,33 @@ int topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out,
 int reduce_i32(const int32_t *in, int64_t n, int32_t op, int64_t *out_i64,
                libtopk_stream_t stream);
 
+/*
+ * reduce_stats_i32 — count, sum, max, min and sum of squares of in[0..n),
+ * all from one read of the data.
+ *
+ * Operation: [TopK] §6 (the two-stage reduction also serves large-scale
+ * statistics such as the mean and the variance) and [Reduce] "Basic
+ * concepts" (each statistic is a fold through one binary operator).  Mean
+ * and population variance follow from the result: sum / count and
+ * (count * sumsq - sum^2) / count^2.  Two stages in one launch, as
+ * reduce_i32.
+ *
+ *   in       device, int32[n] (may be NULL when n == 0)
+ *   n        0 <= n <= 2^32
+ *   out      device, int64[6], written in full:
+ *              out[0]  count = n
+ *              out[1]  exact sum (int64; cannot overflow for n <= 2^32)
+ *              out[2]  max, sign-extended (INT32_MIN when n == 0)
+ *              out[3]  min, sign-extended (INT32_MAX when n == 0)
+ *              out[4]  sum of squares, low 64 bits  } one unsigned 128-bit
+ *              out[5]  sum of squares, high 64 bits } integer, exact
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer (out must be
+ * 8-byte aligned), n out of range, or overlapping in and out.
+ */
+int reduce_stats_i32(const int32_t *in, int64_t n, int64_t *out,
+                     libtopk_stream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *libtopk_strerror(int status);
 

@@ -31,8 +31,8 @@ def no_gpu():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"topk_i32", "reduce_i32", "libtopk_strerror", "libtopk_max_k",
-            "libtopk_set_grid", "libtopk_grid_for",
+    assert {"topk_i32", "reduce_i32", "reduce_stats_i32", "libtopk_strerror",
+            "libtopk_max_k", "libtopk_set_grid", "libtopk_grid_for",
             "libtopk_release"} <= set(names)
 
 
@@ -95,11 +95,27 @@ def test_reduce_rejects_invalid_arguments(args, status):
     assert ltk.reduce_raw(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 10, 0), ltk.ERR_INVALID),                      # NULL output
+    ((FAKE, 10, FAKE * 4 + 4), ltk.ERR_INVALID),           # out not 8-aligned
+    ((FAKE + 1, 10, FAKE * 4), ltk.ERR_INVALID),           # misaligned input
+    ((0, 10, FAKE * 4), ltk.ERR_INVALID),                  # NULL input, n > 0
+    ((FAKE, -1, FAKE * 4), ltk.ERR_INVALID),               # n < 0
+    ((FAKE, (1 << 32) + 1, 1 << 40), ltk.ERR_INVALID),     # n > 2^32
+    ((FAKE, 100, FAKE + 16), ltk.ERR_INVALID),             # out inside in
+    ((FAKE, 100, FAKE - 24), ltk.ERR_INVALID),             # out overlaps in
+])
+def test_stats_rejects_invalid_arguments(args, status):
+    assert ltk.stats_raw(*args) == status
+
+
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
     assert ltk.reduce_raw(FAKE, 1000, 0, FAKE * 4) == ltk.ERR_HIP
     assert ltk.reduce_raw(0, 0, 1, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.stats_raw(FAKE, 1000, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.stats_raw(0, 0, FAKE * 4) == ltk.ERR_HIP
 
 
 def test_grid_setting():

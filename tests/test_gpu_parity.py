@@ -198,6 +198,7 @@ def test_repeated_calls_and_two_streams(ltk):
     ds = [dev(x) for x in xs]
     want = [oracle.topk(x, 20) for x in xs]
     sums = [oracle.reduce(x, oracle.SUM) for x in xs]
+    torch.cuda.synchronize()  # inputs were written on the default stream
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for rep in range(3):

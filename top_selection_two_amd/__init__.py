@@ -7,6 +7,10 @@ if the library is not built, importing this package raises.
 
     topk(x, k)      -> int32 tensor [k], the k largest of x, descending
     reduce(x, op)   -> int64 tensor [1]: SUM, MAX or MIN of x
+    stats(x)        -> int64 tensor [6]: count, sum, max, min and the sum of
+                       squares (low, high 64 bits) of x, from one read
+    unpack_stats(t) -> the same as a dict of Python ints (sum of squares
+                       joined into one integer)
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ SIGNATURES = {
                  ctypes.c_int),
     "reduce_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
                    ctypes.c_int),
+    "reduce_stats_i32": ([_VP, ctypes.c_int64, _VP, _VP], ctypes.c_int),
     "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "libtopk_max_k": ([], ctypes.c_int),
     "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
@@ -100,6 +105,12 @@ def reduce_raw(in_ptr: int, n: int, op: int, out_ptr: int,
                           stream or None)
 
 
+def stats_raw(in_ptr: int, n: int, out_ptr: int, stream: int = 0) -> int:
+    """Call reduce_stats_i32 on raw device pointers; returns the status."""
+    return lib.reduce_stats_i32(in_ptr or None, n, out_ptr or None,
+                                stream or None)
+
+
 # ---------------------------------------------------------------- tensors
 def _check_input(x):
     import torch
@@ -151,3 +162,31 @@ def reduce(x, op, out=None):
     if rc != OK:
         raise LibtopkError(rc, "reduce_i32")
     return out
+
+
+def stats(x, out=None):
+    """count, sum, max, min, sum of squares (low, high) of the int32 device
+    tensor x, as an int64 device tensor [6] (see reduce_stats_i32)."""
+    import torch
+    _check_input(x)
+    if out is None:
+        out = torch.empty(6, dtype=torch.int64, device=x.device)
+    elif (out.dtype != torch.int64 or out.device != x.device
+          or out.numel() != 6 or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int64 [6] tensor on x's "
+                         "device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.reduce_stats_i32(x.data_ptr() if x.numel() else None,
+                                  x.numel(), out.data_ptr(), stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "reduce_stats_i32")
+    return out
+
+
+def unpack_stats(t) -> dict:
+    """The [6] result of stats() as Python ints (copies to the host)."""
+    v = [int(a) for a in t.cpu().tolist()]
+    lo, hi = v[4] & (2 ** 64 - 1), v[5] & (2 ** 64 - 1)
+    return {"count": v[0], "sum": v[1], "max": v[2], "min": v[3],
+            "sumsq": lo | (hi << 64)}

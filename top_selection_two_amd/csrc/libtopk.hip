@@ -1,5 +1,5 @@
 // libtopk host side: argument checks, launch geometry, per-(device, stream)
-// scratch, and the two C entry points declared in include/libtopk.h.
+// scratch, and the C entry points declared in include/libtopk.h.
 //
 // The launch plan follows the two-stage design of
 //   [TopK]   "CUDA并行优化实战：从TopK问题剖析共享内存与规约算法设计", §2.2
@@ -21,6 +21,7 @@
 
 #include "libtopk.h"
 #include "reduce_kernel.hpp"
+#include "stats_kernel.hpp"
 #include "topk_kernel.hpp"
 
 namespace {
@@ -37,13 +38,16 @@ struct Scratch {
   int* heads = nullptr;        // kMaxGrid
   int* kths = nullptr;         // kMaxGrid
   int64_t* partials = nullptr; // kMaxGrid
+  uint64_t* spart = nullptr;   // kMaxGrid * 4 (statistics partials)
   unsigned* ticket = nullptr;  // 1 word, kept at 0 between calls
 };
 
 constexpr size_t kCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(int);
 constexpr size_t kHeadBytes = (size_t)kMaxGrid * sizeof(int);
 constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
-constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes + 256;
+constexpr size_t kStatBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
+constexpr size_t kScratchBytes =
+    kCandBytes + 2 * kHeadBytes + kPartBytes + kStatBytes + 256;
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Scratch> g_cache;
@@ -107,6 +111,8 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   b += kHeadBytes;
   s.partials = (int64_t*)b;
   b += kPartBytes;
+  s.spart = (uint64_t*)b;
+  b += kStatBytes;
   s.ticket = (unsigned*)b;
   // A kernel (not a memset) clears the counter, ordered on the caller's
   // stream before the first real launch.
@@ -257,6 +263,41 @@ int reduce_i32(const int32_t* in, int64_t n, int32_t op, int64_t* out_i64,
   p.ticket = sc.ticket;
   p.out = out_i64;
   return launch(reduce_fn(op), pl.grid, p, s);
+}
+
+int reduce_stats_i32(const int32_t* in, int64_t n, int64_t* out,
+                     libtopk_stream_t stream) {
+  if (!out || ((uintptr_t)out & 7u)) return LIBTOPK_ERR_INVALID;
+  if (n < 0 || n > kMaxN) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && (!in || ((uintptr_t)in & 3u))) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && overlaps(in, (size_t)n * 4, out, 6 * 8))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  // n == 0: a one-block launch with nothing to read writes the identities.
+  static const int32_t kDummy = 0;
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  StatsParams p;
+  p.in = in;
+  p.n = n;
+  p.head = pl.head;
+  p.ntiles = pl.ntiles;
+  p.covered = pl.covered;
+  p.grid = pl.grid;
+  p.partials = sc.spart;
+  p.ticket = sc.ticket;
+  p.out = out;
+  return launch((const void*)&stats_kernel<kTileVec>, pl.grid, p, s);
 }
 
 const char* libtopk_strerror(int status) {
