@@ -1,23 +1,28 @@
 """Benchmark: Top-20 over 1e8 int32 on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path topk|stats]
 
-One step is one full topk_i32 call (both stages; a single kernel launch) over
-the resident 1e8-element input.  The input is synthetic (seeded SplitMix64,
-uniform over the full int32 range, seed 3) and sits in HBM before timing
-starts.  W untimed calls, then K timed back-to-back calls bracketed by device
-synchronisation and by a pair of HIP events on the stream they are launched
-on; each call is one kernel launch, so the event time over K is the kernel's
-average launch duration for the roofline.  The result is checked against the CPU
-oracle before timing, and the oracle itself is timed on the host cores as a
-reported baseline.
+One step is one full library call (both stages; a single kernel launch)
+over a resident synthetic input (seeded SplitMix64).  The default path,
+`topk`, is the headline: topk_i32 with k = 20 over 1e8 int32 uniform over
+the full range (seed 3).  `--path stats` measures reduce_stats_i32 (count,
+sum, max, min and sum of squares in one pass) over 2^26 int32 uniform in
+[-1000, 1000] (seed 2), the array whose sum, max and min are otherwise
+asked for in three separate calls.
+
+The input sits in HBM before timing starts.  W untimed calls, then K timed
+back-to-back calls bracketed by device synchronisation and by a pair of HIP
+events on the stream they are launched on; each call is one kernel launch,
+so the event time over K is the kernel's average launch duration for the
+roofline.  The result is checked against the CPU oracle before timing, and
+the oracle itself is timed on the host cores as a reported baseline.
 
 Prints ONE JSON line.  `value` is elements per second (higher is better);
-`roofline` relates the kernel's algorithmic bytes (4 bytes per input element
-plus 4 per output element) per launch to its measured duration and the
-8 TB/s HBM peak; `traffic` is the HBM byte count per launch measured with
-rocprofv3 counters (profiles/topk_counters_full_1e8_k20.json), reported only
-while the kernel sources still match the ones the counters were taken on.
+`roofline` relates the kernel's algorithmic bytes (4 bytes per input
+element plus the output) per launch to its measured duration and the 8 TB/s
+HBM peak; `traffic` is the HBM byte count per launch measured with rocprofv3
+counters (profiles/<path>_counters_*.json), reported only while the kernel
+sources still match the ones the counters were taken on.
 
 Modes for profiling runs (no JSON line): --mode counters runs a few calls
 plus a plain device copy of known size, to calibrate FETCH_SIZE/WRITE_SIZE.
@@ -36,48 +41,96 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = ("Top-20 over 1e8 int32: ms, elements/s, HBM GB/s as % of 8 TB/s "
-          "peak")
 PEAK_GBPS = 8000.0
-WORKLOAD = "full_1e8"
 K = 20
-COUNTERS = os.path.join(ROOT, "profiles", "topk_counters_full_1e8_k20.json")
-KERNEL_SOURCES = ["wave.hpp", "topk_kernel.hpp", "libtopk.hip"]
+
+PATHS = {
+    "topk": {
+        "metric": ("Top-20 over 1e8 int32: ms, elements/s, HBM GB/s as % of "
+                   "8 TB/s peak"),
+        "workload": "full_1e8",
+        "describe": ("top-20 of 1e8 int32, uniform over the full int32 range "
+                     "(SplitMix64 seed 3), resident in HBM"),
+        "short": "top-20 of 1e8 int32, uniform full range, seed 3",
+        "kernel": "topk_kernel",
+        "sources": ["wave.hpp", "topk_kernel.hpp", "libtopk.hip"],
+        "counters": "topk_counters_full_1e8_k20.json",
+        "summary": "topk_full_1e8_k20.md",
+        "out_bytes": 4 * K,
+        "oracle_what": "top-20 by copy + std::sort",
+    },
+    "stats": {
+        "metric": ("One-pass statistics (count, sum, max, min, sum of "
+                   "squares) over 2^26 int32: elements/s, HBM GB/s as % of "
+                   "8 TB/s peak"),
+        "workload": "pm1000_2p26",
+        "describe": ("count, sum, max, min and exact sum of squares of 2^26 "
+                     "int32 uniform in [-1000, 1000] (SplitMix64 seed 2), "
+                     "resident in HBM"),
+        "short": "statistics of 2^26 int32 in [-1000, 1000], seed 2",
+        "kernel": "stats_kernel",
+        "sources": ["wave.hpp", "stats_kernel.hpp", "libtopk.hip"],
+        "counters": "stats_counters_pm1000_2p26.json",
+        "summary": "stats_pm1000_2p26.md",
+        "out_bytes": 48,
+        "oracle_what": "the five statistics by one loop (128-bit squares)",
+    },
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in PATHS[path]["sources"]:
         with open(os.path.join(ROOT, "top_selection_two_amd", "csrc", name),
                   "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path: str):
     """HBM bytes per launch from committed counter runs, if still valid."""
     try:
-        with open(COUNTERS) as f:
+        with open(os.path.join(ROOT, "profiles",
+                               PATHS[path]["counters"])) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return c.get("traffic_bytes_per_launch")
 
 
-def summarize(run_dir: str, out_dir: str) -> None:
+def commands(path: str):
+    flag = "" if path == "topk" else " --path %s" % path
+    return (
+        "rocprofv3 --kernel-trace --stats -d <run>/trace -o trace "
+        "--output-format csv -- python3 bench.py --steps 200 --warmup 20 "
+        "--no-cpu-baseline" + flag,
+        "rocprofv3 --pmc FETCH_SIZE -d <run>/fetch -o fetch --output-format "
+        "csv -- python3 bench.py --mode counters" + flag,
+        "rocprofv3 --pmc WRITE_SIZE -d <run>/write -o write --output-format "
+        "csv -- python3 bench.py --mode counters" + flag,
+    )
+
+
+def summarize(run_dir: str, out_dir: str, path: str) -> None:
     """Turn rocprofv3 CSV output into the committed summaries.
 
     run_dir holds the three profiler runs made by the commands printed in
     the summaries: trace/ (--kernel-trace --stats over a timed bench run),
     fetch/ and write/ (--pmc FETCH_SIZE, --pmc WRITE_SIZE over --mode
     counters).  The counter values (KiB per dispatch) are scaled by what the
-    same counter reads for the plain 400 MB device copy that --mode counters
-    runs first (torch's copy kernel), so that traffic is in bytes.
+    same counter reads for the plain device copy of the input's size that
+    --mode counters runs first (torch's copy kernel), so that traffic is in
+    bytes.
     """
     import csv
     import glob
+
+    import synth
+
+    P = PATHS[path]
+    kern = P["kernel"]
 
     def rows(pattern):
         files = glob.glob(os.path.join(run_dir, pattern), recursive=True)
@@ -86,8 +139,9 @@ def summarize(run_dir: str, out_dir: str) -> None:
         with open(files[0]) as f:
             return list(csv.DictReader(f))
 
-    n = 100_000_000
+    n = synth.WORKLOADS[P["workload"]]["n"]
     copy_bytes = 4 * n
+    algo = 4 * n + P["out_bytes"]
 
     def counter(pattern, name):
         per = {}
@@ -95,51 +149,44 @@ def summarize(run_dir: str, out_dir: str) -> None:
             if r["Counter_Name"] != name:
                 continue
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        topk = [v for kname, v in per.items() if "topk_kernel" in kname]
+        mine = [v for kname, v in per.items() if kern in kname]
         copy = [v for kname, v in per.items() if "copyBuffer" in kname]
-        if not topk or not copy:
+        if not mine or not copy:
             raise SystemExit("counter %s: kernels not found" % name)
-        return (sum(topk[0]) / len(topk[0]), sum(copy[0]) / len(copy[0]),
-                [kname for kname in per if "topk_kernel" in kname][0])
+        return (sum(mine[0]) / len(mine[0]), sum(copy[0]) / len(copy[0]),
+                [kname for kname in per if kern in kname][0])
 
-    fetch_topk, fetch_copy, kname = counter("fetch/**/*counter_collection.csv",
-                                            "FETCH_SIZE")
-    write_topk, write_copy, _ = counter("write/**/*counter_collection.csv",
-                                        "WRITE_SIZE")
+    fetch_k, fetch_copy, kname = counter("fetch/**/*counter_collection.csv",
+                                         "FETCH_SIZE")
+    write_k, write_copy, _ = counter("write/**/*counter_collection.csv",
+                                     "WRITE_SIZE")
     f_scale = copy_bytes / fetch_copy   # bytes per counted unit (read side)
     w_scale = copy_bytes / write_copy   # bytes per counted unit (write side)
-    traffic = fetch_topk * f_scale + write_topk * w_scale
+    traffic = fetch_k * f_scale + write_k * w_scale
 
     stats = rows("trace/**/*kernel_stats.csv")
-    krow = [r for r in stats if "topk_kernel" in r["Name"]][0]
-    cmd_trace = ("rocprofv3 --kernel-trace --stats -d <run>/trace -o trace "
-                 "--output-format csv -- python3 bench.py --steps 200 "
-                 "--warmup 20 --no-cpu-baseline")
-    cmd_fetch = ("rocprofv3 --pmc FETCH_SIZE -d <run>/fetch -o fetch "
-                 "--output-format csv -- python3 bench.py --mode counters")
-    cmd_write = ("rocprofv3 --pmc WRITE_SIZE -d <run>/write -o write "
-                 "--output-format csv -- python3 bench.py --mode counters")
+    krow = [r for r in stats if kern in r["Name"]][0]
+    cmd_trace, cmd_fetch, cmd_write = commands(path)
     os.makedirs(out_dir, exist_ok=True)
     data = {
         "kernel": kname,
-        "workload": "top-20 of 1e8 int32, uniform full range, seed 3",
-        "kernel_source_hash": kernel_source_hash(),
-        "fetch_size_kib_per_dispatch": fetch_topk,
-        "write_size_kib_per_dispatch": write_topk,
+        "workload": P["short"],
+        "kernel_source_hash": kernel_source_hash(path),
+        "fetch_size_kib_per_dispatch": fetch_k,
+        "write_size_kib_per_dispatch": write_k,
         "copy_calibration": {
             "bytes_read_and_written": copy_bytes,
             "fetch_size_kib": fetch_copy, "write_size_kib": write_copy,
             "bytes_per_fetch_unit": f_scale, "bytes_per_write_unit": w_scale},
         "traffic_bytes_per_launch": round(traffic),
-        "algorithmic_bytes_per_launch": 4 * n + 4 * K,
+        "algorithmic_bytes_per_launch": algo,
         "commands": [cmd_fetch, cmd_write],
     }
-    with open(os.path.join(out_dir, "topk_counters_full_1e8_k20.json"),
-              "w") as f:
+    with open(os.path.join(out_dir, P["counters"]), "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
     lines = [
-        "# topk_kernel on top-20 of 1e8 int32 (uniform full range, seed 3)",
+        "# %s on %s" % (kern, P["short"]),
         "",
         "Kernel trace (rocprofv3 --kernel-trace --stats), from the repository "
         "root:",
@@ -156,28 +203,29 @@ def summarize(run_dir: str, out_dir: str) -> None:
     avg_ns = float(krow["AverageNs"])
     lines += [
         "",
-        "topk_kernel average: %.2f us -> algorithmic %.0f GB/s (%.1f %% of "
-        "8 TB/s)." % (avg_ns / 1e3, (4 * n + 4 * K) / avg_ns,
-                      100 * (4 * n + 4 * K) / avg_ns / 8000.0),
+        "%s average: %.2f us -> algorithmic %.0f GB/s (%.1f %% of "
+        "8 TB/s)." % (kern, avg_ns / 1e3, algo / avg_ns,
+                      100 * algo / avg_ns / 8000.0),
         "",
         "HBM traffic (rocprofv3 --pmc, one counter per run):",
         "",
         "    " + cmd_fetch,
         "    " + cmd_write,
         "",
-        "| counter | topk_kernel (KiB/dispatch) | 400 MB copy (KiB) | bytes per "
-        "unit | topk bytes |",
+        "| counter | %s (KiB/dispatch) | %d MB copy (KiB) | bytes per "
+        "unit | %s bytes |" % (kern, copy_bytes // 10 ** 6, kern),
         "|---|---|---|---|---|",
         "| FETCH_SIZE | %.1f | %.1f | %.4f | %.0f |" % (
-            fetch_topk, fetch_copy, f_scale, fetch_topk * f_scale),
+            fetch_k, fetch_copy, f_scale, fetch_k * f_scale),
         "| WRITE_SIZE | %.1f | %.1f | %.4f | %.0f |" % (
-            write_topk, write_copy, w_scale, write_topk * w_scale),
+            write_k, write_copy, w_scale, write_k * w_scale),
         "",
-        "Traffic per launch: %.0f bytes = %.4f x the 4N + 4k algorithmic "
-        "bytes." % (traffic, traffic / (4 * n + 4 * K)),
+        "Traffic per launch: %.0f bytes = %.4f x the algorithmic bytes "
+        "(4 per input element + %d out)." % (traffic, traffic / algo,
+                                             P["out_bytes"]),
         "",
     ]
-    with open(os.path.join(out_dir, "topk_full_1e8_k20.md"), "w") as f:
+    with open(os.path.join(out_dir, P["summary"]), "w") as f:
         f.write("\n".join(lines))
     print("wrote summaries to", out_dir)
 
@@ -193,14 +241,13 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def time_oracle(x, k, budget_s=12.0, max_reps=3):
-    """Median wall time of the single-threaded CPU oracle on x."""
-    import oracle
+def time_oracle(fn, budget_s=12.0, max_reps=3):
+    """Median wall time of a single-threaded CPU oracle call."""
     times = []
     t_start = time.perf_counter()
     while len(times) < max_reps:
         t0 = time.perf_counter()
-        oracle.topk(x, k)
+        fn()
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s:
             break
@@ -212,6 +259,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--path", choices=sorted(PATHS), default="topk")
     ap.add_argument("--mode", choices=["bench", "counters"], default="bench")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grid", type=int, default=0,
@@ -220,8 +268,9 @@ def main():
                     help="write profiles/ summaries from rocprofv3 output "
                          "(CPU only)")
     args = ap.parse_args()
+    P = PATHS[args.path]
     if args.summarize:
-        summarize(args.summarize, os.path.join(ROOT, "profiles"))
+        summarize(args.summarize, os.path.join(ROOT, "profiles"), args.path)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -241,35 +290,50 @@ def main():
     torch.cuda.set_device(dev)
     ltk.set_grid(args.grid)
 
-    x = synth.workload(WORKLOAD)
+    x = synth.workload(P["workload"])
     n = x.size
     xd = torch.from_numpy(x).to(dev)
-    out = torch.empty(K, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.path == "topk":
+        out = torch.empty(K, dtype=torch.int32, device=dev)
+
+        def call():
+            return ltk.topk(xd, K, out=out)
+    else:
+        out = torch.empty(6, dtype=torch.int64, device=dev)
+
+        def call():
+            return ltk.stats(xd, out=out)
 
     if args.mode == "counters":
         # A plain copy of known size (calibrates the counters), then a few
-        # top-k launches.
+        # launches of the measured kernel.
         src = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
         dst = torch.empty_like(src)
         dst.copy_(src)
         for _ in range(5):
-            ltk.topk(xd, K, out=out)
+            call()
         torch.cuda.synchronize()
-        print("counters mode: copy %d bytes read + %d written; 5 topk calls "
-              "over n=%d" % (4 * n, 4 * n, n), flush=True)
+        print("counters mode: copy %d bytes read + %d written; 5 %s calls "
+              "over n=%d" % (4 * n, 4 * n, args.path, n), flush=True)
         return
 
     # Correctness first (the oracle is the CPU reference; test-only code).
     import oracle
-    got = ltk.topk(xd, K, out=out).cpu().numpy()
-    want = oracle.topk(x, K)
-    if not np.array_equal(got, want):
+    if args.path == "topk":
+        got = call().cpu().numpy()
+        want = oracle.topk(x, K)
+        ok = np.array_equal(got, want)
+    else:
+        got = ltk.unpack_stats(call())
+        want = oracle.stats(x)
+        ok = got == want
+    if not ok:
         print("MISMATCH against the oracle", got, want, file=sys.stderr)
         sys.exit(3)
 
     for _ in range(args.warmup):
-        ltk.topk(xd, K, out=out)
+        call()
     torch.cuda.synchronize()
 
     # Timed region: K back-to-back calls on the stream, bracketed by device
@@ -283,7 +347,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        ltk.topk(xd, K, out=out)
+        call()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -291,7 +355,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = n * args.steps / wall
 
-    algo_bytes = 4 * n + 4 * K
+    algo_bytes = 4 * n + P["out_bytes"]
     achieved = algo_bytes / (avg_launch_ms * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
@@ -299,25 +363,40 @@ def main():
         "peak": PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / PEAK_GBPS, 4),
-        "traffic": measured_traffic(),
+        "traffic": measured_traffic(args.path),
     }
 
     cpu = None
     if not args.no_cpu_baseline:
-        t_med, reps = time_oracle(x, K)
+        if args.path == "topk":
+            t_med, reps = time_oracle(lambda: oracle.topk(x, K))
+            what = "the full workload (1e8 int32, seed 3)"
+        else:
+            # one pass takes ~0.05 s: repeat it for about 10 s of CPU work
+            t_med, reps = time_oracle(lambda: oracle.stats(x), budget_s=10.0,
+                                      max_reps=250)
+            what = "the full workload (2^26 int32, seed 2)"
         cpu = {
             "value": round(n / t_med, 1),
             "unit": "elements/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": "the full workload (1e8 int32, seed 3), top-20 by "
-                      "copy + std::sort on one thread; median of %d run(s) "
-                      "of %.2f s; host %s, %d logical CPUs"
-                      % (reps, t_med, cpu_model(), os.cpu_count() or 0),
+            "sample": "%s, %s on one thread; median of %d run(s) of %.2f s; "
+                      "host %s, %d logical CPUs"
+                      % (what, P["oracle_what"], reps, t_med, cpu_model(),
+                         os.cpu_count() or 0),
         }
 
+    config = {"workload": P["describe"], "n": n}
+    if args.path == "topk":
+        config["k"] = K
+    config.update({
+        "grid": ltk.grid_for(n),
+        "kernel_ms_avg": round(avg_launch_ms, 5),
+        "hbm_gbps_per_step": round(algo_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+    })
     line = {
-        "metric": METRIC,
+        "metric": P["metric"],
         "value": round(value, 1),
         "unit": "elements/s",
         "n_gpus": 1,
@@ -329,16 +408,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {
-            "workload": "top-20 of 1e8 int32, uniform over the full int32 "
-                        "range (SplitMix64 seed 3), resident in HBM",
-            "n": n,
-            "k": K,
-            "grid": ltk.grid_for(n),
-            "kernel_ms_avg": round(avg_launch_ms, 5),
-            "hbm_gbps_per_step": round(algo_bytes / (ms_per_step * 1e-3) / 1e9,
-                                       1),
-        },
+        "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
