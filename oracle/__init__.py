@@ -62,6 +62,10 @@ class Oracle:
         lib.oracle_check_topk.restype = ctypes.c_int
         lib.oracle_stats_i32.argtypes = [p, ctypes.c_int64, p]
         lib.oracle_stats_i32.restype = ctypes.c_int
+        for name in ("oracle_topk_kv_i32", "oracle_topk_kv_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, p]
+            fn.restype = ctypes.c_int
         self.lib = lib
 
     def topk(self, x, k: int) -> np.ndarray:
@@ -98,6 +102,22 @@ class Oracle:
         u = out.view(np.uint64)
         return {"count": int(out[0]), "sum": int(out[1]), "max": int(out[2]),
                 "min": int(out[3]), "sumsq": int(u[4]) | (int(u[5]) << 64)}
+
+    def topk_kv(self, x, k: int):
+        """(values, int64 positions) of the k largest elements of x, int32 or
+        float32, ordered by value descending, then position ascending."""
+        a = np.ascontiguousarray(x)
+        if a.ndim != 1 or a.dtype not in (np.int32, np.float32):
+            raise ValueError("expected a 1-D int32 or float32 array")
+        fn = (self.lib.oracle_topk_kv_i32 if a.dtype == np.int32
+              else self.lib.oracle_topk_kv_f32)
+        vals = np.empty(max(k, 0), dtype=a.dtype)
+        idx = np.empty(max(k, 0), dtype=np.int64)
+        rc = fn(a.ctypes.data, a.size, k, vals.ctypes.data, idx.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_topk_kv: invalid arguments (n=%d, k=%d)"
+                             % (a.size, k))
+        return vals, idx
 
     def check_topk(self, x, k: int, cand) -> int:
         """0 if cand is exactly the descending top-k of x, else 1/2/3."""
@@ -141,3 +161,7 @@ def check_topk(x, k: int, cand) -> int:
 
 def stats(x) -> dict:
     return default().stats(x)
+
+
+def topk_kv(x, k: int):
+    return default().topk_kv(x, k)

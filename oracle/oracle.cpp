@@ -46,6 +46,24 @@
  *                     accumulated exactly in unsigned 128-bit arithmetic
  *                     (x^2 <= 2^62, so n <= 2^32 elements stay below 2^94).
  *
+ *   oracle_topk_kv_i32, oracle_topk_kv_f32
+ *                     the k largest values together with their positions
+ *                     in the input ([TopK] §6: the reduction keeps a
+ *                     candidate list of items ordered by their score;
+ *                     "GPU基数排序优化：10亿级数据处理与性能调优" §8: key-value
+ *                     pairs, and floating-point keys through a suitable bit
+ *                     transform).  With indices the answer is no longer
+ *                     unique under ties, so a rule is fixed: order by value,
+ *                     descending, and among equal values by index,
+ *                     ascending (the earlier element first).  Definition: a
+ *                     stable sort of the positions by value, descending,
+ *                     then the first k.  Float scores are ordered by the
+ *                     usual order-preserving map of their bits to unsigned
+ *                     integers (negative: all bits flipped; otherwise the
+ *                     sign bit set), which agrees with numerical order on
+ *                     numbers and puts -0 below +0, positive NaNs above
+ *                     +infinity and negative NaNs below -infinity.
+ *
  *   oracle_check_topk a second, sort-free characterisation of the top-k
  *                     multiset, linear in n.  It is used to check results
  *                     at sizes where sorting is too slow, and as an
@@ -135,6 +153,52 @@ int oracle_stats_i32(const int32_t *in, int64_t n, int64_t *out)
     out[3] = (int64_t)mn;
     out[4] = (int64_t)(uint64_t)sq;
     out[5] = (int64_t)(uint64_t)(sq >> 64);
+    return 0;
+}
+
+/* out_v[i], out_i[i] for i < k: the value and the position of the i-th
+ * element in the order (value descending, position ascending).  Returns 0,
+ * or -1 on invalid arguments (null pointers, n < 0, k < 1, k > n). */
+int oracle_topk_kv_i32(const int32_t *in, int64_t n, int32_t k,
+                       int32_t *out_v, int64_t *out_i)
+{
+    if (!in || !out_v || !out_i || n < 0 || k < 1 || (int64_t)k > n)
+        return -1;
+    std::vector<int64_t> pos((size_t)n);
+    for (int64_t i = 0; i < n; ++i)
+        pos[(size_t)i] = i;
+    std::stable_sort(pos.begin(), pos.end(),
+                     [in](int64_t a, int64_t b) { return in[a] > in[b]; });
+    for (int32_t i = 0; i < k; ++i) {
+        out_i[i] = pos[(size_t)i];
+        out_v[i] = in[pos[(size_t)i]];
+    }
+    return 0;
+}
+
+/* The same for float scores, ordered through their bit patterns (see
+ * above); out_v receives the input's own bits. */
+int oracle_topk_kv_f32(const float *in, int64_t n, int32_t k, float *out_v,
+                       int64_t *out_i)
+{
+    if (!in || !out_v || !out_i || n < 0 || k < 1 || (int64_t)k > n)
+        return -1;
+    std::vector<uint32_t> key((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t b;
+        std::memcpy(&b, &in[i], sizeof b);
+        key[(size_t)i] = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    }
+    std::vector<int64_t> pos((size_t)n);
+    for (int64_t i = 0; i < n; ++i)
+        pos[(size_t)i] = i;
+    std::stable_sort(pos.begin(), pos.end(), [&key](int64_t a, int64_t b) {
+        return key[(size_t)a] > key[(size_t)b];
+    });
+    for (int32_t i = 0; i < k; ++i) {
+        out_i[i] = pos[(size_t)i];
+        std::memcpy(&out_v[i], &in[pos[(size_t)i]], sizeof(float));
+    }
     return 0;
 }
 

@@ -230,9 +230,60 @@ def pin_stats(o, rng):
     assert 50 * eq["sumsq"] == eq["sum"] ** 2   # zero variance
 
 
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def pin_topk_kv(o, rng):
+    """Key-value top-k: hand examples of the tie rule (value descending,
+    then position ascending), Python brute force with a different sort,
+    agreement with the value-only top-k, and float order pinned by Python's
+    own float comparison (-0 below +0, NaNs at the two ends)."""
+    x = np.array([5, 7, 7, 3, 7], np.int32)
+    v, i = o.topk_kv(x, 2)
+    assert list(v) == [7, 7] and list(i) == [1, 2]
+    v, i = o.topk_kv(x, 5)
+    assert list(v) == [7, 7, 7, 5, 3] and list(i) == [1, 2, 4, 0, 3]
+    v, i = o.topk_kv(np.full(50, -4, np.int32), 10)
+    assert list(v) == [-4] * 10 and list(i) == list(range(10))
+    v, i = o.topk_kv(np.arange(100, dtype=np.int32), 3)
+    assert list(v) == [99, 98, 97] and list(i) == [99, 98, 97]
+    for trial in range(60):
+        n = int(rng.integers(1, 300))
+        hi = int(rng.choice([2, 10, 2 ** 31]))
+        a = rng.integers(-hi, hi, size=n, dtype=np.int64).astype(np.int32)
+        k = int(rng.integers(1, n + 1))
+        want = sorted(range(n), key=lambda j: (-int(a[j]), j))[:k]
+        v, i = o.topk_kv(a, k)
+        assert list(i) == want, (a, k)
+        assert list(v) == [int(a[j]) for j in want]
+        assert list(v) == list(o.topk(a, k))
+    # floats: numerical order, +0 before -0, ties by position
+    specials = [0.0, -0.0, np.inf, -np.inf, 1.5, -1.5, 1e-40, -1e-40,
+                3.4e38, -3.4e38, 1.0, 1.0]
+    for trial in range(40):
+        n = int(rng.integers(1, 200))
+        a = rng.choice(specials + list(rng.normal(size=8)), size=n)
+        a = a.astype(np.float32)
+        k = int(rng.integers(1, n + 1))
+
+        def key(j):
+            f = float(a[j])
+            return (-f, 1 if (f == 0.0 and np.signbit(a[j])) else 0, j)
+        want = sorted(range(n), key=key)[:k]
+        v, i = o.topk_kv(a, k)
+        assert list(i) == want, (a, k)
+        assert v.view(np.uint32).tolist() == a[want].view(np.uint32).tolist()
+    # NaNs: a positive NaN ranks above +inf, a negative one below -inf
+    pnan, nnan = _f32(0x7FC00000), _f32(0xFFC00000)
+    a = np.array([1.0, nnan, np.inf, pnan, -np.inf], np.float32)
+    v, i = o.topk_kv(a, 5)
+    assert list(i) == [3, 2, 0, 4, 1]
+
+
 BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
            pin_empty_identities, pin_int64_sum, pin_closed_forms,
-           pin_invariants, pin_checker_rejects, pin_stats]
+           pin_invariants, pin_checker_rejects, pin_stats, pin_topk_kv]
 
 
 def run_battery(o, seed=7):
@@ -294,6 +345,16 @@ MUTANTS = {
                                  "int32_t mx = 0, mn = INT32_MAX;"),
     "stats_min_starts_at_zero": (r"int32_t mx = INT32_MIN, mn = INT32_MAX;",
                                  "int32_t mx = INT32_MIN, mn = 0;"),
+    "kv_ties_by_larger_index": (
+        r"std::stable_sort\(pos.begin\(\), pos.end\(\),\n\s*\[in\]\(int64_t a, int64_t b\) \{ return in\[a\] > in\[b\]; \}\);",
+        "std::sort(pos.begin(), pos.end(), [in](int64_t a, int64_t b) "
+        "{ return in[a] > in[b] || (in[a] == in[b] && a > b); });"),
+    "kv_index_off_by_one": (r"out_i\[i\] = pos\[\(size_t\)i\];\n        out_v\[i\] = in",
+                            "out_i[i] = pos[(size_t)i] + (i > 0);\n        out_v[i] = in"),
+    "kv_float_raw_bits": (r"key\[\(size_t\)i\] = \(b & 0x80000000u\) \? ~b : \(b \| 0x80000000u\);",
+                          "key[(size_t)i] = b;"),
+    "kv_float_sign_only": (r"key\[\(size_t\)i\] = \(b & 0x80000000u\) \? ~b : \(b \| 0x80000000u\);",
+                           "key[(size_t)i] = b ^ 0x80000000u;"),
 }
 
 
