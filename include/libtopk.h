@@ -110,6 +110,35 @@ int reduce_i32(const int32_t *in, int64_t n, int32_t op, int64_t *out_i64,
                libtopk_stream_t stream);
 
 /*
+ * topk_kv_i32 / topk_kv_f32 — the k largest elements of in[0..n) with their
+ * positions: out_values[i] and out_indices[i] for i < k, ordered by value,
+ * descending, and among equal values by position, ascending (the earlier
+ * element first), so the result is unique.
+ *
+ * Operation: [TopK] §6 (the reduction keeps a candidate list of items
+ * ordered by their score) with [TopK] §2's two stages, and "GPU基数排序优化：
+ * 10亿级数据处理与性能调优" §8 (key-value pairs carried together; float keys
+ * through a bit transform).  Float order: the order-preserving map of the
+ * bits to unsigned integers (negative: all bits flipped; otherwise the sign
+ * bit set): numerical order on numbers, -0 below +0, positive NaNs above
+ * +infinity, negative NaNs below -infinity.  One launch, as topk_i32.
+ *
+ *   in           device, int32[n] or float32[n], read once
+ *   n            1 <= n < 2^32 (positions must fit 32 bits)
+ *   k            1 <= k <= min(n, LIBTOPK_MAX_K)
+ *   out_values   device, int32[k] / float32[k] (the input's own bits)
+ *   out_indices  device, int64[k], positions in [0, n)
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer (out_indices
+ * 8-byte aligned), n out of range, k < 1 or k > n, or overlapping buffers;
+ * LIBTOPK_ERR_UNSUPPORTED for k > LIBTOPK_MAX_K.
+ */
+int topk_kv_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out_values,
+                int64_t *out_indices, libtopk_stream_t stream);
+int topk_kv_f32(const float *in, int64_t n, int32_t k, float *out_values,
+                int64_t *out_indices, libtopk_stream_t stream);
+
+/*
  * reduce_stats_i32 — count, sum, max, min and sum of squares of in[0..n),
  * all from one read of the data.
  *

@@ -31,7 +31,8 @@ def no_gpu():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"topk_i32", "reduce_i32", "reduce_stats_i32", "libtopk_strerror",
+    assert {"topk_i32", "reduce_i32", "reduce_stats_i32", "topk_kv_i32",
+            "topk_kv_f32", "libtopk_strerror",
             "libtopk_max_k", "libtopk_set_grid", "libtopk_grid_for",
             "libtopk_release"} <= set(names)
 
@@ -109,6 +110,27 @@ def test_stats_rejects_invalid_arguments(args, status):
     assert ltk.stats_raw(*args) == status
 
 
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("args,status", [
+    ((0, 100, 5, FAKE * 4, FAKE * 8), ltk.ERR_INVALID),          # NULL input
+    ((FAKE, 100, 5, 0, FAKE * 8), ltk.ERR_INVALID),              # NULL values
+    ((FAKE, 100, 5, FAKE * 4, 0), ltk.ERR_INVALID),              # NULL indices
+    ((FAKE + 2, 100, 5, FAKE * 4, FAKE * 8), ltk.ERR_INVALID),   # misaligned in
+    ((FAKE, 100, 5, FAKE * 4 + 1, FAKE * 8), ltk.ERR_INVALID),   # misaligned vals
+    ((FAKE, 100, 5, FAKE * 4, FAKE * 8 + 4), ltk.ERR_INVALID),   # indices not 8-aligned
+    ((FAKE, 0, 1, FAKE * 4, FAKE * 8), ltk.ERR_INVALID),         # n = 0
+    ((FAKE, 1 << 32, 5, 1 << 40, 1 << 41), ltk.ERR_INVALID),     # n = 2^32
+    ((FAKE, 100, 0, FAKE * 4, FAKE * 8), ltk.ERR_INVALID),       # k = 0
+    ((FAKE, 10, 11, FAKE * 4, FAKE * 8), ltk.ERR_INVALID),       # k > n
+    ((FAKE, 1000, 129, FAKE * 4, FAKE * 8), ltk.ERR_UNSUPPORTED),
+    ((FAKE, 1000, 20, FAKE + 400, FAKE * 8), ltk.ERR_INVALID),   # vals inside in
+    ((FAKE, 1000, 20, FAKE * 4, FAKE + 800), ltk.ERR_INVALID),   # indices inside in
+    ((FAKE, 100, 20, FAKE * 8, FAKE * 8 + 40), ltk.ERR_INVALID), # vals/indices overlap
+])
+def test_topk_kv_rejects_invalid_arguments(args, status, f32):
+    assert ltk.topk_kv_raw(*args, f32=f32) == status
+
+
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
@@ -116,6 +138,9 @@ def test_valid_call_without_device_reports_hip_error():
     assert ltk.reduce_raw(0, 0, 1, FAKE * 4) == ltk.ERR_HIP
     assert ltk.stats_raw(FAKE, 1000, FAKE * 4) == ltk.ERR_HIP
     assert ltk.stats_raw(0, 0, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.topk_kv_raw(FAKE, 1000, 20, FAKE * 4, FAKE * 8) == ltk.ERR_HIP
+    assert ltk.topk_kv_raw(FAKE, 1000, 20, FAKE * 4, FAKE * 8,
+                           f32=True) == ltk.ERR_HIP
 
 
 def test_grid_setting():

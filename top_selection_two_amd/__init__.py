@@ -7,6 +7,8 @@ if the library is not built, importing this package raises.
 
     topk(x, k)      -> int32 tensor [k], the k largest of x, descending
     reduce(x, op)   -> int64 tensor [1]: SUM, MAX or MIN of x
+    topk_kv(x, k)   -> (values [k], int64 positions [k]) of an int32 or
+                       float32 x: value descending, then position ascending
     stats(x)        -> int64 tensor [6]: count, sum, max, min and the sum of
                        squares (low, high 64 bits) of x, from one read
     unpack_stats(t) -> the same as a dict of Python ints (sum of squares
@@ -32,6 +34,10 @@ SIGNATURES = {
     "reduce_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
                    ctypes.c_int),
     "reduce_stats_i32": ([_VP, ctypes.c_int64, _VP, _VP], ctypes.c_int),
+    "topk_kv_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP],
+                    ctypes.c_int),
+    "topk_kv_f32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP],
+                    ctypes.c_int),
     "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "libtopk_max_k": ([], ctypes.c_int),
     "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
@@ -111,13 +117,21 @@ def stats_raw(in_ptr: int, n: int, out_ptr: int, stream: int = 0) -> int:
                                 stream or None)
 
 
+def topk_kv_raw(in_ptr: int, n: int, k: int, vals_ptr: int, idx_ptr: int,
+                stream: int = 0, f32: bool = False) -> int:
+    """Call topk_kv_i32 (or topk_kv_f32) on raw device pointers."""
+    fn = lib.topk_kv_f32 if f32 else lib.topk_kv_i32
+    return fn(in_ptr or None, n, k, vals_ptr or None, idx_ptr or None,
+              stream or None)
+
+
 # ---------------------------------------------------------------- tensors
-def _check_input(x):
+def _check_input(x, dtypes=("int32",)):
     import torch
     if not isinstance(x, torch.Tensor):
         raise TypeError("expected a torch.Tensor")
-    if x.dtype != torch.int32:
-        raise TypeError("expected int32, got %s" % x.dtype)
+    if str(x.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError("expected %s, got %s" % (" or ".join(dtypes), x.dtype))
     if x.device.type != "cuda":
         raise ValueError("expected a device tensor, got %s" % x.device)
     if x.dim() != 1 or not x.is_contiguous():
@@ -190,3 +204,31 @@ def unpack_stats(t) -> dict:
     lo, hi = v[4] & (2 ** 64 - 1), v[5] & (2 ** 64 - 1)
     return {"count": v[0], "sum": v[1], "max": v[2], "min": v[3],
             "sumsq": lo | (hi << 64)}
+
+
+def topk_kv(x, k: int, out=None):
+    """The k largest elements of the int32 or float32 device tensor x and
+    their positions: (values [k] of x's dtype, int64 positions [k]), ordered
+    by value descending, then position ascending (see topk_kv_i32)."""
+    import torch
+    _check_input(x, ("int32", "float32"))
+    if out is None:
+        vals = torch.empty(max(int(k), 0), dtype=x.dtype, device=x.device)
+        idx = torch.empty(max(int(k), 0), dtype=torch.int64, device=x.device)
+    else:
+        vals, idx = out
+        if (vals.dtype != x.dtype or idx.dtype != torch.int64
+                or vals.numel() != k or idx.numel() != k
+                or vals.device != x.device or idx.device != x.device
+                or not vals.is_contiguous() or not idx.is_contiguous()):
+            raise ValueError("out must be contiguous ([k] of x's dtype, "
+                             "int64 [k]) on x's device")
+    fn = lib.topk_kv_f32 if x.dtype == torch.float32 else lib.topk_kv_i32
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = fn(x.data_ptr() if x.numel() else None, x.numel(), k,
+                vals.data_ptr() if vals.numel() else None,
+                idx.data_ptr() if idx.numel() else None, stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, fn.__name__)
+    return vals, idx

@@ -23,6 +23,7 @@
 #include "reduce_kernel.hpp"
 #include "stats_kernel.hpp"
 #include "topk_kernel.hpp"
+#include "topk_kv_kernel.hpp"
 
 namespace {
 
@@ -39,6 +40,9 @@ struct Scratch {
   int* kths = nullptr;         // kMaxGrid
   int64_t* partials = nullptr; // kMaxGrid
   uint64_t* spart = nullptr;   // kMaxGrid * 4 (statistics partials)
+  uint64_t* kvcand = nullptr;  // kMaxGrid * kMaxK (key-value candidates)
+  uint64_t* kvheads = nullptr; // kMaxGrid
+  uint64_t* kvkths = nullptr;  // kMaxGrid
   unsigned* ticket = nullptr;  // 1 word, kept at 0 between calls
 };
 
@@ -46,8 +50,11 @@ constexpr size_t kCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(int);
 constexpr size_t kHeadBytes = (size_t)kMaxGrid * sizeof(int);
 constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
 constexpr size_t kStatBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
-constexpr size_t kScratchBytes =
-    kCandBytes + 2 * kHeadBytes + kPartBytes + kStatBytes + 256;
+constexpr size_t kKvCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(uint64_t);
+constexpr size_t kKvHeadBytes = (size_t)kMaxGrid * sizeof(uint64_t);
+constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes +
+                                 kStatBytes + kKvCandBytes +
+                                 2 * kKvHeadBytes + 256;
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Scratch> g_cache;
@@ -113,6 +120,12 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   b += kPartBytes;
   s.spart = (uint64_t*)b;
   b += kStatBytes;
+  s.kvcand = (uint64_t*)b;
+  b += kKvCandBytes;
+  s.kvheads = (uint64_t*)b;
+  b += kKvHeadBytes;
+  s.kvkths = (uint64_t*)b;
+  b += kKvHeadBytes;
   s.ticket = (unsigned*)b;
   // A kernel (not a memset) clears the counter, ordered on the caller's
   // stream before the first real launch.
@@ -178,6 +191,63 @@ const void* topk_fn(int k) {
   if (k <= 32) return (const void*)&topk_kernel<32, true, kTileVec>;
   if (k <= 64) return (const void*)&topk_kernel<64, false, kTileVec>;
   return (const void*)&topk_kernel<128, false, kTileVec>;
+}
+
+template <bool F32>
+const void* topk_kv_fn(int k) {
+  if (k <= 8) return (const void*)&topk_kv_kernel<8, true, kTileVec, F32>;
+  if (k <= 16) return (const void*)&topk_kv_kernel<16, true, kTileVec, F32>;
+  if (k <= 24) return (const void*)&topk_kv_kernel<24, true, kTileVec, F32>;
+  if (k <= 32) return (const void*)&topk_kv_kernel<32, true, kTileVec, F32>;
+  if (k <= 64) return (const void*)&topk_kv_kernel<64, false, kTileVec, F32>;
+  return (const void*)&topk_kv_kernel<128, false, kTileVec, F32>;
+}
+
+// Both key-value entry points: values are 32-bit words (int32 or float32
+// bits); F32 selects the float order.
+int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
+            int64_t* out_i, libtopk_stream_t stream, bool f32) {
+  if (!in || !out_v || !out_i) return LIBTOPK_ERR_INVALID;
+  if (((uintptr_t)in & 3u) || ((uintptr_t)out_v & 3u) ||
+      ((uintptr_t)out_i & 7u))
+    return LIBTOPK_ERR_INVALID;
+  if (n < 1 || n >= kMaxN) return LIBTOPK_ERR_INVALID;
+  if (k < 1 || (int64_t)k > n) return LIBTOPK_ERR_INVALID;
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (overlaps(in, (size_t)n * 4, out_v, (size_t)k * 4) ||
+      overlaps(in, (size_t)n * 4, out_i, (size_t)k * 8) ||
+      overlaps(out_v, (size_t)k * 4, out_i, (size_t)k * 8))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  const Plan pl = plan(in, n, cus);
+  TopkKvParams p;
+  p.in = in;
+  p.n = n;
+  p.head = pl.head;
+  p.ntiles = pl.ntiles;
+  p.covered = pl.covered;
+  p.k = k;
+  p.grid = pl.grid;
+  p.refresh = kRefreshPeriod;
+  p.cand = sc.kvcand;
+  p.heads = sc.kvheads;
+  p.kths = sc.kvkths;
+  p.ticket = sc.ticket;
+  p.out_v = out_v;
+  p.out_i = out_i;
+  return launch(f32 ? topk_kv_fn<true>(k) : topk_kv_fn<false>(k), pl.grid,
+                p, s);
 }
 
 const void* reduce_fn(int op) {
@@ -263,6 +333,18 @@ int reduce_i32(const int32_t* in, int64_t n, int32_t op, int64_t* out_i64,
   p.ticket = sc.ticket;
   p.out = out_i64;
   return launch(reduce_fn(op), pl.grid, p, s);
+}
+
+int topk_kv_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out_values,
+                int64_t* out_indices, libtopk_stream_t stream) {
+  return topk_kv(in, n, k, out_values, out_indices, stream, false);
+}
+
+int topk_kv_f32(const float* in, int64_t n, int32_t k, float* out_values,
+                int64_t* out_indices, libtopk_stream_t stream) {
+  return topk_kv(reinterpret_cast<const int32_t*>(in), n, k,
+                 reinterpret_cast<int32_t*>(out_values), out_indices, stream,
+                 true);
 }
 
 int reduce_stats_i32(const int32_t* in, int64_t n, int64_t* out,

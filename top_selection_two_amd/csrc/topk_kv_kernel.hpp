@@ -1,0 +1,668 @@
+// Key-value Top-K: the k largest elements of an int32 or float32 array
+// together with their positions, both stages in one launch.
+//
+// Sources:
+//   [TopK]  "CUDA并行优化实战：从TopK问题剖析共享内存与规约算法设计", §2
+//           (the two-stage design), §6 (the reduction keeps a candidate
+//           list of items ordered by their score).
+//   [Radix] "GPU基数排序优化：10亿级数据处理与性能调优", §8 (key-value pairs
+//           carried together; floating-point keys through a suitable bit
+//           transform).
+//
+// With positions the answer is unique only under a tie rule; the one used
+// here orders by value, descending, then by position, ascending.  Every
+// element becomes a 64-bit key
+//     key = (order(value) << 32) | ~position        (position < 2^32)
+// where order() maps the value to an unsigned 32-bit integer with the same
+// order (int32: flip the sign bit; float32: flip all bits of negatives,
+// the sign bit of the rest, so -0 < +0 and NaNs sit at the two ends).  The
+// keys are distinct, so "the k largest keys" is exactly the rule, and the
+// key 0 (order 0, position 2^32 - 1) is free to mark an empty list slot.
+//
+// The structure is that of topk_kernel (see there for the streaming ring,
+// the filter and the certified bound); what changes:
+//  * Lists hold keys (two VGPRs per slot); insertion compares keys.
+//  * The filter still looks at 32-bit values first.  A lane sees its
+//    elements in increasing position, so a later element whose value equals
+//    the lane's k-th entry is worse than it: the lane-local test stays
+//    "skip values <= the k-th entry's value".  The shared bound T is
+//    certified on values only, and an element whose value equals T may
+//    still win on position, so that test becomes "skip values < T".
+//  * The epilogue bound is the exact k-th largest lane-head KEY, found by
+//    ranking the 256 head keys; entries with keys >= it (usually about k)
+//    are ranked by key.  If too many reach it, the k-th largest key is
+//    selected by counting (two 32-bit radix passes) and exactly k remain.
+//  * Stage 2 works on keys throughout: block maxima and k-th keys certify
+//    the bound T2, survivors are ranked by key (or selected by counting),
+//    and the result is written as values (in the input's own bits) plus
+//    int64 positions.
+#pragma once
+
+#include "topk_kernel.hpp"
+
+namespace ltk {
+
+struct TopkKvParams {
+  const int* in;      // int32 values, or float32 bit patterns
+  int64_t n;          // < 2^32
+  int64_t head;       // leading elements before the first 16-byte boundary
+  int64_t ntiles;     // full tiles of the aligned body
+  int64_t covered;    // elements in those tiles (they start at `head`)
+  int k;
+  int grid;
+  int refresh;        // certificate refresh period, in tiles (power of 2)
+  uint64_t* cand;     // [grid * k]  per-block candidate keys, descending
+  uint64_t* heads;    // [grid]      largest candidate key of each block
+  uint64_t* kths;     // [grid]      k-th largest candidate key of each block
+  unsigned* ticket;   // completion counter; 0 between calls
+  int* out_v;         // [k]         values (input bits), descending
+  int64_t* out_i;     // [k]         their positions
+};
+
+// The value as a signed int32 with the order the keys use: the identity for
+// int32; for float32 bits b, b with the 31 low bits flipped when negative.
+// The map is its own inverse.
+template <bool F32>
+__device__ __forceinline__ int kv_value(int b) {
+  return F32 ? (b ^ ((b >> 31) & 0x7fffffff)) : b;
+}
+
+__device__ __forceinline__ uint64_t kv_key(int s, uint32_t pos) {
+  return ((uint64_t)bias(s) << 32) | (uint32_t)~pos;
+}
+__device__ __forceinline__ int key_value(uint64_t key) {
+  return unbias((unsigned)(key >> 32));
+}
+__device__ __forceinline__ uint32_t key_pos(uint64_t key) {
+  return ~(uint32_t)key;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) {
+  return a < b ? a : b;
+}
+
+// Insert key x into the descending key list (see list_insert); returns the
+// evicted key.
+template <int KCAP, bool FIT>
+__device__ __forceinline__ uint64_t kv_list_insert(uint64_t (&L)[KCAP],
+                                                   uint64_t x, int k) {
+  static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
+#pragma unroll
+  for (int c = 0; c < KCAP; c += 8) {
+    if (FIT || c < k) {
+#pragma unroll
+      for (int i = c; i < c + 8; ++i) {
+        const uint64_t lo = umin64(L[i], x);
+        L[i] = umax64(L[i], x);
+        x = lo;
+      }
+    }
+  }
+  return x;
+}
+
+// thr: skip elements whose value is <= thr (64-bit, so "skip nothing" is
+// representable).  tsk: the shared bound's contribution, T - 1.
+template <int KCAP, bool FIT>
+__device__ __forceinline__ void kv_admit(uint64_t (&L)[KCAP], int s,
+                                         uint32_t pos, int k, int64_t tsk,
+                                         int64_t& thr) {
+  if (ballot((int64_t)s > thr)) {
+    const uint64_t e = kv_list_insert<KCAP, FIT>(L, kv_key(s, pos), k);
+    // A real evicted key bounds every later element of this lane (they come
+    // at larger positions); the empty-slot key 0 bounds nothing.
+    if (e != 0) thr = max(thr, (int64_t)key_value(e));
+    thr = max(thr, tsk);
+  }
+}
+
+template <bool F32, int U>
+__device__ __forceinline__ void kv_values(v4i (&d)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    d[u].x = kv_value<F32>(d[u].x);
+    d[u].y = kv_value<F32>(d[u].y);
+    d[u].z = kv_value<F32>(d[u].z);
+    d[u].w = kv_value<F32>(d[u].w);
+  }
+}
+
+// One tile (values already in key order): max-of-16 vote, then per vector,
+// then per element.  pos0: position of this lane's first element of vector
+// u = 0; vector u starts 4 * kBlock * u positions later.
+template <int KCAP, bool FIT, int U>
+__device__ __forceinline__ void kv_consume(uint64_t (&L)[KCAP],
+                                           const v4i (&d)[U], uint32_t pos0,
+                                           int k, int64_t tsk, int64_t& thr) {
+  int mu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    mu[u] = max(max(d[u].x, d[u].y), max(d[u].z, d[u].w));
+  int m = mu[0];
+#pragma unroll
+  for (int u = 1; u < U; ++u) m = max(m, mu[u]);
+  if (!ballot((int64_t)m > thr)) return;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!ballot((int64_t)mu[u] > thr)) continue;
+    const uint32_t p = pos0 + (uint32_t)(4 * kBlock * u);
+    kv_admit<KCAP, FIT>(L, d[u].x, p, k, tsk, thr);
+    kv_admit<KCAP, FIT>(L, d[u].y, p + 1, k, tsk, thr);
+    kv_admit<KCAP, FIT>(L, d[u].z, p + 2, k, tsk, thr);
+    kv_admit<KCAP, FIT>(L, d[u].w, p + 3, k, tsk, thr);
+  }
+}
+
+// First tile: a bitonic network over the 4U keys (see init_list).
+template <int KCAP, int U>
+__device__ __forceinline__ void kv_init_list(uint64_t (&L)[KCAP],
+                                             const v4i (&d)[U], uint32_t pos0,
+                                             int64_t& thr) {
+  constexpr int M = 4 * U;
+  static_assert((M & (M - 1)) == 0, "the network needs a power of two");
+  uint64_t v[M];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t p = pos0 + (uint32_t)(4 * kBlock * u);
+    v[4 * u + 0] = kv_key(d[u].x, p);
+    v[4 * u + 1] = kv_key(d[u].y, p + 1);
+    v[4 * u + 2] = kv_key(d[u].z, p + 2);
+    v[4 * u + 3] = kv_key(d[u].w, p + 3);
+  }
+#pragma unroll
+  for (int size = 2; size <= M; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t hi = umax64(v[i], v[j]);
+          const uint64_t lo = umin64(v[i], v[j]);
+          const bool desc = (i & size) == 0;
+          v[i] = desc ? hi : lo;
+          v[j] = desc ? lo : hi;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) L[i] = i < M ? v[i] : 0ull;
+  if (KCAP <= M) thr = max(thr, (int64_t)key_value(L[KCAP - 1]));
+}
+
+// Certified value bound from the lane-head snapshot (see refresh_bound);
+// the head value is the key's high word.
+template <int KCAP, class SH>
+__device__ __forceinline__ void kv_refresh_bound(const uint64_t (&L)[KCAP],
+                                                 int k, int& tsh, int64_t& thr,
+                                                 SH& sh) {
+  __hip_atomic_store(&sh.heads[threadIdx.x], (unsigned)(L[0] >> 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  unsigned u[kWaves];
+  int mx = kI32Min;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    u[j] = __hip_atomic_load(&sh.heads[lane() + kWave * j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+    mx = max(mx, unbias(u[j]));
+  }
+  const RegCount<kWaves> cnt{u};
+  const unsigned lo = bias(tsh);
+  if (cnt(lo) >= k) {
+    mx = wave_max(mx);
+    tsh = unbias(radix_lower_bound(lo, bias(mx), k, 6, cnt));
+  }
+  thr = max(thr, (int64_t)tsh - 1);
+}
+
+// Ranks of distinct keys by counting (see block_rank64 and rank_all, which
+// do the same for values): the rank of keys[i] is the number of larger
+// keys.  kv_block_rank64: n <= 64 keys, whole workgroup, ranks[] zero on
+// entry, barriers inside.  kv_rank_all: n <= kBlock, one key per thread,
+// keys[] with room for n rounded up to 8; a barrier inside.  Slots past n
+// are set to 0, which no real key is below.
+__device__ __forceinline__ uint64_t kv_block_rank64(uint64_t* keys, int n,
+                                                    int* ranks) {
+  const int i = threadIdx.x & (kWave - 1);
+  const int g = threadIdx.x / kWave;
+  if ((int)threadIdx.x >= n && threadIdx.x < kWave) keys[threadIdx.x] = 0ull;
+  __syncthreads();
+  const uint64_t v = keys[i];
+  const v4i* q = reinterpret_cast<const v4i*>(keys + 16 * g);
+  int r = 0;
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) {
+    const v4i o4 = q[qq];
+    const uint64_t a = ((uint64_t)(uint32_t)o4.y << 32) | (uint32_t)o4.x;
+    const uint64_t b = ((uint64_t)(uint32_t)o4.w << 32) | (uint32_t)o4.z;
+    r += (a > v) + (b > v);
+  }
+  if (i < n && r > 0) atomicAdd(&ranks[i], r);
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ int kv_rank_all(uint64_t* keys, int n,
+                                           uint64_t& v) {
+  const int t = threadIdx.x;
+  const int n8 = (n + 7) & ~7;
+  for (int j = n + t; j < n8; j += kBlock) keys[j] = 0ull;
+  __syncthreads();
+  v = keys[t];
+  const v4i* q = reinterpret_cast<const v4i*>(keys);
+  int r = 0;
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    v4i o4[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) o4[qq] = q[j0 / 2 + qq];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint64_t a = ((uint64_t)(uint32_t)o4[qq].y << 32) |
+                         (uint32_t)o4[qq].x;
+      const uint64_t b = ((uint64_t)(uint32_t)o4[qq].w << 32) |
+                         (uint32_t)o4[qq].z;
+      r += (a > v) + (b > v);
+    }
+  }
+  return r;
+}
+
+// Append the lanes where p holds to an LDS key list (one LDS atomic per
+// wave); returns the wave's base position (wave-uniform).
+__device__ __forceinline__ int kv_wave_append(bool p, uint64_t v,
+                                              int* counter, uint64_t* dst,
+                                              int cap) {
+  const uint64_t b = ballot(p);
+  if (b == 0) return 0;
+  int base = 0;
+  if (lane() == 0) base = atomicAdd(counter, popc(b));
+  base = uni(base);
+  const int pos = base + lanes_below(b);
+  if (p && pos < cap) dst[pos] = v;
+  return base;
+}
+
+// The k-th largest of a set of distinct keys spread over the workgroup, by
+// counting: a 32-bit radix pass on the high words, then one on the low
+// words among the keys with that high word.  visit(f) calls f(key) for
+// each key this thread holds (a fixed, uniform loop structure); at least k
+// keys must exist.  Barriers inside: call uniformly.
+template <class SH, class Visit>
+__device__ __forceinline__ uint64_t kv_select(int k, SH& sh, Visit&& visit) {
+  int parity = 0;
+  auto count_hi = [&](unsigned c) __attribute__((always_inline)) -> int {
+    int m = 0;
+    visit([&](uint64_t key) { m += (unsigned)(key >> 32) >= c; });
+    return block_sum(m, sh, parity);
+  };
+  const unsigned ghi = radix_select(0u, 0xffffffffu, k, count_hi);
+  int above = 0;
+  visit([&](uint64_t key) { above += (unsigned)(key >> 32) > ghi; });
+  above = block_sum(above, sh, parity);
+  auto count_lo = [&](unsigned c) __attribute__((always_inline)) -> int {
+    int m = 0;
+    visit([&](uint64_t key) {
+      m += ((unsigned)(key >> 32) == ghi) & ((unsigned)key >= c);
+    });
+    return block_sum(m, sh, parity);
+  };
+  const unsigned glo = radix_select(0u, 0xffffffffu, k - above, count_lo);
+  return ((uint64_t)ghi << 32) | glo;
+}
+
+// ---- LDS layouts ----------------------------------------------------------
+template <int KCAP>
+struct TopkKvShared {
+  unsigned heads[kBlock];                 // lane-head snapshot (biased)
+  alignas(16) uint64_t hkeys[kBlock + 8]; // lane-head keys, then ranks' use
+  alignas(16) uint64_t blist[kBlock + 8]; // keys >= the final bound
+  int ranks[kWave];
+  int bcnt;
+  int red[2][kWaves];
+  int bcast[8];
+  uint64_t bkey[2];
+  int is_last;
+};
+
+constexpr int kKvSurvCap = 512;  // stage-2 survivor keys staged in LDS
+struct KvStage2Lds {
+  alignas(16) uint64_t surv[kKvSurvCap + 8];
+  alignas(16) uint64_t gmax[kBlock + 8];  // group maxima of the block maxima
+  uint64_t heads[kMaxGrid];
+  int blocks[kMaxGrid];                   // blocks whose maximum reaches T2
+  int gmax_rank[kWave];
+  int surv_rank[kWave];
+};
+
+// Visit the candidate keys of the flagged blocks, 8 agent-coherent 8-byte
+// loads per thread in flight at a time; f(valid, key) is called uniformly.
+template <class F>
+__device__ __forceinline__ void kv_scan_flagged(const TopkKvParams& p,
+                                                const int* blocks, int total,
+                                                F&& f) {
+  const int k = p.k;
+  constexpr int B = 8;
+  for (int base = 0; base < total; base += kBlock * B) {
+    uint64_t v[B];
+    bool ok[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      int idx = base + j * kBlock + (int)threadIdx.x;
+      ok[j] = idx < total;
+      idx = ok[j] ? idx : total - 1;
+      const int fb = idx / k;
+      const int e = idx - fb * k;
+      v[j] = ld_agent(p.cand + (int64_t)blocks[fb] * k + e);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) f(ok[j], v[j]);
+  }
+}
+
+// Write the i-th result (rank r < k) from its key.
+template <bool F32>
+__device__ __forceinline__ void kv_write_out(const TopkKvParams& p, int r,
+                                             uint64_t key) {
+  p.out_v[r] = kv_value<F32>(key_value(key));
+  p.out_i[r] = (int64_t)key_pos(key);
+}
+
+// ---- stage 2 --------------------------------------------------------------
+// The grid's k largest keys from the per-block candidates:
+//  1. block maxima into LDS (one round trip), the largest block k-th key
+//     T2b on the way;
+//  2. T2a = the k-th largest of group maxima over disjoint groups of blocks
+//     (64 groups for k <= 64, else 256, ranked by key); T2 = max(T2a, T2b):
+//     at least k candidate keys are >= T2;
+//  3. survivors = candidate keys >= T2 of the blocks whose maximum reaches
+//     it (read from memory), into LDS;
+//  4. up to 256 survivors are ranked; more are cut to exactly k by
+//     selecting the k-th largest key by counting, then ranked.
+template <bool F32, int KCAP>
+__device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
+                                               TopkKvShared<KCAP>& sh,
+                                               KvStage2Lds& s2) {
+  const int G = p.grid, k = p.k, tid = threadIdx.x;
+  const int w = tid / kWave;
+  if (tid < kWave) {
+    s2.gmax_rank[tid] = 0;
+    s2.surv_rank[tid] = 0;
+  }
+  if (tid == 0) {
+    sh.bcast[2] = 0;  // survivors
+    sh.bcast[5] = 0;  // flagged blocks
+    sh.bkey[0] = 0;   // T2b
+    sh.bkey[1] = 0;   // T2a (stays 0 when equal empty-group keys tie)
+  }
+  // (1) block maxima into LDS, whole KiB chunks (the heads area holds
+  // kMaxGrid keys, so the last chunk stays inside it).
+  {
+    const int ws = __builtin_amdgcn_readfirstlane(w);
+    const char* hsrc = reinterpret_cast<const char*>(uni_ptr(p.heads));
+    const uint32_t hlds = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)lds_offset(s2.heads));
+    const uint32_t voff = (uint32_t)lane() * 16u;
+    const int chunks = (G * 8 + 1023) / 1024;
+    for (int c = ws; c < chunks; c += kWaves)
+      copy_1k_to_lds(hsrc + c * 1024, hlds + c * 1024u, voff);
+  }
+  uint64_t kt = 0;
+  for (int b = tid; b < G; b += kBlock) kt = umax64(kt, ld_agent(p.kths + b));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  {
+    const uint32_t lo = (uint32_t)kt, hi = (uint32_t)(kt >> 32);
+    // wave max of a 64-bit key: high words first, then low words of the
+    // lanes holding the top high word
+    const unsigned whi = (unsigned)unbias(wave_max(unbias(hi)));
+    const unsigned wlo = (unsigned)unbias(
+        wave_max(unbias(hi == whi ? lo : 0u)));
+    if (lane() == 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(&sh.bkey[0]),
+                (unsigned long long)(((uint64_t)whi << 32) | wlo));
+  }
+  // (2) group maxima
+  const bool narrow = k <= kWave;
+  if (narrow) {
+    if (w == 0) {
+      const int per = (G + kWave - 1) / kWave;
+      uint64_t gm = 0;
+      for (int j = 0; j < per; ++j) {
+        const int b = lane() * per + j;
+        if (b < G) gm = umax64(gm, s2.heads[b]);
+      }
+      s2.gmax[lane()] = gm;
+    }
+  } else {
+    const int per = (G + kBlock - 1) / kBlock;
+    uint64_t gm = 0;
+    for (int j = 0; j < per; ++j) {
+      const int b = tid * per + j;
+      if (b < G) gm = umax64(gm, s2.heads[b]);
+    }
+    s2.gmax[tid] = gm;
+  }
+  __syncthreads();
+  // The k-th largest group maximum.  Empty groups hold 0, which certifies
+  // nothing (with fewer than k blocks the bound is 0).
+  if (narrow) {
+    const uint64_t gv = kv_block_rank64(s2.gmax, kWave, s2.gmax_rank);
+    if (tid < kWave && s2.gmax_rank[tid] == k - 1) sh.bkey[1] = gv;
+  } else {
+    uint64_t gv;
+    if (kv_rank_all(s2.gmax, kBlock, gv) == k - 1) sh.bkey[1] = gv;
+  }
+  __syncthreads();
+  const uint64_t T2 = umax64(sh.bkey[0], sh.bkey[1]);
+
+  // (3) flagged blocks, then their candidate keys >= T2
+  for (int b0 = 0; b0 < G; b0 += kBlock) {
+    const int b = b0 + tid;
+    const bool f = b < G && s2.heads[b] >= T2;
+    wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
+  }
+  __syncthreads();
+  const int total = sh.bcast[5] * k;
+  kv_scan_flagged(p, s2.blocks, total, [&](bool ok, uint64_t c) {
+    kv_wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv, kKvSurvCap);
+  });
+  __syncthreads();
+  int m = sh.bcast[2];
+
+  // (4) cut to exactly k when there are too many to rank
+  if (m > kBlock) {
+    uint64_t g;
+    if (m <= kKvSurvCap) {
+      g = kv_select(k, sh, [&](auto&& f) {
+        for (int i = tid; i < m; i += kBlock) f(s2.surv[i]);
+      });
+    } else {
+      g = kv_select(k, sh, [&](auto&& f) {
+        kv_scan_flagged(p, s2.blocks, total, [&](bool ok, uint64_t c) {
+          if (ok && c >= T2) f(c);
+        });
+      });
+    }
+    // Exactly k keys are >= g: gather them afresh.
+    __syncthreads();
+    if (tid == 0) sh.bcast[2] = 0;
+    __syncthreads();
+    if (m <= kKvSurvCap) {
+      for (int i0 = 0; i0 < m; i0 += kBlock) {
+        const int i = i0 + tid;
+        const uint64_t c = i < m ? s2.surv[i] : 0ull;
+        const bool q = i < m && c >= g;
+        __syncthreads();  // every read of this round before any write
+        kv_wave_append(q, c, &sh.bcast[2], s2.surv, kKvSurvCap);
+      }
+    } else {
+      kv_scan_flagged(p, s2.blocks, total, [&](bool ok, uint64_t c) {
+        kv_wave_append(ok && c >= g, c, &sh.bcast[2], s2.surv, kKvSurvCap);
+      });
+    }
+    __syncthreads();
+    m = sh.bcast[2];  // == k
+  }
+  if (m <= kWave) {
+    const uint64_t v = kv_block_rank64(s2.surv, m, s2.surv_rank);
+    if (tid < m) {
+      const int r = s2.surv_rank[tid];
+      if (r < k) kv_write_out<F32>(p, r, v);
+    }
+  } else {
+    uint64_t v;
+    const int r = kv_rank_all(s2.surv, m, v);
+    if (tid < m && r < k) kv_write_out<F32>(p, r, v);
+  }
+  if (tid == 0) st_agent(p.ticket, 0u);
+}
+
+template <int KCAP, bool FIT, int U, bool F32>
+__global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
+  __shared__ TopkKvShared<KCAP> sh;
+  __shared__ v4i ring_lds[kWaves][kRing][U][kWave];
+  static_assert(sizeof(ring_lds) >= sizeof(KvStage2Lds), "ring too small");
+  const int blk = blockIdx.x;
+  const int k = p.k;
+  const int w = threadIdx.x / kWave;
+
+  uint64_t L[KCAP];
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) L[i] = 0ull;
+  int tsh = kI32Min;               // this wave's certified value bound
+  int64_t thr = INT64_MIN;         // skip values <= thr
+  sh.heads[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) sh.bcnt = 0;
+  if (threadIdx.x < kWave) sh.ranks[threadIdx.x] = 0;
+  __syncthreads();
+
+  // ---- stage 1: the streaming ring of topk_kernel ----------------------
+  const v4i* __restrict__ body = reinterpret_cast<const v4i*>(p.in + p.head);
+  const int64_t count = tiles_of(p.ntiles, blk, p.grid);
+  const int R = p.refresh;
+  if (count > 0) {
+    v4i(*ring)[U][kWave] = ring_lds[w];
+    uint32_t voff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      voff[u] = (uint32_t)((u * kBlock + threadIdx.x) * sizeof(v4i));
+    const char* first = reinterpret_cast<const char*>(body) +
+                        (int64_t)blk * kTileBytes<U>;
+    const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+      if (j < count) issue_tile_lds<U>(first + j * stride, voff, ring[j]);
+    for (int64_t i = 0; i < count; ++i) {
+      wait_tile_loads<U, kRing>(i + kRing - 1 < count);
+      const int slot = (int)(i & (kRing - 1));
+      v4i d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = ring[slot][u][lane()];
+      wait_lds_reads();
+      if (i + kRing < count)
+        issue_tile_lds<U>(first + (i + kRing) * stride, voff, ring[slot]);
+      kv_values<F32, U>(d);
+      // Position of this lane's first element of the tile.
+      const uint32_t pos0 = (uint32_t)(
+          p.head + 4 * ((blk + i * p.grid) * (int64_t)(kBlock * U) +
+                        (int64_t)threadIdx.x));
+      if (i == 0)
+        kv_init_list<KCAP, U>(L, d, pos0, thr);
+      else
+        kv_consume<KCAP, FIT, U>(L, d, pos0, k, (int64_t)tsh - 1, thr);
+      if (refresh_due(i, R)) kv_refresh_bound(L, k, tsh, thr, sh);
+    }
+  }
+  // The unaligned head and the tail: positions out of the lane's order, so
+  // only the shared bound (index-free) filters them; insertion compares
+  // whole keys.
+  if (blk == p.grid - 1) {
+    const int64_t left = p.n - p.covered;
+    for (int64_t base = 0; base < left; base += kBlock) {
+      const int64_t i = base + threadIdx.x;
+      const bool ok = i < left;
+      const int64_t pos = i < p.head ? i : p.covered + i;
+      const int s = ok ? kv_value<F32>(p.in[pos]) : kI32Min;
+      const bool q = ok && s >= tsh;
+      // Inserting the empty key 0 leaves a list unchanged.
+      if (ballot(q))
+        kv_list_insert<KCAP, FIT>(L, q ? kv_key(s, (uint32_t)pos) : 0ull, k);
+    }
+  }
+
+  // ---- epilogue: the block's k largest keys ------------------------------
+  // T = the exact k-th largest lane-head key (k distinct heads reach it, so
+  // every one of the block's top-k keys does too).
+  sh.hkeys[threadIdx.x] = L[0];
+  if (threadIdx.x == 0) sh.bkey[0] = 0;
+  uint64_t hv;
+  if (kv_rank_all(sh.hkeys, kBlock, hv) == k - 1) sh.bkey[0] = hv;
+  __syncthreads();
+  const uint64_t T = sh.bkey[0];
+  uint64_t* dst = p.cand + (int64_t)blk * k;
+  {
+    bool more = true;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) {
+      if (more) {
+        const bool q = i < k && L[i] >= T && L[i] != 0ull;
+        const uint64_t b = ballot(q);
+        more = b != 0;
+        if (more) {
+          int base = 0;
+          if (lane() == 0) base = atomicAdd(&sh.bcnt, popc(b));
+          base = uni(base);
+          const int pos = base + lanes_below(b);
+          if (q && pos < kBlock) sh.blist[pos] = L[i];
+          more = base + popc(b) < kBlock;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  int lb = sh.bcnt;
+  if (lb > kBlock) {
+    // Too many keys reach T: select the k-th largest g among the list
+    // entries >= T by counting, then keep exactly the k keys >= g.
+    const uint64_t g = kv_select(k, sh, [&](auto&& f) {
+#pragma unroll
+      for (int i = 0; i < KCAP; ++i)
+        if (i < k && L[i] >= T && L[i] != 0ull) f(L[i]);
+    });
+    if (threadIdx.x == 0) sh.bcnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KCAP; ++i) {
+      const bool q = i < k && L[i] >= g && L[i] != 0ull;
+      kv_wave_append(q, L[i], &sh.bcnt, sh.blist, kBlock);
+    }
+    __syncthreads();
+    lb = sh.bcnt;  // == k
+  }
+  {
+    uint64_t v;
+    int rk = kBlock;
+    if (lb <= kWave) {
+      v = kv_block_rank64(sh.blist, lb, sh.ranks);
+      if ((int)threadIdx.x < lb) rk = sh.ranks[threadIdx.x];
+    } else {
+      rk = kv_rank_all(sh.blist, lb, v);
+    }
+    if ((int)threadIdx.x < lb && rk < k) {
+      st_agent(dst + rk, v);
+      if (rk == 0) st_agent(p.heads + blk, v);
+      if (rk == k - 1) st_agent(p.kths + blk, v);
+    }
+  }
+
+  // ---- hand-off: the last workgroup to finish runs stage 2 --------------
+  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
+  topk_kv_stage2<F32, KCAP>(
+      p, sh, *reinterpret_cast<KvStage2Lds*>(&ring_lds[0][0][0][0]));
+}
+
+}  // namespace ltk
