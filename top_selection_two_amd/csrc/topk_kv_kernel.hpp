@@ -85,8 +85,16 @@ __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) {
 }
 
 // Insert key x into the descending key list (see list_insert); returns the
-// evicted key.
-template <int KCAP, bool FIT>
+// evicted key.  One comparison per slot decides both the slot's new key and
+// the key carried on.
+//
+// LANE_ORDER: x comes after every key already in this lane's list (larger
+// position), which holds for the whole stream: a lane visits its elements
+// in increasing position.  Then the key order is the value order with x
+// placed after equal values, so comparing the high (value) words alone is
+// exact.  Otherwise (the head and tail elements visited last) whole keys are
+// compared.
+template <int KCAP, bool FIT, bool LANE_ORDER>
 __device__ __forceinline__ uint64_t kv_list_insert(uint64_t (&L)[KCAP],
                                                    uint64_t x, int k) {
   static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
@@ -95,9 +103,12 @@ __device__ __forceinline__ uint64_t kv_list_insert(uint64_t (&L)[KCAP],
     if (FIT || c < k) {
 #pragma unroll
       for (int i = c; i < c + 8; ++i) {
-        const uint64_t lo = umin64(L[i], x);
-        L[i] = umax64(L[i], x);
-        x = lo;
+        const uint64_t li = L[i];
+        const bool gt = LANE_ORDER
+                            ? (uint32_t)(x >> 32) > (uint32_t)(li >> 32)
+                            : x > li;
+        L[i] = gt ? x : li;
+        x = gt ? li : x;
       }
     }
   }
@@ -111,7 +122,8 @@ __device__ __forceinline__ void kv_admit(uint64_t (&L)[KCAP], int s,
                                          uint32_t pos, int k, int64_t tsk,
                                          int64_t& thr) {
   if (ballot((int64_t)s > thr)) {
-    const uint64_t e = kv_list_insert<KCAP, FIT>(L, kv_key(s, pos), k);
+    const uint64_t e =
+        kv_list_insert<KCAP, FIT, true>(L, kv_key(s, pos), k);
     // A real evicted key bounds every later element of this lane (they come
     // at larger positions); the empty-slot key 0 bounds nothing.
     if (e != 0) thr = max(thr, (int64_t)key_value(e));
@@ -180,11 +192,12 @@ __device__ __forceinline__ void kv_init_list(uint64_t (&L)[KCAP],
       for (int i = 0; i < M; ++i) {
         const int j = i ^ stride;
         if (j > i) {
-          const uint64_t hi = umax64(v[i], v[j]);
-          const uint64_t lo = umin64(v[i], v[j]);
+          // one comparison: swap when the pair is out of this stage's order
           const bool desc = (i & size) == 0;
-          v[i] = desc ? hi : lo;
-          v[j] = desc ? lo : hi;
+          const bool swap = desc ? v[j] > v[i] : v[i] > v[j];
+          const uint64_t a = v[i];
+          v[i] = swap ? v[j] : a;
+          v[j] = swap ? a : v[j];
         }
       }
     }
@@ -590,19 +603,60 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       const bool q = ok && s >= tsh;
       // Inserting the empty key 0 leaves a list unchanged.
       if (ballot(q))
-        kv_list_insert<KCAP, FIT>(L, q ? kv_key(s, (uint32_t)pos) : 0ull, k);
+        kv_list_insert<KCAP, FIT, false>(L, q ? kv_key(s, (uint32_t)pos) : 0ull,
+                                         k);
     }
   }
 
   // ---- epilogue: the block's k largest keys ------------------------------
   // T = the exact k-th largest lane-head key (k distinct heads reach it, so
-  // every one of the block's top-k keys does too).
+  // every one of the block's top-k keys does too), found by every wave from
+  // the final snapshot: the k-th largest head value by radix select over
+  // ballots, then, among the heads of that value, the right one by their
+  // low words (a second search only when several heads share the value).
+  sh.heads[threadIdx.x] = (unsigned)(L[0] >> 32);
   sh.hkeys[threadIdx.x] = L[0];
-  if (threadIdx.x == 0) sh.bkey[0] = 0;
-  uint64_t hv;
-  if (kv_rank_all(sh.hkeys, kBlock, hv) == k - 1) sh.bkey[0] = hv;
   __syncthreads();
-  const uint64_t T = sh.bkey[0];
+  uint64_t T;
+  {
+    unsigned u[kWaves];
+    uint32_t lw[kWaves];
+    int mx = kI32Min;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) {
+      u[j] = sh.heads[lane() + kWave * j];
+      lw[j] = (uint32_t)sh.hkeys[lane() + kWave * j];
+      mx = max(mx, unbias(u[j]));
+    }
+    mx = wave_max(mx);
+    const RegCount<kWaves> cnt{u};
+    // tsh is certified on these heads (they only grew since), so the
+    // search may start there.
+    const unsigned tv = radix_select(bias(tsh), bias(mx), k, cnt);
+    const int above = tv == 0xffffffffu ? 0 : cnt(tv + 1u);
+    const int need = k - above;  // >= 1 heads of value tv are needed
+    int ties = 0;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) ties += popc(ballot(u[j] == tv));
+    uint32_t tl;
+    if (ties == need) {
+      // all of them: the smallest low word among them
+      uint32_t m = 0xffffffffu;
+#pragma unroll
+      for (int j = 0; j < kWaves; ++j) m = u[j] == tv ? min(m, lw[j]) : m;
+      tl = (uint32_t)unbias((unsigned)wave_min(unbias(m)));
+    } else {
+      auto count_lo = [&](unsigned c) __attribute__((always_inline)) -> int {
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < kWaves; ++j)
+          n += popc(ballot(u[j] == tv && lw[j] >= c));
+        return n;
+      };
+      tl = radix_select(0u, 0xffffffffu, need, count_lo);
+    }
+    T = ((uint64_t)tv << 32) | tl;
+  }
   uint64_t* dst = p.cand + (int64_t)blk * k;
   {
     bool more = true;  // wave-uniform
