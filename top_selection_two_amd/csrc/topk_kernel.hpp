@@ -182,28 +182,51 @@ __device__ __forceinline__ void admit(int (&L)[KCAP], int x, int k, int tsh,
   }
 }
 
-// One tile's worth of values (U x 4 per lane): a max-of-16 and one vote
-// reject the whole group in the common case; otherwise each 4-element
-// vector, then each element, is tested the same way before insertion.
+// One tile's worth of values (U x 4 per lane).  A max-of-16 and one vote
+// reject the whole tile in the common case.  Otherwise each lane marks its
+// elements above its threshold and the wave runs insertion rounds: in each
+// round every lane inserts one marked element (its earliest, picked by a
+// select tree), until no lane has one left.  Admissions spread over many
+// lanes and element slots then cost one or two rounds instead of one per
+// slot.
 template <int KCAP, bool FIT, int U>
 __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
                                         int k, int tsh, int& thr) {
-  int mu[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    mu[u] = max(max(d[u].x, d[u].y), max(d[u].z, d[u].w));
-  int m = mu[0];
-#pragma unroll
-  for (int u = 1; u < U; ++u) m = max(m, mu[u]);
-  if (!ballot(m > thr)) return;
+  constexpr int M = 4 * U;
+  static_assert(M <= 16, "slot masks are 16 bits");
+  int e[M];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (!ballot(mu[u] > thr)) continue;
-    admit<KCAP, FIT>(L, d[u].x, k, tsh, thr);
-    admit<KCAP, FIT>(L, d[u].y, k, tsh, thr);
-    admit<KCAP, FIT>(L, d[u].z, k, tsh, thr);
-    admit<KCAP, FIT>(L, d[u].w, k, tsh, thr);
+    e[4 * u + 0] = d[u].x;
+    e[4 * u + 1] = d[u].y;
+    e[4 * u + 2] = d[u].z;
+    e[4 * u + 3] = d[u].w;
   }
+  int m = e[0];
+#pragma unroll
+  for (int j = 1; j < M; ++j) m = max(m, e[j]);
+  if (!ballot(m > thr)) return;
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) pend |= e[j] > thr ? (1u << j) : 0u;
+  do {
+    const uint32_t j = (uint32_t)__builtin_ctz(pend | (1u << M));
+    int a[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) a[t] = e[t];
+#pragma unroll
+    for (int w = M / 2; w >= 1; w >>= 1) {
+      const uint32_t bit = (uint32_t)((M / 2) / w);
+#pragma unroll
+      for (int t = 0; t < w; ++t) a[t] = (j & bit) ? a[2 * t + 1] : a[2 * t];
+    }
+    // The threshold may have risen since the element was marked; a lane
+    // with nothing to insert inserts INT_MIN, which changes nothing.
+    const int x = (pend != 0 && a[0] > thr) ? a[0] : kI32Min;
+    const int evicted = list_insert<KCAP, FIT>(L, x, k);
+    thr = max(thr, max(evicted, tsh));
+    pend &= pend - 1;
+  } while (ballot(pend != 0));
 }
 
 // The first tile of a lane's stream goes straight into its (empty) list:
@@ -756,6 +779,15 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
         init_list<KCAP, U>(L, d, thr);
       else
         consume<KCAP, FIT, U>(L, d, k, tsh, thr);
+      // After each of the first two tiles every lane publishes its head and
+      // the workgroup waits, so that bound refresh sees all 256 fresh
+      // heads: the early bounds are much tighter and far fewer elements are
+      // admitted in the tiles that follow.
+      if (i <= 1) {
+        __hip_atomic_store(&sh.heads[threadIdx.x], bias(L[0]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_barrier();
+      }
       if (refresh_due(i, R)) refresh_bound(L, k, tsh, thr, sh);
     }
   }

@@ -84,51 +84,59 @@ __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) {
   return a < b ? a : b;
 }
 
-// Insert key x into the descending key list (see list_insert); returns the
-// evicted key.  One comparison per slot decides both the slot's new key and
-// the key carried on.
+// A lane's candidate list: slot i holds the key (bias(v[i]) << 32) | w[i],
+// kept as its two 32-bit words (the value in its signed order, and the low
+// word ~position) so that insertion works on 32-bit registers.  Descending
+// by key; an empty slot is the key 0 (v = INT_MIN, w = 0).
+template <int KCAP>
+struct KvList {
+  int v[KCAP];
+  uint32_t w[KCAP];
+  __device__ __forceinline__ uint64_t key(int i) const {
+    return ((uint64_t)bias(v[i]) << 32) | w[i];
+  }
+};
+
+// Insert the key (xv, xw) into the list (see list_insert); on return
+// (xv, xw) is the evicted key.  One comparison per slot decides the slot's
+// new key and the key carried on.
 //
-// LANE_ORDER: x comes after every key already in this lane's list (larger
-// position), which holds for the whole stream: a lane visits its elements
-// in increasing position.  Then the key order is the value order with x
-// placed after equal values, so comparing the high (value) words alone is
-// exact.  Otherwise (the head and tail elements visited last) whole keys are
-// compared.
+// LANE_ORDER: the key comes after every key already in this lane's list
+// (larger position), which holds for the whole stream: a lane visits its
+// elements in increasing position.  Then the key order is the value order
+// with the new key placed after equal values, so the value words alone
+// decide.  One corner differs from whole keys: a value of INT_MIN never
+// displaces an empty slot.  Such an element is never needed: by then its
+// block's first tile has supplied 4096 keys that beat it (smaller
+// positions, values >= INT_MIN), and k <= 128.  Otherwise (the head and
+// tail elements visited last) whole keys are compared.
 template <int KCAP, bool FIT, bool LANE_ORDER>
-__device__ __forceinline__ uint64_t kv_list_insert(uint64_t (&L)[KCAP],
-                                                   uint64_t x, int k) {
+__device__ __forceinline__ void kv_list_insert(KvList<KCAP>& L, int& xv,
+                                               uint32_t& xw, int k) {
   static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
 #pragma unroll
   for (int c = 0; c < KCAP; c += 8) {
     if (FIT || c < k) {
 #pragma unroll
       for (int i = c; i < c + 8; ++i) {
-        const uint64_t li = L[i];
-        const bool gt = LANE_ORDER
-                            ? (uint32_t)(x >> 32) > (uint32_t)(li >> 32)
-                            : x > li;
-        L[i] = gt ? x : li;
-        x = gt ? li : x;
+        const int lv = L.v[i];
+        const uint32_t lw = L.w[i];
+        const bool gt = LANE_ORDER ? xv > lv
+                                   : (xv > lv) | ((xv == lv) & (xw > lw));
+        L.v[i] = gt ? xv : lv;
+        L.w[i] = gt ? xw : lw;
+        xv = gt ? lv : xv;
+        xw = gt ? lw : xw;
       }
     }
   }
-  return x;
 }
 
-// thr: skip elements whose value is <= thr (64-bit, so "skip nothing" is
-// representable).  tsk: the shared bound's contribution, T - 1.
-template <int KCAP, bool FIT>
-__device__ __forceinline__ void kv_admit(uint64_t (&L)[KCAP], int s,
-                                         uint32_t pos, int k, int64_t tsk,
-                                         int64_t& thr) {
-  if (ballot((int64_t)s > thr)) {
-    const uint64_t e =
-        kv_list_insert<KCAP, FIT, true>(L, kv_key(s, pos), k);
-    // A real evicted key bounds every later element of this lane (they come
-    // at larger positions); the empty-slot key 0 bounds nothing.
-    if (e != 0) thr = max(thr, (int64_t)key_value(e));
-    thr = max(thr, tsk);
-  }
+// tsk: the shared bound's contribution to the lane threshold: T - 1, or
+// INT_MIN while T is INT_MIN (values of INT_MIN are not needed after the
+// first tile, see kv_list_insert).
+__device__ __forceinline__ int kv_tsk(int tsh) {
+  return tsh == kI32Min ? kI32Min : tsh - 1;
 }
 
 template <bool F32, int U>
@@ -142,37 +150,67 @@ __device__ __forceinline__ void kv_values(v4i (&d)[U]) {
   }
 }
 
-// One tile (values already in key order): max-of-16 vote, then per vector,
-// then per element.  pos0: position of this lane's first element of vector
-// u = 0; vector u starts 4 * kBlock * u positions later.
+// One tile (values already in key order).  A max-of-16 vote rejects the
+// whole tile in the common case.  Otherwise each lane marks its elements
+// above its threshold and the wave runs insertion rounds: in each round
+// every lane inserts its earliest marked element (so a lane still inserts
+// in position order), and the rounds end when no lane has one left.  A
+// tile with a few admissions spread over many lanes and element slots
+// costs one or two rounds instead of one per slot.
 template <int KCAP, bool FIT, int U>
-__device__ __forceinline__ void kv_consume(uint64_t (&L)[KCAP],
-                                           const v4i (&d)[U], uint32_t pos0,
-                                           int k, int64_t tsk, int64_t& thr) {
-  int mu[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    mu[u] = max(max(d[u].x, d[u].y), max(d[u].z, d[u].w));
-  int m = mu[0];
-#pragma unroll
-  for (int u = 1; u < U; ++u) m = max(m, mu[u]);
-  if (!ballot((int64_t)m > thr)) return;
+__device__ __forceinline__ void kv_consume(KvList<KCAP>& L, const v4i (&d)[U],
+                                           uint32_t pos0, int k, int tsk,
+                                           int& thr) {
+  constexpr int M = 4 * U;
+  static_assert(M <= 16, "slot masks are 16 bits");
+  int e[M];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (!ballot((int64_t)mu[u] > thr)) continue;
-    const uint32_t p = pos0 + (uint32_t)(4 * kBlock * u);
-    kv_admit<KCAP, FIT>(L, d[u].x, p, k, tsk, thr);
-    kv_admit<KCAP, FIT>(L, d[u].y, p + 1, k, tsk, thr);
-    kv_admit<KCAP, FIT>(L, d[u].z, p + 2, k, tsk, thr);
-    kv_admit<KCAP, FIT>(L, d[u].w, p + 3, k, tsk, thr);
+    e[4 * u + 0] = d[u].x;
+    e[4 * u + 1] = d[u].y;
+    e[4 * u + 2] = d[u].z;
+    e[4 * u + 3] = d[u].w;
   }
+  int m = e[0];
+#pragma unroll
+  for (int j = 1; j < M; ++j) m = max(m, e[j]);
+  if (!ballot(m > thr)) return;
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) pend |= e[j] > thr ? (1u << j) : 0u;
+  do {
+    // the earliest marked slot j (M when none), its value by a select tree
+    const uint32_t j = (uint32_t)__builtin_ctz(pend | (1u << M));
+    int a[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) a[t] = e[t];
+#pragma unroll
+    for (int w = M / 2; w >= 1; w >>= 1) {
+      const uint32_t bit = (uint32_t)((M / 2) / w);
+#pragma unroll
+      for (int t = 0; t < w; ++t) a[t] = (j & bit) ? a[2 * t + 1] : a[2 * t];
+    }
+    // slot j = 4u + c lies at pos0 + 4 * kBlock * u + c
+    const uint32_t pos = pos0 + (j >> 2) * (uint32_t)(4 * kBlock) + (j & 3u);
+    // The threshold may have risen since the slot was marked; a lane with
+    // nothing to insert inserts the empty key, which changes nothing.
+    const bool act = pend != 0 && a[0] > thr;
+    int xv = act ? a[0] : kI32Min;
+    uint32_t xw = act ? ~pos : 0u;
+    kv_list_insert<KCAP, FIT, true>(L, xv, xw, k);
+    // An evicted key bounds every later element of this lane (they come at
+    // larger positions).
+    thr = max(thr, max(xv, tsk));
+    pend &= pend - 1;
+  } while (ballot(pend != 0));
 }
 
-// First tile: a bitonic network over the 4U keys (see init_list).
+// First tile: a bitonic network over the 4U keys (see init_list), on whole
+// keys.
 template <int KCAP, int U>
-__device__ __forceinline__ void kv_init_list(uint64_t (&L)[KCAP],
+__device__ __forceinline__ void kv_init_list(KvList<KCAP>& L,
                                              const v4i (&d)[U], uint32_t pos0,
-                                             int64_t& thr) {
+                                             int& thr) {
   constexpr int M = 4 * U;
   static_assert((M & (M - 1)) == 0, "the network needs a power of two");
   uint64_t v[M];
@@ -203,18 +241,20 @@ __device__ __forceinline__ void kv_init_list(uint64_t (&L)[KCAP],
     }
   }
 #pragma unroll
-  for (int i = 0; i < KCAP; ++i) L[i] = i < M ? v[i] : 0ull;
-  if (KCAP <= M) thr = max(thr, (int64_t)key_value(L[KCAP - 1]));
+  for (int i = 0; i < KCAP; ++i) {
+    L.v[i] = i < M ? key_value(v[i]) : kI32Min;
+    L.w[i] = i < M ? (uint32_t)v[i] : 0u;
+  }
+  if (KCAP <= M) thr = max(thr, L.v[KCAP - 1]);
 }
 
-// Certified value bound from the lane-head snapshot (see refresh_bound);
-// the head value is the key's high word.
+// Certified value bound from the lane-head snapshot (see refresh_bound).
 template <int KCAP, class SH>
-__device__ __forceinline__ void kv_refresh_bound(const uint64_t (&L)[KCAP],
-                                                 int k, int& tsh, int64_t& thr,
+__device__ __forceinline__ void kv_refresh_bound(const KvList<KCAP>& L,
+                                                 int k, int& tsh, int& thr,
                                                  SH& sh) {
-  __hip_atomic_store(&sh.heads[threadIdx.x], (unsigned)(L[0] >> 32),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_store(&sh.heads[threadIdx.x], bias(L.v[0]), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_WORKGROUP);
   unsigned u[kWaves];
   int mx = kI32Min;
 #pragma unroll
@@ -229,7 +269,7 @@ __device__ __forceinline__ void kv_refresh_bound(const uint64_t (&L)[KCAP],
     mx = wave_max(mx);
     tsh = unbias(radix_lower_bound(lo, bias(mx), k, 6, cnt));
   }
-  thr = max(thr, (int64_t)tsh - 1);
+  thr = max(thr, kv_tsk(tsh));
 }
 
 // Ranks of distinct keys by counting (see block_rank64 and rank_all, which
@@ -543,11 +583,14 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   const int k = p.k;
   const int w = threadIdx.x / kWave;
 
-  uint64_t L[KCAP];
+  KvList<KCAP> L;
 #pragma unroll
-  for (int i = 0; i < KCAP; ++i) L[i] = 0ull;
-  int tsh = kI32Min;               // this wave's certified value bound
-  int64_t thr = INT64_MIN;         // skip values <= thr
+  for (int i = 0; i < KCAP; ++i) {
+    L.v[i] = kI32Min;
+    L.w[i] = 0u;
+  }
+  int tsh = kI32Min;   // this wave's certified value bound
+  int thr = kI32Min;   // skip values <= thr (the first tile skips nothing)
   sh.heads[threadIdx.x] = 0u;
   if (threadIdx.x == 0) sh.bcnt = 0;
   if (threadIdx.x < kWave) sh.ranks[threadIdx.x] = 0;
@@ -566,6 +609,9 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     const char* first = reinterpret_cast<const char*>(body) +
                         (int64_t)blk * kTileBytes<U>;
     const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
+    // First position of tile i of this block, advanced per tile.
+    uint32_t tpos = (uint32_t)(p.head + (int64_t)blk * (4 * kBlock * U));
+    const uint32_t tstep = (uint32_t)p.grid * (uint32_t)(4 * kBlock * U);
 #pragma unroll
     for (int j = 0; j < kRing; ++j)
       if (j < count) issue_tile_lds<U>(first + j * stride, voff, ring[j]);
@@ -579,14 +625,22 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       if (i + kRing < count)
         issue_tile_lds<U>(first + (i + kRing) * stride, voff, ring[slot]);
       kv_values<F32, U>(d);
-      // Position of this lane's first element of the tile.
-      const uint32_t pos0 = (uint32_t)(
-          p.head + 4 * ((blk + i * p.grid) * (int64_t)(kBlock * U) +
-                        (int64_t)threadIdx.x));
+      // Position of this lane's first element of the tile (n < 2^32).
+      const uint32_t pos0 = tpos + 4u * threadIdx.x;
+      tpos += tstep;
       if (i == 0)
         kv_init_list<KCAP, U>(L, d, pos0, thr);
       else
-        kv_consume<KCAP, FIT, U>(L, d, pos0, k, (int64_t)tsh - 1, thr);
+        kv_consume<KCAP, FIT, U>(L, d, pos0, k, kv_tsk(tsh), thr);
+      // After each of the first two tiles every lane publishes its head and
+      // the workgroup waits, so that bound refresh sees all 256 fresh
+      // heads: the early bounds are much tighter and far fewer elements are
+      // admitted in the tiles that follow.
+      if (i <= 1) {
+        __hip_atomic_store(&sh.heads[threadIdx.x], bias(L.v[0]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        lds_barrier();
+      }
       if (refresh_due(i, R)) kv_refresh_bound(L, k, tsh, thr, sh);
     }
   }
@@ -602,9 +656,11 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       const int s = ok ? kv_value<F32>(p.in[pos]) : kI32Min;
       const bool q = ok && s >= tsh;
       // Inserting the empty key 0 leaves a list unchanged.
-      if (ballot(q))
-        kv_list_insert<KCAP, FIT, false>(L, q ? kv_key(s, (uint32_t)pos) : 0ull,
-                                         k);
+      if (ballot(q)) {
+        int xv = q ? s : kI32Min;
+        uint32_t xw = q ? ~(uint32_t)pos : 0u;
+        kv_list_insert<KCAP, FIT, false>(L, xv, xw, k);
+      }
     }
   }
 
@@ -614,8 +670,8 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   // the final snapshot: the k-th largest head value by radix select over
   // ballots, then, among the heads of that value, the right one by their
   // low words (a second search only when several heads share the value).
-  sh.heads[threadIdx.x] = (unsigned)(L[0] >> 32);
-  sh.hkeys[threadIdx.x] = L[0];
+  sh.heads[threadIdx.x] = bias(L.v[0]);
+  sh.hkeys[threadIdx.x] = L.key(0);
   __syncthreads();
   uint64_t T;
   {
@@ -663,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
 #pragma unroll
     for (int i = 0; i < KCAP; ++i) {
       if (more) {
-        const bool q = i < k && L[i] >= T && L[i] != 0ull;
+        const bool q = i < k && L.key(i) >= T && L.key(i) != 0ull;
         const uint64_t b = ballot(q);
         more = b != 0;
         if (more) {
@@ -671,7 +727,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
           if (lane() == 0) base = atomicAdd(&sh.bcnt, popc(b));
           base = uni(base);
           const int pos = base + lanes_below(b);
-          if (q && pos < kBlock) sh.blist[pos] = L[i];
+          if (q && pos < kBlock) sh.blist[pos] = L.key(i);
           more = base + popc(b) < kBlock;
         }
       }
@@ -685,14 +741,14 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     const uint64_t g = kv_select(k, sh, [&](auto&& f) {
 #pragma unroll
       for (int i = 0; i < KCAP; ++i)
-        if (i < k && L[i] >= T && L[i] != 0ull) f(L[i]);
+        if (i < k && L.key(i) >= T && L.key(i) != 0ull) f(L.key(i));
     });
     if (threadIdx.x == 0) sh.bcnt = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KCAP; ++i) {
-      const bool q = i < k && L[i] >= g && L[i] != 0ull;
-      kv_wave_append(q, L[i], &sh.bcnt, sh.blist, kBlock);
+      const bool q = i < k && L.key(i) >= g && L.key(i) != 0ull;
+      kv_wave_append(q, L.key(i), &sh.bcnt, sh.blist, kBlock);
     }
     __syncthreads();
     lb = sh.bcnt;  // == k

@@ -250,6 +250,12 @@ __device__ __forceinline__ void wait_lds_reads() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Workgroup barrier that waits for this wave's LDS traffic only: the tile
+// loads in flight stay in flight (a __syncthreads() would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Bitwise radix selection.  Given a wave-uniform range [lo, hi] (biased
 // values) that is known to contain the answer, return the largest t in it
 // with count_ge(t) >= k, where count_ge is a wave-uniform count of the
