@@ -1,6 +1,6 @@
 """Benchmark: Top-20 over 1e8 int32 on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path topk|stats]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path topk|stats|kv]
 
 One step is one full library call (both stages; a single kernel launch)
 over a resident synthetic input (seeded SplitMix64).  The default path,
@@ -8,7 +8,9 @@ over a resident synthetic input (seeded SplitMix64).  The default path,
 the full range (seed 3).  `--path stats` measures reduce_stats_i32 (count,
 sum, max, min and sum of squares in one pass) over 2^26 int32 uniform in
 [-1000, 1000] (seed 2), the array whose sum, max and min are otherwise
-asked for in three separate calls.
+asked for in three separate calls.  `--path kv` measures topk_kv_i32, the
+key-value variant (the 20 largest values with their int64 positions, ties
+by position), on the same 1e8 array as `topk`.
 
 The input sits in HBM before timing starts.  W untimed calls, then K timed
 back-to-back calls bracketed by device synchronisation and by a pair of HIP
@@ -74,6 +76,22 @@ PATHS = {
         "summary": "stats_pm1000_2p26.md",
         "out_bytes": 48,
         "oracle_what": "the five statistics by one loop (128-bit squares)",
+    },
+    "kv": {
+        "metric": ("Key-value Top-20 (values + int64 positions) over 1e8 "
+                   "int32: elements/s, HBM GB/s as % of 8 TB/s peak"),
+        "workload": "full_1e8",
+        "describe": ("top-20 of 1e8 int32 with their positions (ties by "
+                     "position), uniform over the full int32 range "
+                     "(SplitMix64 seed 3), resident in HBM"),
+        "short": "key-value top-20 of 1e8 int32, uniform full range, seed 3",
+        "kernel": "topk_kv_kernel",
+        "sources": ["wave.hpp", "topk_kernel.hpp", "topk_kv_kernel.hpp",
+                    "libtopk.hip"],
+        "counters": "topk_kv_counters_full_1e8_k20.json",
+        "summary": "topk_kv_full_1e8_k20.md",
+        "out_bytes": 12 * K,
+        "oracle_what": "top-20 keys by a stable sort of positions",
     },
 }
 
@@ -299,6 +317,12 @@ def main():
 
         def call():
             return ltk.topk(xd, K, out=out)
+    elif args.path == "kv":
+        outs = (torch.empty(K, dtype=torch.int32, device=dev),
+                torch.empty(K, dtype=torch.int64, device=dev))
+
+        def call():
+            return ltk.topk_kv(xd, K, out=outs)
     else:
         out = torch.empty(6, dtype=torch.int64, device=dev)
 
@@ -324,6 +348,14 @@ def main():
         got = call().cpu().numpy()
         want = oracle.topk(x, K)
         ok = np.array_equal(got, want)
+    elif args.path == "kv":
+        gv, gi = call()
+        got = (gv.cpu().numpy(), gi.cpu().numpy())
+        t_kv = time.perf_counter()
+        want = oracle.topk_kv(x, K)
+        t_kv = time.perf_counter() - t_kv   # the baseline: one oracle call
+        ok = (np.array_equal(got[0], want[0])
+              and np.array_equal(got[1], want[1]))
     else:
         got = ltk.unpack_stats(call())
         want = oracle.stats(x)
@@ -371,6 +403,9 @@ def main():
         if args.path == "topk":
             t_med, reps = time_oracle(lambda: oracle.topk(x, K))
             what = "the full workload (1e8 int32, seed 3)"
+        elif args.path == "kv":
+            t_med, reps = t_kv, 1
+            what = "the full workload (1e8 int32, seed 3)"
         else:
             # one pass takes ~0.05 s: repeat it for about 10 s of CPU work
             t_med, reps = time_oracle(lambda: oracle.stats(x), budget_s=10.0,
@@ -388,7 +423,7 @@ def main():
         }
 
     config = {"workload": P["describe"], "n": n}
-    if args.path == "topk":
+    if args.path in ("topk", "kv"):
         config["k"] = K
     config.update({
         "grid": ltk.grid_for(n),
