@@ -62,6 +62,13 @@ class Oracle:
         lib.oracle_check_topk.restype = ctypes.c_int
         lib.oracle_stats_i32.argtypes = [p, ctypes.c_int64, p]
         lib.oracle_stats_i32.restype = ctypes.c_int
+        lib.oracle_topk_batched_i32.argtypes = [p, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int32, p]
+        lib.oracle_topk_batched_i32.restype = ctypes.c_int
+        lib.oracle_topk_merge_i32.argtypes = [p, ctypes.c_int64,
+                                              ctypes.c_int32, ctypes.c_int32, p]
+        lib.oracle_topk_merge_i32.restype = ctypes.c_int
         for name in ("oracle_topk_kv_i32", "oracle_topk_kv_f32"):
             fn = getattr(lib, name)
             fn.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, p]
@@ -119,6 +126,42 @@ class Oracle:
                              % (a.size, k))
         return vals, idx
 
+    def topk_batched(self, x, k: int, cols: int | None = None) -> np.ndarray:
+        """Top-k of every row of the 2-D int32 array x, shape (rows, k).
+        With cols given, only the first cols columns of each row count
+        (the rest is the row stride's padding)."""
+        a = np.ascontiguousarray(x, dtype=np.int32)
+        if a.ndim != 2:
+            raise ValueError("expected a 2-D array")
+        rows, ld = a.shape
+        c = ld if cols is None else cols
+        out = np.empty((rows, max(k, 0)), dtype=np.int32)
+        rc = self.lib.oracle_topk_batched_i32(a.ctypes.data, rows, c, ld, k,
+                                              out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_topk_batched_i32: invalid arguments "
+                             "(rows=%d, cols=%d, ld=%d, k=%d)"
+                             % (rows, c, ld, k))
+        return out
+
+    def topk_merge(self, lists, k: int) -> np.ndarray:
+        """The k largest values of the union of the rows of `lists` (a 2-D
+        int32 array whose rows are each in descending order)."""
+        a = np.ascontiguousarray(lists, dtype=np.int32)
+        if a.ndim != 2:
+            raise ValueError("expected a 2-D array")
+        m, ln = a.shape
+        out = np.empty(max(k, 0), dtype=np.int32)
+        rc = self.lib.oracle_topk_merge_i32(a.ctypes.data, m, ln, k,
+                                            out.ctypes.data)
+        if rc == -2:
+            raise ValueError("oracle_topk_merge_i32: a list is not in "
+                             "descending order")
+        if rc != 0:
+            raise ValueError("oracle_topk_merge_i32: invalid arguments "
+                             "(m=%d, len=%d, k=%d)" % (m, ln, k))
+        return out
+
     def check_topk(self, x, k: int, cand) -> int:
         """0 if cand is exactly the descending top-k of x, else 1/2/3."""
         a = _as_i32(x)
@@ -165,3 +208,11 @@ def stats(x) -> dict:
 
 def topk_kv(x, k: int):
     return default().topk_kv(x, k)
+
+
+def topk_batched(x, k: int, cols: int | None = None) -> np.ndarray:
+    return default().topk_batched(x, k, cols)
+
+
+def topk_merge(lists, k: int) -> np.ndarray:
+    return default().topk_merge(lists, k)

@@ -64,6 +64,28 @@
  *                     numbers and puts -0 below +0, positive NaNs above
  *                     +infinity and negative NaNs below -infinity.
  *
+ *   oracle_topk_batched_i32
+ *                     the top-k of every row of a row-major matrix: rows
+ *                     r = 0..rows-1 of `cols` values each, row r starting
+ *                     at in[r * ld] ([TopK] §6: the two-stage pattern is a
+ *                     building block, for instance candidate selection per
+ *                     user in a recommender).  Definition: for each row,
+ *                     the row's top-k exactly as oracle_topk_i32 defines
+ *                     it, written to out[r * k .. r * k + k).  Elements
+ *                     between cols and ld of a row are not part of it.
+ *
+ *   oracle_topk_merge_i32
+ *                     merging several top-k results into one ([TopK] §6:
+ *                     several TopK results merged again; §2.2: stage 2
+ *                     merges the per-block top-k lists into the final
+ *                     one).  Input: m lists of `len` values each, row-major
+ *                     and contiguous, each in descending order (as the
+ *                     top-k calls write them).  Result: the k largest
+ *                     values of the union of the lists, descending --
+ *                     by definition, sort all m * len values and read the
+ *                     last k backwards.  A list that is not in descending
+ *                     order is a caller error, reported as such.
+ *
  *   oracle_check_topk a second, sort-free characterisation of the top-k
  *                     multiset, linear in n.  It is used to check results
  *                     at sizes where sorting is too slow, and as an
@@ -255,6 +277,46 @@ int oracle_check_topk(const int32_t *in, int64_t n, int32_t k,
             ++above_cand;
     if (above_in != above_cand)
         return 3;
+    return 0;
+}
+
+/* out[r * k + i], i < k: the i-th largest value of row r, which is
+ * in[r * ld .. r * ld + cols).  Returns 0, or -1 on invalid arguments
+ * (null pointers, rows < 0, cols < 1, ld < cols, k < 1, k > cols). */
+int oracle_topk_batched_i32(const int32_t *in, int64_t rows, int64_t cols,
+                            int64_t ld, int32_t k, int32_t *out)
+{
+    if (!in || !out || rows < 0 || cols < 1 || ld < cols || k < 1 ||
+        (int64_t)k > cols)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int32_t *row = in + r * ld;
+        std::vector<int32_t> v(row, row + cols);
+        std::sort(v.begin(), v.end());
+        for (int32_t i = 0; i < k; ++i)
+            out[r * k + i] = v[(size_t)(cols - 1 - i)];
+    }
+    return 0;
+}
+
+/* out[0..k): the k largest of the m * len values of lists[], descending.
+ * Returns 0; -1 on invalid arguments (null pointers, m < 1, len < 1,
+ * k < 1, k > m * len); -2 if some list is not in descending order. */
+int oracle_topk_merge_i32(const int32_t *lists, int64_t m, int32_t len,
+                          int32_t k, int32_t *out)
+{
+    if (!lists || !out || m < 1 || len < 1 || k < 1 ||
+        (int64_t)k > m * (int64_t)len)
+        return -1;
+    for (int64_t j = 0; j < m; ++j)
+        for (int32_t i = 1; i < len; ++i)
+            if (lists[j * len + i] > lists[j * len + i - 1])
+                return -2;
+    const int64_t total = m * (int64_t)len;
+    std::vector<int32_t> v(lists, lists + total);
+    std::sort(v.begin(), v.end());
+    for (int32_t i = 0; i < k; ++i)
+        out[i] = v[(size_t)(total - 1 - i)];
     return 0;
 }
 

@@ -281,9 +281,80 @@ def pin_topk_kv(o, rng):
     assert list(i) == [3, 2, 0, 4, 1]
 
 
+def np_topk_rows(x, k):
+    """numpy's own sort along rows, read backwards: a library routine that
+    shares nothing with the oracle's std::sort."""
+    return np.sort(np.asarray(x, dtype=np.int64), axis=1)[:, ::-1][:, :k]
+
+
+def pin_topk_batched(o, rng):
+    """Per-row top-k: a hand example, numpy's sort along rows, exhaustive
+    brute force on tiny matrices, and the row stride: columns past `cols`
+    (filled with INT32_MAX here) must never reach the result."""
+    x = np.array([[3, 1, 2], [9, 9, 0]], np.int32)
+    assert o.topk_batched(x, 2).tolist() == [[3, 2], [9, 9]]
+    assert o.topk_batched(x, 3).tolist() == [[3, 2, 1], [9, 9, 0]]
+    assert o.topk_batched(x, 1, cols=2).tolist() == [[3], [9]]
+    assert o.topk_batched(np.zeros((0, 4), np.int32), 2).shape == (0, 2)
+    alphabet = [I32_MIN, -1, 0, I32_MAX]
+    for cols in (1, 2, 3):
+        for flat in itertools.product(alphabet, repeat=2 * cols):
+            a = np.array(flat, np.int32).reshape(2, cols)
+            for k in range(1, cols + 1):
+                got = o.topk_batched(a, k).tolist()
+                assert got == [brute_topk(a[0], k), brute_topk(a[1], k)]
+    for trial in range(40):
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 300))
+        pad = int(rng.integers(0, 5))
+        hi = int(rng.choice([3, 1000, 2 ** 31]))
+        a = rng.integers(-hi, hi, size=(rows, cols), dtype=np.int64)
+        a = a.astype(np.int32)
+        k = int(rng.integers(1, cols + 1))
+        want = np_topk_rows(a, k)
+        assert (o.topk_batched(a, k) == want).all()
+        wide = np.full((rows, cols + pad), I32_MAX, np.int32)
+        wide[:, :cols] = a
+        assert (o.topk_batched(wide, k, cols=cols) == want).all()
+
+
+def pin_topk_merge(o, rng):
+    """Merging top-k lists: hand examples, and the two-stage lemma itself
+    (the top-k of the union of every shard's top-k is the top-k of the
+    whole), with numpy's sort on both sides; a list out of order is
+    refused."""
+    lists = np.array([[9, 5, 1], [7, 6, 2]], np.int32)
+    assert o.topk_merge(lists, 3).tolist() == [9, 7, 6]
+    assert o.topk_merge(lists, 6).tolist() == [9, 7, 6, 5, 2, 1]
+    assert o.topk_merge(np.array([[5, 5], [5, 4]], np.int32), 3).tolist() \
+        == [5, 5, 5]
+    assert o.topk_merge(np.array([[4], [8], [-3]], np.int32), 3).tolist() \
+        == [8, 4, -3]
+    refused = False
+    try:
+        o.topk_merge(np.array([[3, 1], [1, 2]], np.int32), 1)
+    except ValueError:
+        refused = True
+    assert refused, "a list out of order must be refused"
+    for trial in range(40):
+        m = int(rng.integers(1, 30))
+        size = int(rng.integers(1, 200))
+        k = int(rng.integers(1, min(size, 128) + 1))
+        hi = int(rng.choice([3, 1000, 2 ** 31]))
+        shards = rng.integers(-hi, hi, size=(m, size), dtype=np.int64)
+        shards = shards.astype(np.int32)
+        tops = np_topk_rows(shards, k).astype(np.int32)
+        want = np.sort(shards.ravel().astype(np.int64))[::-1][:k]
+        assert o.topk_merge(tops, k).tolist() == want.tolist()
+        kk = int(rng.integers(1, m * k + 1))
+        whole = np.sort(tops.ravel().astype(np.int64))[::-1][:kk]
+        assert o.topk_merge(tops, kk).tolist() == whole.tolist()
+
+
 BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
            pin_empty_identities, pin_int64_sum, pin_closed_forms,
-           pin_invariants, pin_checker_rejects, pin_stats, pin_topk_kv]
+           pin_invariants, pin_checker_rejects, pin_stats, pin_topk_kv,
+           pin_topk_batched, pin_topk_merge]
 
 
 def run_battery(o, seed=7):
@@ -355,6 +426,21 @@ MUTANTS = {
                           "key[(size_t)i] = b;"),
     "kv_float_sign_only": (r"key\[\(size_t\)i\] = \(b & 0x80000000u\) \? ~b : \(b \| 0x80000000u\);",
                            "key[(size_t)i] = b ^ 0x80000000u;"),
+    "batched_ignores_row_stride": (r"const int32_t \*row = in \+ r \* ld;",
+                                   "const int32_t *row = in + r * cols;"),
+    "batched_reads_past_cols": (
+        r"std::vector<int32_t> v\(row, row \+ cols\);",
+        "std::vector<int32_t> v(row, row + cols + (cols < ld ? 1 : 0));"),
+    "batched_rows_shifted": (r"out\[r \* k \+ i\] = v",
+                             "out[(r + 1 < rows ? r + 1 : r) * k + i] = v"),
+    "merge_drops_last_list": (
+        r"std::vector<int32_t> v\(lists, lists \+ total\);",
+        "std::vector<int32_t> v(lists, lists + total); if (m > 1) for "
+        "(int32_t i = 0; i < len; ++i) v[(size_t)(total - len + i)] = "
+        "INT32_MIN;"),
+    "merge_accepts_unsorted": (r"return -2;", "(void)0;"),
+    "merge_ascending": (r"out\[i\] = v\[\(size_t\)\(total - 1 - i\)\];",
+                        "out[i] = v[(size_t)(total - k + i)];"),
 }
 
 
