@@ -165,6 +165,64 @@ int topk_kv_f32(const float *in, int64_t n, int32_t k, float *out_values,
 int reduce_stats_i32(const int32_t *in, int64_t n, int64_t *out,
                      libtopk_stream_t stream);
 
+/*
+ * topk_batched_i32 — the top-k of every row of a row-major int32 matrix:
+ * out[r * k + i], i < k, is the i-th largest value of row r, which is
+ * in[r * ld .. r * ld + cols); each row's k values in descending order,
+ * duplicates kept.
+ *
+ * Operation: [TopK] §6 (the two-stage pattern as a building block, e.g.
+ * candidate selection per user in a recommender) with [TopK] §2's two
+ * stages per row.  Long rows get several workgroups each and the last of a
+ * row's workgroups merges its candidates; rows of up to 4096 elements are
+ * handled one wave per row.
+ *
+ *   in    device, int32, rows of `cols` elements `ld` elements apart;
+ *         elements between cols and ld of a row are never read
+ *   rows  0 <= rows (0: nothing is enqueued and LIBTOPK_OK is returned
+ *         once cols, ld and k are valid; in and out may then be NULL)
+ *   cols  1 <= cols <= 2^32
+ *   ld    row stride in elements, ld >= cols (any value: rows need not be
+ *         16-byte aligned)
+ *   k     1 <= k <= min(cols, LIBTOPK_MAX_K)
+ *   out   device, int32[rows * k], written in full
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, rows < 0,
+ * cols or ld out of range, k < 1 or k > cols, an input span beyond 2^60
+ * elements, or overlapping input and output; LIBTOPK_ERR_UNSUPPORTED for
+ * k > LIBTOPK_MAX_K.
+ */
+int topk_batched_i32(const int32_t *in, int64_t rows, int64_t cols,
+                     int64_t ld, int32_t k, int32_t *out,
+                     libtopk_stream_t stream);
+
+/*
+ * topk_merge_i32 — merge several top-k results: the k largest values of the
+ * union of m lists, written to out[0..k) in descending order.
+ *
+ * Operation: [TopK] §6 (several TopK results merged again) and §2.2 (the
+ * second stage merges per-block top-k lists into the final one).  Only the
+ * first min(len, k) entries of a list are read, plus what the merge needs
+ * to bound the result.  Typical inputs: the outputs of topk_i32 on shards
+ * of one array (the merge of the shards' top-k lists is the top-k of the
+ * whole), or the rows written by topk_batched_i32.
+ *
+ *   lists  device, int32[m * len], list j at lists + j * len; every list
+ *          MUST be in descending order (as the top-k calls write them).
+ *          The library does not check this; on a list out of order the
+ *          result is unspecified (nothing is read outside lists[]).
+ *   m      1 <= m <= 2^20 lists
+ *   len    entries per list, len >= 1
+ *   k      1 <= k <= min(m * len, LIBTOPK_MAX_K)
+ *   out    device, int32[k], written in full
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, m or len
+ * out of range, k < 1 or k > m * len, or overlapping lists and out;
+ * LIBTOPK_ERR_UNSUPPORTED for k > LIBTOPK_MAX_K.
+ */
+int topk_merge_i32(const int32_t *lists, int64_t m, int32_t len, int32_t k,
+                   int32_t *out, libtopk_stream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *libtopk_strerror(int status);
 

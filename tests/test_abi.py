@@ -32,7 +32,8 @@ def no_gpu():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"topk_i32", "reduce_i32", "reduce_stats_i32", "topk_kv_i32",
-            "topk_kv_f32", "libtopk_strerror",
+            "topk_kv_f32", "topk_batched_i32", "topk_merge_i32",
+            "libtopk_strerror",
             "libtopk_max_k", "libtopk_set_grid", "libtopk_grid_for",
             "libtopk_release"} <= set(names)
 
@@ -131,6 +132,53 @@ def test_topk_kv_rejects_invalid_arguments(args, status, f32):
     assert ltk.topk_kv_raw(*args, f32=f32) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    # (in, rows, cols, ld, k, out)
+    ((0, 4, 100, 100, 5, FAKE * 64), ltk.ERR_INVALID),           # NULL input
+    ((FAKE, 4, 100, 100, 5, 0), ltk.ERR_INVALID),                # NULL output
+    ((FAKE + 2, 4, 100, 100, 5, FAKE * 64), ltk.ERR_INVALID),    # misaligned in
+    ((FAKE, 4, 100, 100, 5, FAKE * 64 + 2), ltk.ERR_INVALID),    # misaligned out
+    ((FAKE, -1, 100, 100, 5, FAKE * 64), ltk.ERR_INVALID),       # rows < 0
+    ((FAKE, 4, 0, 100, 1, FAKE * 64), ltk.ERR_INVALID),          # cols = 0
+    ((FAKE, 4, (1 << 32) + 1, 1 << 33, 5, 1 << 46), ltk.ERR_INVALID),  # cols
+    ((FAKE, 4, 100, 99, 5, FAKE * 64), ltk.ERR_INVALID),         # ld < cols
+    ((FAKE, 4, 100, 100, 0, FAKE * 64), ltk.ERR_INVALID),        # k = 0
+    ((FAKE, 4, 10, 10, 11, FAKE * 64), ltk.ERR_INVALID),         # k > cols
+    ((FAKE, 4, 1000, 1000, 129, FAKE * 64), ltk.ERR_UNSUPPORTED),
+    ((FAKE, 1 << 40, 1 << 30, 1 << 30, 5, FAKE * 64), ltk.ERR_INVALID),  # span
+    ((FAKE, 4, 100, 100, 5, FAKE + 800), ltk.ERR_INVALID),       # out inside in
+    ((FAKE, 4, 100, 1000, 5, FAKE + 4 * 3000), ltk.ERR_INVALID), # out in a gap
+    ((FAKE, 4, 100, 100, 20, FAKE - 40), ltk.ERR_INVALID),       # out overlaps
+])
+def test_topk_batched_rejects_invalid_arguments(args, status):
+    assert ltk.topk_batched_raw(*args) == status
+
+
+def test_topk_batched_zero_rows_is_a_no_op():
+    # Validated, nothing enqueued: no device is needed.
+    assert ltk.topk_batched_raw(FAKE, 0, 100, 100, 5, FAKE * 64) == ltk.OK
+    assert ltk.topk_batched_raw(0, 0, 100, 100, 5, 0) == ltk.OK
+    assert ltk.topk_batched_raw(0, 0, 100, 100, 101, 0) == ltk.ERR_INVALID
+
+
+@pytest.mark.parametrize("args,status", [
+    # (lists, m, len, k, out)
+    ((0, 8, 20, 20, FAKE * 64), ltk.ERR_INVALID),                # NULL lists
+    ((FAKE, 8, 20, 20, 0), ltk.ERR_INVALID),                     # NULL output
+    ((FAKE + 1, 8, 20, 20, FAKE * 64), ltk.ERR_INVALID),         # misaligned
+    ((FAKE, 8, 20, 20, FAKE * 64 + 3), ltk.ERR_INVALID),         # misaligned
+    ((FAKE, 0, 20, 1, FAKE * 64), ltk.ERR_INVALID),              # m = 0
+    ((FAKE, (1 << 20) + 1, 1, 1, FAKE * 64), ltk.ERR_INVALID),   # m > 2^20
+    ((FAKE, 8, 0, 1, FAKE * 64), ltk.ERR_INVALID),               # len = 0
+    ((FAKE, 8, 20, 0, FAKE * 64), ltk.ERR_INVALID),              # k = 0
+    ((FAKE, 2, 3, 7, FAKE * 64), ltk.ERR_INVALID),               # k > m * len
+    ((FAKE, 8, 200, 129, FAKE * 64), ltk.ERR_UNSUPPORTED),
+    ((FAKE, 8, 20, 20, FAKE + 100), ltk.ERR_INVALID),            # out inside
+])
+def test_topk_merge_rejects_invalid_arguments(args, status):
+    assert ltk.topk_merge_raw(*args) == status
+
+
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
@@ -141,6 +189,9 @@ def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_kv_raw(FAKE, 1000, 20, FAKE * 4, FAKE * 8) == ltk.ERR_HIP
     assert ltk.topk_kv_raw(FAKE, 1000, 20, FAKE * 4, FAKE * 8,
                            f32=True) == ltk.ERR_HIP
+    assert ltk.topk_batched_raw(FAKE, 4, 100, 100, 5, FAKE * 64) == \
+        ltk.ERR_HIP
+    assert ltk.topk_merge_raw(FAKE, 8, 20, 20, FAKE * 64) == ltk.ERR_HIP
 
 
 def test_grid_setting():

@@ -13,6 +13,13 @@ if the library is not built, importing this package raises.
                        squares (low, high 64 bits) of x, from one read
     unpack_stats(t) -> the same as a dict of Python ints (sum of squares
                        joined into one integer)
+    topk_batched(x, k, cols=None)
+                    -> int32 tensor [rows, k]: the top-k of every row of the
+                       2-D int32 x (rows may be strided; with cols, only the
+                       first cols columns of each row count)
+    topk_merge(lists, k)
+                    -> int32 tensor [k]: the k largest of the union of the
+                       rows of lists (each row in descending order)
 """
 from __future__ import annotations
 
@@ -38,6 +45,11 @@ SIGNATURES = {
                     ctypes.c_int),
     "topk_kv_f32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP, _VP],
                     ctypes.c_int),
+    "topk_batched_i32": ([_VP, ctypes.c_int64, ctypes.c_int64,
+                          ctypes.c_int64, ctypes.c_int32, _VP, _VP],
+                         ctypes.c_int),
+    "topk_merge_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                        _VP, _VP], ctypes.c_int),
     "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "libtopk_max_k": ([], ctypes.c_int),
     "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
@@ -123,6 +135,20 @@ def topk_kv_raw(in_ptr: int, n: int, k: int, vals_ptr: int, idx_ptr: int,
     fn = lib.topk_kv_f32 if f32 else lib.topk_kv_i32
     return fn(in_ptr or None, n, k, vals_ptr or None, idx_ptr or None,
               stream or None)
+
+
+def topk_batched_raw(in_ptr: int, rows: int, cols: int, ld: int, k: int,
+                     out_ptr: int, stream: int = 0) -> int:
+    """Call topk_batched_i32 on raw device pointers; returns the status."""
+    return lib.topk_batched_i32(in_ptr or None, rows, cols, ld, k,
+                                out_ptr or None, stream or None)
+
+
+def topk_merge_raw(lists_ptr: int, m: int, length: int, k: int, out_ptr: int,
+                   stream: int = 0) -> int:
+    """Call topk_merge_i32 on raw device pointers; returns the status."""
+    return lib.topk_merge_i32(lists_ptr or None, m, length, k,
+                              out_ptr or None, stream or None)
 
 
 # ---------------------------------------------------------------- tensors
@@ -232,3 +258,72 @@ def topk_kv(x, k: int, out=None):
     if rc != OK:
         raise LibtopkError(rc, fn.__name__)
     return vals, idx
+
+
+def _check_rows(x):
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if x.dtype != torch.int32:
+        raise TypeError("expected int32, got %s" % x.dtype)
+    if x.device.type != "cuda":
+        raise ValueError("expected a device tensor, got %s" % x.device)
+    if x.dim() != 2 or x.stride(1) != 1 or (x.size(0) > 1
+                                            and x.stride(0) < x.size(1)):
+        raise ValueError("expected a 2-D tensor with unit column stride and "
+                         "row stride >= its row length")
+
+
+def topk_batched(x, k: int, cols: int | None = None, out=None):
+    """Top-k of every row of the 2-D int32 device tensor x (row stride
+    x.stride(0), unit column stride): an int32 tensor [rows, k], each row
+    descending.  With cols, only the first cols columns of each row count."""
+    import torch
+    _check_rows(x)
+    rows, width = x.shape
+    c = width if cols is None else int(cols)
+    if c > width:
+        raise ValueError("cols exceeds the tensor's row length")
+    ld = x.stride(0) if rows > 1 else max(width, 1)
+    if out is None:
+        out = torch.empty((rows, max(int(k), 0)), dtype=torch.int32,
+                          device=x.device)
+    elif (out.dtype != torch.int32 or out.device != x.device
+          or out.numel() != rows * k or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [rows, k] tensor on "
+                         "x's device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.topk_batched_i32(x.data_ptr() if x.numel() else None, rows,
+                                  c, ld, k,
+                                  out.data_ptr() if out.numel() else None,
+                                  stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "topk_batched_i32")
+    return out
+
+
+def topk_merge(lists, k: int, out=None):
+    """The k largest values of the union of the rows of the 2-D int32 device
+    tensor `lists` (contiguous; each row in descending order), descending."""
+    import torch
+    _check_rows(lists)
+    if not lists.is_contiguous():
+        raise ValueError("expected a contiguous 2-D tensor")
+    m, length = lists.shape
+    if out is None:
+        out = torch.empty(max(int(k), 0), dtype=torch.int32,
+                          device=lists.device)
+    elif (out.dtype != torch.int32 or out.device != lists.device
+          or out.numel() != k or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [k] tensor on the "
+                         "lists' device")
+    with torch.cuda.device(lists.device):
+        stream = torch.cuda.current_stream(lists.device).cuda_stream
+        rc = lib.topk_merge_i32(lists.data_ptr() if lists.numel() else None,
+                                m, length, k,
+                                out.data_ptr() if out.numel() else None,
+                                stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "topk_merge_i32")
+    return out

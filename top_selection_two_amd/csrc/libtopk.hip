@@ -24,6 +24,7 @@
 #include "stats_kernel.hpp"
 #include "topk_kernel.hpp"
 #include "topk_kv_kernel.hpp"
+#include "topk_rows_kernel.hpp"
 
 namespace {
 
@@ -43,7 +44,7 @@ struct Scratch {
   uint64_t* kvcand = nullptr;  // kMaxGrid * kMaxK (key-value candidates)
   uint64_t* kvheads = nullptr; // kMaxGrid
   uint64_t* kvkths = nullptr;  // kMaxGrid
-  unsigned* ticket = nullptr;  // 1 word, kept at 0 between calls
+  unsigned* ticket = nullptr;  // kMaxGrid words (one per row), 0 between calls
 };
 
 constexpr size_t kCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(int);
@@ -52,9 +53,10 @@ constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
 constexpr size_t kStatBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
 constexpr size_t kKvCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(uint64_t);
 constexpr size_t kKvHeadBytes = (size_t)kMaxGrid * sizeof(uint64_t);
+constexpr size_t kTicketBytes = (size_t)kMaxGrid * sizeof(unsigned);
 constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes +
                                  kStatBytes + kKvCandBytes +
-                                 2 * kKvHeadBytes + 256;
+                                 2 * kKvHeadBytes + kTicketBytes;
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Scratch> g_cache;
@@ -129,7 +131,8 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   s.ticket = (unsigned*)b;
   // A kernel (not a memset) clears the counter, ordered on the caller's
   // stream before the first real launch.
-  hipLaunchKernelGGL(zero_words, dim3(1), dim3(64), 0, stream, s.ticket, 64);
+  hipLaunchKernelGGL(zero_words, dim3(kMaxGrid / 256), dim3(256), 0, stream,
+                     s.ticket, kMaxGrid);
   e = hipGetLastError();
   if (e != hipSuccess) {
     debug_hip("zero_words launch", e);
@@ -256,6 +259,38 @@ const void* reduce_fn(int op) {
   return (const void*)&reduce_kernel<kOpMin, kTileVec>;
 }
 
+// Rows of at most this many elements go one wave per row, the whole row in
+// registers (topk_rows_kernel); longer rows stream through topk_kernel.
+constexpr int64_t kShortRow = 4096;
+// Workgroups per launch of topk_kernel on many rows (later rows go in
+// further launches).
+constexpr int64_t kMaxLaunchBlocks = (int64_t)1 << 20;
+
+// Elements per lane: the row length rounded up to a multiple of 64 from
+// {256, 512, 1024, 2048, 4096}.
+const void* rows_fn(int64_t n) {
+  if (n <= 256) return (const void*)&topk_rows_kernel<4>;
+  if (n <= 512) return (const void*)&topk_rows_kernel<8>;
+  if (n <= 1024) return (const void*)&topk_rows_kernel<16>;
+  if (n <= 2048) return (const void*)&topk_rows_kernel<32>;
+  return (const void*)&topk_rows_kernel<64>;
+}
+
+// Workgroups per row for rows longer than kShortRow: enough workgroups in
+// all to give every CU two, but never more than a row has tiles, and few
+// enough rows x workgroups for the per-block scratch.  Many rows: one
+// workgroup per row, whose own top-k is the row's result.
+int row_grid(int64_t rows, int64_t cols, int cus) {
+  int target = g_grid_override.load();
+  if (target <= 0) target = 2 * cus;
+  const int64_t tiles = (cols / 4) / (kBlock * kTileVec);
+  if (rows >= target || rows > kMaxGrid || tiles < 2) return 1;
+  int64_t g = (target + rows - 1) / rows;
+  if (g > tiles) g = tiles;
+  if (g > kMaxGrid / rows) g = kMaxGrid / rows;
+  return g < 1 ? 1 : (int)g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -285,9 +320,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   TopkParams p;
   p.in = in;
   p.n = n;
-  p.head = pl.head;
-  p.ntiles = pl.ntiles;
-  p.covered = pl.covered;
+  p.ld = n;  // one row
   p.k = k;
   p.grid = pl.grid;
   p.refresh = kRefreshPeriod;
@@ -380,6 +413,100 @@ int reduce_stats_i32(const int32_t* in, int64_t n, int64_t* out,
   p.ticket = sc.ticket;
   p.out = out;
   return launch((const void*)&stats_kernel<kTileVec>, pl.grid, p, s);
+}
+
+int topk_batched_i32(const int32_t* in, int64_t rows, int64_t cols,
+                     int64_t ld, int32_t k, int32_t* out,
+                     libtopk_stream_t stream) {
+  if (rows < 0 || cols < 1 || cols > kMaxN || ld < cols)
+    return LIBTOPK_ERR_INVALID;
+  if (k < 1 || (int64_t)k > cols) return LIBTOPK_ERR_INVALID;
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (rows == 0) return LIBTOPK_OK;
+  if (!in || !out) return LIBTOPK_ERR_INVALID;
+  if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return LIBTOPK_ERR_INVALID;
+  // The input spans (rows - 1) * ld + cols elements: keep byte sizes far
+  // from overflow.
+  const int64_t kSpanMax = (int64_t)1 << 60;
+  if (rows - 1 > (kSpanMax - cols) / ld || rows > kSpanMax / k)
+    return LIBTOPK_ERR_INVALID;
+  const size_t in_bytes = (size_t)((rows - 1) * ld + cols) * 4;
+  if (overlaps(in, in_bytes, out, (size_t)(rows * k) * 4))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  if (cols <= kShortRow) {
+    RowsParams p;
+    p.in = in;
+    p.rows = rows;
+    p.ld = ld;
+    p.n = (int)cols;
+    p.k = k;
+    p.out = out;
+    const int64_t want = (rows + kWaves - 1) / kWaves;
+    const int grid = (int)(want < 8 * cus ? want : 8 * cus);
+    return launch(rows_fn(cols), grid, p, s);
+  }
+  const int gr = row_grid(rows, cols, cus);
+  TopkParams p;
+  p.n = cols;
+  p.ld = ld;
+  p.k = k;
+  p.grid = gr;
+  p.refresh = kRefreshPeriod;
+  p.cand = sc.cand;
+  p.heads = sc.heads;
+  p.kths = sc.kths;
+  p.ticket = sc.ticket;
+  const int64_t per_launch = kMaxLaunchBlocks / gr;
+  for (int64_t r0 = 0; r0 < rows; r0 += per_launch) {
+    const int64_t nr = rows - r0 < per_launch ? rows - r0 : per_launch;
+    p.in = in + r0 * ld;
+    p.out = out + r0 * k;
+    rc = launch(topk_fn(k), (int)(nr * gr), p, s);
+    if (rc != LIBTOPK_OK) return rc;
+  }
+  return LIBTOPK_OK;
+}
+
+int topk_merge_i32(const int32_t* lists, int64_t m, int32_t len, int32_t k,
+                   int32_t* out, libtopk_stream_t stream) {
+  if (!lists || !out) return LIBTOPK_ERR_INVALID;
+  if (((uintptr_t)lists & 3u) || ((uintptr_t)out & 3u))
+    return LIBTOPK_ERR_INVALID;
+  if (m < 1 || m > (int64_t)kMaxGrid * kMaxGrid || len < 1)
+    return LIBTOPK_ERR_INVALID;
+  if (k < 1 || (int64_t)k > m * len) return LIBTOPK_ERR_INVALID;
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (overlaps(lists, (size_t)(m * len) * 4, out, (size_t)k * 4))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  MergeParams p;
+  p.lists = lists;
+  p.m = m;
+  p.len = len;
+  p.k = k;
+  p.groups = (int)((m + kMaxGrid - 1) / kMaxGrid);
+  p.cand = sc.cand;
+  p.ticket = sc.ticket;
+  p.out = out;
+  return launch((const void*)&topk_merge_kernel, p.groups, p, s);
 }
 
 const char* libtopk_strerror(int status) {

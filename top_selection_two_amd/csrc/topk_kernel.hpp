@@ -44,20 +44,51 @@
 
 namespace ltk {
 
+// One launch covers `rows` rows of n elements each (row r starts at
+// in + r * ld); a single array is one row.  Each row gets `grid`
+// workgroups, blockIdx.x = row * grid + sub.  With grid > 1 the per-block
+// candidates of row r sit at cand + r * grid * k (heads, kths at
+// r * grid) and the last of the row's workgroups to finish merges them;
+// with grid == 1 the workgroup's own top-k is the row's result.
 struct TopkParams {
   const int* in;
-  int64_t n;
-  int64_t head;      // leading elements before the first 16-byte boundary
-  int64_t ntiles;    // full tiles of the aligned body
-  int64_t covered;   // elements in those tiles (they start at `head`)
+  int64_t n;         // elements per row
+  int64_t ld;        // elements between row starts
   int k;
-  int grid;          // stage-1 workgroups
+  int grid;          // stage-1 workgroups per row
   int refresh;       // certificate refresh period, in tiles (power of 2)
-  int* cand;         // [grid * k]  per-block candidates
-  int* heads;        // [grid]      max of each block's candidates
-  int* kths;         // [grid]      k-th largest of each block's candidates
-  unsigned* ticket;  // completion counter; 0 between calls
-  int* out;          // [k]         result, descending
+  int* cand;         // [rows * grid * k]  per-block candidates
+  int* heads;        // [rows * grid]      max of each block's candidates
+  int* kths;         // [rows * grid]      k-th largest of each block's
+  unsigned* ticket;  // [rows]             completion counters; 0 between calls
+  int* out;          // [rows * k]         results, descending
+};
+
+// Where a row's elements lie: `head` leading elements before the first
+// 16-byte boundary, then `ntiles` full tiles (`covered` elements), then the
+// tail.
+struct RowGeometry {
+  int64_t head, ntiles, covered;
+};
+
+template <int U>
+__device__ __forceinline__ RowGeometry row_geometry(const int* row,
+                                                    int64_t n) {
+  RowGeometry g;
+  const uint32_t a = (uint32_t)(uintptr_t)row;
+  g.head = (int64_t)(((16u - (a & 15u)) & 15u) >> 2);
+  if (g.head > n) g.head = n;
+  g.ntiles = ((n - g.head) >> 2) / (kBlock * U);
+  g.covered = g.ntiles * (kBlock * U * 4);
+  return g;
+}
+
+// A set of descending candidate lists: list b holds its entries at
+// cand[b * stride + e], e < per.
+struct CandView {
+  const int* cand;
+  int64_t stride;
+  int per;
 };
 
 constexpr int kSurvCap = 1024;  // stage-2 survivors staged in LDS
@@ -339,10 +370,10 @@ __device__ __forceinline__ void wave_append(bool p, int v, int* counter,
 // independent agent-coherent loads per thread are in flight before any is
 // used.  f(valid, value) is called uniformly across the block.
 template <class F>
-__device__ __forceinline__ void scan_flagged(const TopkParams& p,
+__device__ __forceinline__ void scan_flagged(const CandView& cv,
                                              const int* blocks, int total,
                                              F&& f) {
-  const int k = p.k;
+  const int per = cv.per;
   constexpr int B = 16;
   for (int base = 0; base < total; base += kBlock * B) {
     int v[B];
@@ -352,9 +383,9 @@ __device__ __forceinline__ void scan_flagged(const TopkParams& p,
       int idx = base + j * kBlock + (int)threadIdx.x;
       ok[j] = idx < total;
       idx = ok[j] ? idx : total - 1;
-      const int fb = idx / k;
-      const int e = idx - fb * k;
-      v[j] = ld_agent(p.cand + (int64_t)blocks[fb] * k + e);
+      const int fb = idx / per;
+      const int e = idx - fb * per;
+      v[j] = ld_agent(cv.cand + (int64_t)blocks[fb] * cv.stride + e);
     }
 #pragma unroll
     for (int j = 0; j < B; ++j) f(ok[j], v[j]);
@@ -472,24 +503,21 @@ __device__ __forceinline__ int rank_all(int* vals, int n, int& v) {
   return r;
 }
 
+// (1) Fill for the top-k kernel's own candidates: whole KiB chunks of the
+// block maxima (and of every candidate when all_in_lds) go to LDS in one
+// round trip; the largest block k-th value is T2b.  The last chunk may read
+// up to 1 KiB past a row's maxima or candidates: the maxima are followed by
+// the k-th values and the candidates by the maxima in the scratch area, so
+// it stays inside it, and the LDS areas hold kMaxGrid and kDirectCand
+// (multiples of 256) ints.  Ints past G or `total` are ignored.
 template <class SH>
-__device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
-                                                     SH& sh, Stage2Lds& s2,
-                                                     bool all_in_lds) {
-  const int G = p.grid, k = p.k, tid = threadIdx.x;
+__device__ __forceinline__ void stage2_fill_blocks(const int* heads,
+                                                   const int* kths,
+                                                   const int* cand, int G,
+                                                   int total, bool all_in_lds,
+                                                   SH& sh, Stage2Lds& s2) {
+  const int tid = threadIdx.x;
   const int w = tid / kWave;
-  const int total = G * k;
-  if (tid < kWave) s2.gmax_rank[tid] = 0;
-  if (tid == 0) {
-    sh.bcast[1] = kI32Min;  // largest block maximum
-    sh.bcast[2] = 0;        // survivors
-    sh.bcast[5] = 0;        // flagged blocks
-    sh.bcast[6] = kI32Min;  // T2b
-  }
-
-  // (1) Whole KiB chunks: the source areas hold kMaxGrid and more than
-  // kDirectCand ints, so the last chunk of each stays inside them; ints
-  // past G or `total` are ignored.
   constexpr int kChunkInts = 1024 / 4;
   const int hchunks = (G + kChunkInts - 1) / kChunkInts;
   const int chunks =
@@ -498,8 +526,8 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
     // Scalar bookkeeping: the wave index as a scalar, so that every
     // address below is computed once per wave, not per lane.
     const int ws = __builtin_amdgcn_readfirstlane(w);
-    const char* hsrc = reinterpret_cast<const char*>(uni_ptr(p.heads));
-    const char* csrc = reinterpret_cast<const char*>(uni_ptr(p.cand));
+    const char* hsrc = reinterpret_cast<const char*>(uni_ptr(heads));
+    const char* csrc = reinterpret_cast<const char*>(uni_ptr(cand));
     const uint32_t hlds = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)lds_offset(s2.heads));
     const uint32_t clds = (uint32_t)__builtin_amdgcn_readfirstlane(
@@ -514,11 +542,58 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
     }
   }
   int kt = kI32Min;
-  for (int b = tid; b < G; b += kBlock) kt = max(kt, ld_agent(p.kths + b));
+  for (int b = tid; b < G; b += kBlock) kt = max(kt, ld_agent(kths + b));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   kt = wave_max(kt);
   if (lane() == 0) atomicMax(&sh.bcast[6], kt);
+}
+
+// (1) Fill for G descending lists seen through a view (merging): each
+// list's first entry is its maximum; a list of at least k entries
+// certifies its k-th (T2b).
+template <class SH>
+__device__ __forceinline__ void stage2_fill_lists(const CandView& cv, int G,
+                                                  int k, SH& sh,
+                                                  Stage2Lds& s2) {
+  int kt = kI32Min;
+  for (int b = threadIdx.x; b < G; b += kBlock) {
+    const int* l = cv.cand + (int64_t)b * cv.stride;
+    s2.heads[b] = ld_agent(l);
+    if (cv.per >= k) kt = max(kt, ld_agent(l + (k - 1)));
+  }
+  __syncthreads();
+  kt = wave_max(kt);
+  if (lane() == 0) atomicMax(&sh.bcast[6], kt);
+}
+
+// Zero the stage-2 counters.  Barriers follow inside every fill before any
+// of them is updated.
+template <class SH>
+__device__ __forceinline__ void stage2_init(SH& sh, Stage2Lds& s2) {
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    s2.gmax_rank[tid] = 0;
+    s2.surv_rank[tid] = 0;
+  }
+  if (tid == 0) {
+    sh.bcast[1] = kI32Min;  // largest block maximum
+    sh.bcast[2] = 0;        // survivors
+    sh.bcast[5] = 0;        // flagged blocks
+    sh.bcast[6] = kI32Min;  // T2b
+  }
+}
+
+// (2) and (3), after a fill: the certified bound T2 and the survivors.
+// `all_in_lds`: the candidates were copied to s2.cand (contiguous lists,
+// stride == per).
+template <class SH>
+__device__ __forceinline__ Stage2Bound stage2_bound(const CandView& cv, int G,
+                                                    int k, bool all_in_lds,
+                                                    SH& sh, Stage2Lds& s2) {
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int per = cv.per;
 
   // (2) Group maxima into s2.gmax.  k <= 64: wave 0 forms 64 groups, lane
   // l taking blocks l*per .. l*per + per - 1 (per = G/64 rounded up to a
@@ -530,13 +605,13 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
   if (narrow) {
     if (w == 0) {
       constexpr int VH = kMaxGrid / kWave;
-      const int per = (((G + kWave - 1) / kWave) + 3) & ~3;
-      const v4i* h4 = reinterpret_cast<const v4i*>(s2.heads + lane() * per);
+      const int gper = (((G + kWave - 1) / kWave) + 3) & ~3;
+      const v4i* h4 = reinterpret_cast<const v4i*>(s2.heads + lane() * gper);
 #pragma unroll
       for (int q = 0; q < VH / 4; ++q) {
-        if (4 * q < per) {
+        if (4 * q < gper) {
           const v4i t = h4[q];
-          const int b = lane() * per + 4 * q;
+          const int b = lane() * gper + 4 * q;
           gm = max(gm, b < G ? t.x : kI32Min);
           gm = max(gm, b + 1 < G ? t.y : kI32Min);
           gm = max(gm, b + 2 < G ? t.z : kI32Min);
@@ -546,9 +621,9 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
       s2.gmax[lane()] = gm;
     }
   } else {
-    const int per = (G + kBlock - 1) / kBlock;
-    for (int j = 0; j < per; ++j) {
-      const int b = tid * per + j;
+    const int gper = (G + kBlock - 1) / kBlock;
+    for (int j = 0; j < gper; ++j) {
+      const int b = tid * gper + j;
       if (b < G) gm = max(gm, s2.heads[b]);
     }
     s2.gmax[tid] = gm;
@@ -590,7 +665,7 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
     wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
   }
   __syncthreads();
-  r.total = sh.bcast[5] * k;
+  r.total = sh.bcast[5] * per;
   if (r.t2 == r.mx) return r;  // the caller writes k copies of mx
 
   // Survivors.  Candidates equal to INT_MIN are left out: if T2 is INT_MIN
@@ -602,13 +677,13 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
       const int i = i0 + tid;
       int v = kI32Min;
       if (i < r.total) {
-        const int fb = i / k;
-        v = s2.cand[s2.blocks[fb] * k + (i - fb * k)];
+        const int fb = i / per;
+        v = s2.cand[s2.blocks[fb] * per + (i - fb * per)];
       }
       wave_append(v >= tf, v, &sh.bcast[2], s2.surv, kSurvCap);
     }
   } else {
-    scan_flagged(p, s2.blocks, r.total, [&](bool ok, int c) {
+    scan_flagged(cv, s2.blocks, r.total, [&](bool ok, int c) {
       wave_append(ok && c >= tf, c, &sh.bcast[2], s2.surv, kSurvCap);
     });
   }
@@ -617,24 +692,20 @@ __device__ __forceinline__ Stage2Bound stage2_gather(const TopkParams& p,
   return r;
 }
 
-// Stage 2 proper: gather, rank or select, write the result, re-arm the
-// ticket.
+// Stage 2 proper, after stage2_init, a fill and stage2_bound: rank or
+// select, and write the k results to out (agent-coherent stores, so that
+// another workgroup of the same launch may read them).
 template <class SH>
-__device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
-                                            Stage2Lds& s2) {
-  const int k = p.k;
+__device__ __forceinline__ void stage2_finish(const CandView& cv, int k,
+                                              const Stage2Bound& r, int* out,
+                                              SH& sh, Stage2Lds& s2) {
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
-  if (tid < kWave) s2.surv_rank[tid] = 0;  // barriers follow in the gather
-
-  const Stage2Bound r =
-      stage2_gather(p, sh, s2, (int64_t)p.grid * k <= kDirectCand);
   const int T2 = r.t2, mx = r.mx, m = r.m, total = r.total;
 
   if (T2 == mx) {
     // At least k candidates are >= T2 and none exceeds mx: k copies of mx.
-    for (int j = tid; j < k; j += kBlock) p.out[j] = mx;
-    if (tid == 0) st_agent(p.ticket, 0u);
+    for (int j = tid; j < k; j += kBlock) st_agent(out + j, mx);
     return;
   }
 
@@ -650,9 +721,8 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
     } else {
       rk = rank_all(s2.surv, m, v);
     }
-    if (tid < m && rk < k) p.out[rk] = v;
-    for (int j = m + tid; j < k; j += kBlock) p.out[j] = kI32Min;
-    if (tid == 0) st_agent(p.ticket, 0u);
+    if (tid < m && rk < k) st_agent(out + rk, v);
+    for (int j = m + tid; j < k; j += kBlock) st_agent(out + j, kI32Min);
     return;
   }
 
@@ -682,7 +752,7 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
       if (in_lds) {
         for (int i = tid; i < m; i += kBlock) mine += s2.surv[i] >= s;
       } else {
-        scan_flagged(p, s2.blocks, total, [&](bool ok, int v) {
+        scan_flagged(cv, s2.blocks, total, [&](bool ok, int v) {
           mine += ok & (v >= s) & (v >= T2);
         });
       }
@@ -700,7 +770,7 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
       wave_append(i < m && c > gs, c, &sh.bcast[3], s2.gt, kMaxK);
     }
   } else {
-    scan_flagged(p, s2.blocks, total, [&](bool ok, int c) {
+    scan_flagged(cv, s2.blocks, total, [&](bool ok, int c) {
       wave_append(ok && c > gs, c, &sh.bcast[3], s2.gt, kMaxK);
     });
   }
@@ -713,11 +783,25 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
       const int o = s2.gt[j];
       rk += (o > v) | ((o == v) & (j < tid));
     }
-    p.out[rk] = v;
+    st_agent(out + rk, v);
   } else if (tid < k) {
-    p.out[tid] = gs;
+    st_agent(out + tid, gs);
   }
-  if (tid == 0) st_agent(p.ticket, 0u);
+}
+
+// Stage 2 of the top-k kernel for one row: merge the row's grid * k block
+// candidates into out[0..k), then re-arm the row's ticket.
+template <class SH>
+__device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
+                                            Stage2Lds& s2) {
+  const int G = p.grid, k = p.k;
+  const bool all_in_lds = (int64_t)G * k <= kDirectCand;
+  const CandView cv{p.cand, k, k};
+  stage2_init(sh, s2);
+  stage2_fill_blocks(p.heads, p.kths, p.cand, G, G * k, all_in_lds, sh, s2);
+  const Stage2Bound r = stage2_bound(cv, G, k, all_in_lds, sh, s2);
+  stage2_finish(cv, k, r, p.out, sh, s2);
+  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
 template <int KCAP, bool FIT, int U>
@@ -728,7 +812,12 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   // `sh` apart from the in-flight ring loads and does not wait for those.
   __shared__ v4i ring_lds[kWaves][kRing][U][kWave];
   static_assert(sizeof(ring_lds) >= sizeof(Stage2Lds), "ring too small");
-  const int blk = blockIdx.x;
+  // This workgroup's row, and its place among the row's workgroups.
+  const int row = (int)(blockIdx.x / (unsigned)p.grid);
+  const int blk = (int)blockIdx.x - row * p.grid;
+  const int* __restrict__ rin = p.in + (int64_t)row * p.ld;
+  const RowGeometry geo = row_geometry<U>(rin, p.n);
+  const int64_t slot0 = (int64_t)row * p.grid;  // the row's first block slot
   const int k = p.k;
   const int w = threadIdx.x / kWave;
 
@@ -748,8 +837,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   // quarter of every tile straight into its own LDS ring (global_load_lds,
   // 16 B per lane, no VGPRs), kRing tiles ahead of the one it examines, so
   // the time spent inserting never leaves the memory pipe empty.
-  const v4i* __restrict__ body = reinterpret_cast<const v4i*>(p.in + p.head);
-  const int64_t count = tiles_of(p.ntiles, blk, p.grid);
+  const v4i* __restrict__ body = reinterpret_cast<const v4i*>(rin + geo.head);
+  const int64_t count = tiles_of(geo.ntiles, blk, p.grid);
   const int R = p.refresh;
   if (count > 0) {
     v4i(*ring)[U][kWave] = ring_lds[w];
@@ -793,11 +882,11 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   }
   // Elements outside the full tiles: the unaligned head and the tail.
   if (blk == p.grid - 1) {
-    const int64_t left = p.n - p.covered;
+    const int64_t left = p.n - geo.covered;
     for (int64_t base = 0; base < left; base += kBlock) {
       const int64_t i = base + threadIdx.x;
       int x = kI32Min;
-      if (i < left) x = p.in[i < p.head ? i : p.covered + i];
+      if (i < left) x = rin[i < geo.head ? i : geo.covered + i];
       admit<KCAP, FIT>(L, x, k, tsh, thr);
     }
   }
@@ -805,7 +894,9 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   // barrier: the bound is certified whatever the other waves are doing).
   refresh_bound(L, k, tsh, thr, sh);
   const int T = tsh;  // certified for the workgroup; may differ per wave
-  int* dst = p.cand + (int64_t)blk * k;
+  // A row with one workgroup: its top-k is the row's result.
+  const bool direct = p.grid == 1;
+  int* dst = direct ? p.out + (int64_t)row * k : p.cand + (slot0 + blk) * k;
 
   // ---- block candidates: the workgroup's exact top-k ---------------------
   // The entries >= T among the first k of every list include the
@@ -832,7 +923,12 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
           base = uni(base);
           const int pos = base + lanes_below(b);
           if (q && pos < kBlock) sh.blist[pos] = L[i];
-          more = base + popc(b) < kBlock;
+          // Stop once the list has overflowed (the count then exceeds
+          // kBlock, which sends the workgroup to the fallback).  A list
+          // filled exactly to kBlock must go on: a deeper level may hold
+          // more entries, and stopping would leave the count looking
+          // complete.
+          more = base + popc(b) <= kBlock;
         }
       }
     }
@@ -849,8 +945,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     }
     if ((int)threadIdx.x < lb && rk < k) {
       st_agent(dst + rk, v);
-      if (rk == 0) st_agent(p.heads + blk, v);
-      if (rk == k - 1) st_agent(p.kths + blk, v);
+      if (!direct && rk == 0) st_agent(p.heads + slot0 + blk, v);
+      if (!direct && rk == k - 1) st_agent(p.kths + slot0 + blk, v);
     }
   } else {
     // Wave merge: each wave's top-k of its entries >= T.
@@ -878,6 +974,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     // Block merge (wave 0): top-k of the four wave results.  T of wave 0 is
     // a valid lower end for the search: the workgroup's k-th largest value
     // is >= it, and each wave result holds that wave's share of the top-k.
+    // The values above the k-th (fewer than k) go to LDS, where the whole
+    // workgroup ranks them, so the candidates come out in order here too.
     if (w == 0) {
       constexpr int V = (kWaves * KCAP + kWave - 1) / kWave;
       unsigned u[V];
@@ -899,21 +997,88 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       for (int j = 0; j < V; ++j) {
         const bool q = u[j] > g;
         const uint64_t b = ballot(q);
-        if (q) st_agent(dst + base + lanes_below(b), unbias(u[j]));
+        if (q) sh.blist[base + lanes_below(b)] = unbias(u[j]);
         base += popc(b);
       }
-      for (int j = lane(); j < k - base; j += kWave)
-        st_agent(dst + base + j, unbias(g));
       if (lane() == 0) {
-        st_agent(p.heads + blk, mx);
-        st_agent(p.kths + blk, unbias(g));
+        sh.bcast[0] = base;
+        sh.bcast[1] = unbias(g);
+        if (!direct) {
+          st_agent(p.heads + slot0 + blk, mx);
+          st_agent(p.kths + slot0 + blk, unbias(g));
+        }
       }
     }
+    __syncthreads();
+    const int ngt = sh.bcast[0], gv = sh.bcast[1];
+    int v;
+    const int rk = rank_all(sh.blist, ngt, v);  // ngt < k <= kBlock
+    if ((int)threadIdx.x < ngt) st_agent(dst + rk, v);
+    for (int j = ngt + (int)threadIdx.x; j < k; j += kBlock)
+      st_agent(dst + j, gv);
   }
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
-  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
-  topk_stage2(p, sh, *reinterpret_cast<Stage2Lds*>(&ring_lds[0][0][0][0]));
+  if (direct) return;
+  if (!last_to_finish(p.ticket + row, p.grid, &sh.is_last)) return;
+  TopkParams q = p;  // the row's slice of the scratch and of the output
+  q.cand = p.cand + slot0 * k;
+  q.heads = p.heads + slot0;
+  q.kths = p.kths + slot0;
+  q.ticket = p.ticket + row;
+  q.out = p.out + (int64_t)row * k;
+  topk_stage2(q, sh, *reinterpret_cast<Stage2Lds*>(&ring_lds[0][0][0][0]));
+}
+
+// ---- merging descending lists ---------------------------------------------
+// The k largest values of the union of m descending lists of `len` values
+// each ([TopK] §6: several top-k results merged again; it is exactly the
+// page's stage 2, §2.2, applied to lists the caller provides).  Only the
+// first min(len, k) entries of a list can be among the k largest, each
+// list's first entry is its maximum and a list of at least k entries
+// certifies its k-th, so the stage-2 machinery above applies as is.  One
+// workgroup merges up to kMaxGrid lists; more lists are cut into groups of
+// kMaxGrid, each group's top-k goes to scratch, and the last group to
+// finish merges those (the same hand-off as the top-k kernel).
+struct MergeParams {
+  const int* lists;  // list b at lists + b * len, descending
+  int64_t m;         // lists
+  int len;           // entries per list
+  int k;
+  int groups;        // workgroups, each merging up to kMaxGrid lists
+  int* cand;         // [groups * k] group results (groups > 1)
+  unsigned* ticket;  // completion counter (groups > 1); 0 between calls
+  int* out;          // [k]
+};
+
+struct MergeShared {
+  int red[2][kWaves];
+  int bcast[8];
+  int is_last;
+};
+
+__global__ __launch_bounds__(kBlock) void topk_merge_kernel(MergeParams p) {
+  __shared__ MergeShared sh;
+  __shared__ Stage2Lds s2;
+  const int g = blockIdx.x;
+  const int64_t first = (int64_t)g * kMaxGrid;
+  const int nl = (int)min((int64_t)kMaxGrid, p.m - first);
+  const int k = p.k;
+  const CandView cv{p.lists + first * p.len, p.len, min(p.len, k)};
+  int* dst = p.groups == 1 ? p.out : p.cand + (int64_t)g * k;
+  stage2_init(sh, s2);
+  stage2_fill_lists(cv, nl, k, sh, s2);
+  const Stage2Bound r = stage2_bound(cv, nl, k, false, sh, s2);
+  stage2_finish(cv, k, r, dst, sh, s2);
+  if (p.groups == 1) return;
+
+  if (!last_to_finish(p.ticket, p.groups, &sh.is_last)) return;
+  const CandView cg{p.cand, k, k};
+  stage2_init(sh, s2);
+  stage2_fill_lists(cg, p.groups, k, sh, s2);
+  const Stage2Bound r2 = stage2_bound(cg, p.groups, k, false, sh, s2);
+  stage2_finish(cg, k, r2, p.out, sh, s2);
+  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
 }  // namespace ltk

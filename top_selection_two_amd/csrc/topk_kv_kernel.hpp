@@ -728,7 +728,12 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
           base = uni(base);
           const int pos = base + lanes_below(b);
           if (q && pos < kBlock) sh.blist[pos] = L.key(i);
-          more = base + popc(b) < kBlock;
+          // Stop once the list has overflowed (the count then exceeds
+          // kBlock, which sends the workgroup to the fallback).  A list
+          // filled exactly to kBlock must go on: a deeper level may hold
+          // more entries, and stopping would leave the count looking
+          // complete.
+          more = base + popc(b) <= kBlock;
         }
       }
     }
