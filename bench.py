@@ -1,6 +1,7 @@
 """Benchmark: Top-20 over 1e8 int32 on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path topk|stats|kv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--path topk|stats|kv|batched|batched_short]
 
 One step is one full library call (both stages; a single kernel launch)
 over a resident synthetic input (seeded SplitMix64).  The default path,
@@ -10,7 +11,12 @@ sum, max, min and sum of squares in one pass) over 2^26 int32 uniform in
 [-1000, 1000] (seed 2), the array whose sum, max and min are otherwise
 asked for in three separate calls.  `--path kv` measures topk_kv_i32, the
 key-value variant (the 20 largest values with their int64 positions, ties
-by position), on the same 1e8 array as `topk`.
+by position), on the same 1e8 array as `topk`.  `--path batched` and
+`--path batched_short` measure topk_batched_i32, the top-20 of every row of
+the same array viewed as 1000 rows of 100,000 (streaming kernel, one
+workgroup per row) or as 97,656 rows of 1,024 (one wave per row); the same
+run also times topk_merge_i32 merging the rows' lists into the top-20 of
+the whole, reported in `config.merge`.
 
 The input sits in HBM before timing starts.  W untimed calls, then K timed
 back-to-back calls bracketed by device synchronisation and by a pair of HIP
@@ -93,7 +99,47 @@ PATHS = {
         "out_bytes": 12 * K,
         "oracle_what": "top-20 keys by a stable sort of positions",
     },
+    "batched": {
+        "metric": ("Per-row Top-20 over 1e8 int32 as 1000 rows x 100,000: "
+                   "elements/s, HBM GB/s as % of 8 TB/s peak"),
+        "workload": "full_1e8",
+        "rows": 1000, "cols": 100_000,
+        "describe": ("top-20 of each of 1000 rows of 100,000 int32 (the 1e8 "
+                     "array, uniform over the full int32 range, SplitMix64 "
+                     "seed 3, viewed row-major), resident in HBM"),
+        "short": "per-row top-20 of 1000 x 100,000 int32, seed 3",
+        "kernel": "topk_kernel",
+        "sources": ["wave.hpp", "topk_kernel.hpp", "libtopk.hip"],
+        "counters": "topk_batched_counters_1000x100000_k20.json",
+        "summary": "topk_batched_1000x100000_k20.md",
+        "out_bytes": 4 * K * 1000,
+        "oracle_what": "per-row top-20 by copy + std::sort of each row",
+    },
+    "batched_short": {
+        "metric": ("Per-row Top-20 over 1e8 int32 as 97,656 rows x 1,024: "
+                   "elements/s, HBM GB/s as % of 8 TB/s peak"),
+        "workload": "full_1e8",
+        "rows": 97_656, "cols": 1024,
+        "describe": ("top-20 of each of 97,656 rows of 1,024 int32 (the "
+                     "first 99,999,744 elements of the 1e8 array, uniform "
+                     "over the full int32 range, SplitMix64 seed 3, viewed "
+                     "row-major), resident in HBM"),
+        "short": "per-row top-20 of 97,656 x 1,024 int32, seed 3",
+        "kernel": "topk_rows_kernel",
+        "sources": ["wave.hpp", "topk_rows_kernel.hpp", "libtopk.hip"],
+        "counters": "topk_rows_counters_97656x1024_k20.json",
+        "summary": "topk_rows_97656x1024_k20.md",
+        "out_bytes": 4 * K * 97_656,
+        "oracle_what": "per-row top-20 by copy + std::sort of each row",
+    },
 }
+
+
+def workload_size(P) -> int:
+    import synth
+    if "rows" in P:
+        return P["rows"] * P["cols"]
+    return synth.WORKLOADS[P["workload"]]["n"]
 
 
 def kernel_source_hash(path: str) -> str:
@@ -157,7 +203,7 @@ def summarize(run_dir: str, out_dir: str, path: str) -> None:
         with open(files[0]) as f:
             return list(csv.DictReader(f))
 
-    n = synth.WORKLOADS[P["workload"]]["n"]
+    n = workload_size(P)
     copy_bytes = 4 * n
     algo = 4 * n + P["out_bytes"]
 
@@ -309,10 +355,19 @@ def main():
     ltk.set_grid(args.grid)
 
     x = synth.workload(P["workload"])
+    if "rows" in P:
+        x = x[:P["rows"] * P["cols"]]
     n = x.size
     xd = torch.from_numpy(x).to(dev)
     stream = torch.cuda.current_stream(dev)
-    if args.path == "topk":
+    if "rows" in P:
+        x2 = x.reshape(P["rows"], P["cols"])
+        xd2 = xd.view(P["rows"], P["cols"])
+        out = torch.empty((P["rows"], K), dtype=torch.int32, device=dev)
+
+        def call():
+            return ltk.topk_batched(xd2, K, out=out)
+    elif args.path == "topk":
         out = torch.empty(K, dtype=torch.int32, device=dev)
 
         def call():
@@ -344,7 +399,13 @@ def main():
 
     # Correctness first (the oracle is the CPU reference; test-only code).
     import oracle
-    if args.path == "topk":
+    if "rows" in P:
+        got = call().cpu().numpy()
+        t_rows = time.perf_counter()
+        want = oracle.topk_batched(x2, K)
+        t_rows = time.perf_counter() - t_rows   # the baseline: one call
+        ok = np.array_equal(got, want)
+    elif args.path == "topk":
         got = call().cpu().numpy()
         want = oracle.topk(x, K)
         ok = np.array_equal(got, want)
@@ -398,9 +459,35 @@ def main():
         "traffic": measured_traffic(args.path),
     }
 
+    merge = None
+    if "rows" in P:
+        # The rows' top-20 lists merged into the top-20 of the whole array,
+        # checked against the oracle's merge of its own row results, then
+        # timed the same way (one launch per call).
+        mout = torch.empty(K, dtype=torch.int32, device=dev)
+        got_m = ltk.topk_merge(out, K, out=mout).cpu().numpy()
+        if not np.array_equal(got_m, oracle.topk_merge(want, K)):
+            print("MISMATCH in the merge", got_m, file=sys.stderr)
+            sys.exit(3)
+        for _ in range(args.warmup):
+            ltk.topk_merge(out, K, out=mout)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            ltk.topk_merge(out, K, out=mout)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        merge = {"lists": P["rows"], "len": K, "k": K,
+                 "kernel_ms_avg": round(ev0.elapsed_time(ev1) / args.steps,
+                                        5)}
+
     cpu = None
     if not args.no_cpu_baseline:
-        if args.path == "topk":
+        if "rows" in P:
+            t_med, reps = t_rows, 1
+            what = "the full workload (%d x %d int32, seed 3)" % (
+                P["rows"], P["cols"])
+        elif args.path == "topk":
             t_med, reps = time_oracle(lambda: oracle.topk(x, K))
             what = "the full workload (1e8 int32, seed 3)"
         elif args.path == "kv":
@@ -423,10 +510,14 @@ def main():
         }
 
     config = {"workload": P["describe"], "n": n}
+    if "rows" in P:
+        config.update({"rows": P["rows"], "cols": P["cols"], "k": K,
+                       "merge": merge})
     if args.path in ("topk", "kv"):
         config["k"] = K
+    if "rows" not in P:
+        config["grid"] = ltk.grid_for(n)
     config.update({
-        "grid": ltk.grid_for(n),
         "kernel_ms_avg": round(avg_launch_ms, 5),
         "hbm_gbps_per_step": round(algo_bytes / (ms_per_step * 1e-3) / 1e9, 1),
     })

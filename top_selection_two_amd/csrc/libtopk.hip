@@ -259,6 +259,24 @@ const void* reduce_fn(int op) {
   return (const void*)&reduce_kernel<kOpMin, kTileVec>;
 }
 
+// Workgroups of one kernel that fit on a CU at once (registers, LDS), from
+// the runtime's occupancy calculator; at least 1.
+int resident_blocks(const void* fn) {
+  static std::mutex mu;
+  static std::map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(fn);
+  if (it != cache.end()) return it->second;
+  int b = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, kBlock, 0) !=
+          hipSuccess || b < 1) {
+    (void)hipGetLastError();
+    b = 1;
+  }
+  cache[fn] = b;
+  return b;
+}
+
 // Rows of at most this many elements go one wave per row, the whole row in
 // registers (topk_rows_kernel); longer rows stream through topk_kernel.
 constexpr int64_t kShortRow = 4096;
@@ -266,14 +284,26 @@ constexpr int64_t kShortRow = 4096;
 // further launches).
 constexpr int64_t kMaxLaunchBlocks = (int64_t)1 << 20;
 
-// Elements per lane: the row length rounded up to a multiple of 64 from
-// {256, 512, 1024, 2048, 4096}.
-const void* rows_fn(int64_t n) {
-  if (n <= 256) return (const void*)&topk_rows_kernel<4>;
-  if (n <= 512) return (const void*)&topk_rows_kernel<8>;
-  if (n <= 1024) return (const void*)&topk_rows_kernel<16>;
-  if (n <= 2048) return (const void*)&topk_rows_kernel<32>;
-  return (const void*)&topk_rows_kernel<64>;
+// Elements per lane V: the row length rounded up to 64 V, V from
+// {4, 8, 16, 32, 64}.  Rows of exactly 64 V elements that all start on a
+// 16-byte boundary take the vector-load variant.
+template <int V>
+const void* rows_fn_v(bool full) {
+  return full ? (const void*)&topk_rows_kernel<V, true>
+              : (const void*)&topk_rows_kernel<V, false>;
+}
+
+const void* rows_fn(const int32_t* in, int64_t n, int64_t ld) {
+  const int v = n <= 256 ? 4 : n <= 512 ? 8 : n <= 1024 ? 16 : n <= 2048 ? 32
+                                                                        : 64;
+  const bool full = n == 64 * v && ((uintptr_t)in & 15u) == 0 && ld % 4 == 0;
+  switch (v) {
+    case 4: return rows_fn_v<4>(full);
+    case 8: return rows_fn_v<8>(full);
+    case 16: return rows_fn_v<16>(full);
+    case 32: return rows_fn_v<32>(full);
+    default: return rows_fn_v<64>(full);
+  }
 }
 
 // Workgroups per row for rows longer than kShortRow: enough workgroups in
@@ -453,9 +483,14 @@ int topk_batched_i32(const int32_t* in, int64_t rows, int64_t cols,
     p.n = (int)cols;
     p.k = k;
     p.out = out;
+    // Exactly as many workgroups as fit on the device at once: each wave
+    // then walks its share of the rows to the end, with no second, partly
+    // filled round of workgroups.
+    const void* fn = rows_fn(in, cols, ld);
     const int64_t want = (rows + kWaves - 1) / kWaves;
-    const int grid = (int)(want < 8 * cus ? want : 8 * cus);
-    return launch(rows_fn(cols), grid, p, s);
+    const int64_t slots = (int64_t)resident_blocks(fn) * cus;
+    const int grid = (int)(want < slots ? want : slots);
+    return launch(fn, grid, p, s);
   }
   const int gr = row_grid(rows, cols, cus);
   TopkParams p;

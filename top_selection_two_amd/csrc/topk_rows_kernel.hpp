@@ -22,12 +22,13 @@
 //     larger k, a lower bound on the k-th largest element itself.  Both
 //     come from a short bitwise radix search over ballot counts.
 //  3. The elements >= T (about k to 2k of them on random data) are
-//     compacted into the wave's LDS buffer at offsets from a wave prefix
-//     sum of the per-lane counts.
-//  4. Each is ranked by counting (a 64-bit key: biased value, then the
-//     complement of its buffer slot, so ranks are distinct and equal
-//     values take consecutive ranks); ranks < k are the row's result, in
-//     order.
+//     compacted into the wave's LDS buffer, one ballot per register slot.
+//  4. Up to 64 of them, one per lane, are sorted across the wave by a
+//     bitonic network whose exchanges stay in registers (DPP and the
+//     gfx950 row swaps); lanes 0..k-1 then hold the result in order.  More
+//     candidates (up to 256) are ranked by counting instead (a 64-bit key:
+//     biased value, then the complement of the buffer slot, so ranks are
+//     distinct and equal values take consecutive ranks).
 // Heavy ties (more candidates than the buffer holds) or a bound that
 // certifies nothing (INT_MIN) take an exact path: radix selection of the
 // k-th largest g over the registers, the elements above g ranked, then
@@ -49,26 +50,11 @@ struct RowsParams {
 
 constexpr int kRowCap = 256;  // candidates per wave held in LDS
 
-// One wave's LDS: kRowCap candidate slots, 16 slots of padding for the
-// 16-wide ranking reads, then one slot per lane that takes the writes of
-// lanes with nothing to write (so the compaction has no branches).
-constexpr int kRowDump = kRowCap + 16;
+// One wave's LDS: kRowCap candidate slots and 16 slots of padding for the
+// 16-wide ranking reads.
 struct RowsWaveLds {
-  alignas(16) int buf[kRowDump + kWave];
+  alignas(16) int buf[kRowCap + 16];
 };
-
-// Inclusive prefix sum over the wave (row shifts within 16-lane rows, then
-// the two row broadcasts), and the wave total.
-__device__ __forceinline__ int wave_scan_incl(int v, int& total) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  total = __builtin_amdgcn_readlane(v, 63);
-  return v;
-}
 
 // Rank each of the m (<= kRowCap) values in buf by counting and write those
 // of rank < k to out.  Slots m .. m rounded up to 16 are first set to
@@ -104,103 +90,215 @@ __device__ __forceinline__ void wave_rank_out(int* buf, int m, int k,
   }
 }
 
-template <int V>
+// The value of lane (this lane ^ s), s a power of two below 64, without
+// LDS: quad permutes for 1 and 2, row rotations for 4 and 8 (dst lane i of
+// a 16-lane row reads lane (i - r) mod 16 for row_ror:r), and the gfx950
+// row swaps for 16 and 32 (which return both halves of the exchange).
+__device__ __forceinline__ int xor_lane(int v, int s) {
+  if (s == 1) return __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false);
+  if (s == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false);
+  if (s == 4) {
+    const int a = __builtin_amdgcn_update_dpp(v, v, 0x124, 0xf, 0xf, false);
+    const int b = __builtin_amdgcn_update_dpp(v, v, 0x12c, 0xf, 0xf, false);
+    return (lane() & 4) ? a : b;
+  }
+  if (s == 8) return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xf, 0xf, false);
+  if (s == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v,
+                                                    false, false);
+    return (int)((lane() & 16) ? r[0] : r[1]);
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v,
+                                                  false, false);
+  return (int)((lane() & 32) ? r[0] : r[1]);
+}
+
+// Bitonic sort of one value per lane, descending, within aligned groups of
+// W lanes (W = 32 or 64): lane 0 of a group ends with its largest value.
+// log2(W) (log2(W) + 1) / 2 compare-exchange steps, all in registers.
+template <int W>
+__device__ __forceinline__ int wave_sort_desc(int v) {
+  const int l = lane();
+#pragma unroll
+  for (int size = 2; size <= W; size <<= 1) {
+#pragma unroll
+    for (int s = size / 2; s > 0; s >>= 1) {
+      const int o = xor_lane(v, s);
+      // The lower lane of a pair keeps the larger value in a run that is
+      // being sorted descending, the smaller in an ascending one.
+      const bool keep_max = ((l & s) == 0) == ((l & size) == 0);
+      v = keep_max ? max(v, o) : min(v, o);
+    }
+  }
+  return v;
+}
+
+// Append the elements that pass (x[j] > t, or >= t) to buf, one ballot per
+// register slot, at offsets from a wave-uniform count; nothing is written
+// past cap.  Returns the number that pass (it may exceed cap).  Slots
+// past n (when not FULL) never pass: callers use t > INT_MIN, or strict.
+template <int V, bool STRICT>
+__device__ __forceinline__ int compact(const int (&x)[V], int t, int* buf,
+                                       int cap) {
+  int m = 0;  // wave-uniform
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const bool q = STRICT ? x[j] > t : x[j] >= t;
+    const uint64_t b = ballot(q);
+    if (b != 0) {
+      const int c = popc(b);
+      if (q && m + c <= cap) buf[m + lanes_below(b)] = x[j];
+      m += c;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  return m;
+}
+
+// radix_select counter over a row held in registers: the number of
+// elements >= the candidate, compared as signed values (no biased copy of
+// the row is kept).  Slots past n do not count.
+template <int V, bool FULL>
+struct RowCount {
+  const int (&x)[V];
+  int n;
+  __device__ __forceinline__ int operator()(unsigned c) const {
+    const int t = unbias(c);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      cnt += popc(ballot((FULL || lane() + kWave * j < n) && x[j] >= t));
+    return cnt;
+  }
+};
+
+// The top-k of one row held in registers, V slots per lane.  FULL: every
+// slot holds an element (in any order).  Otherwise x[j] is element
+// lane + 64 j of the row, and slots past n hold INT_MIN and do not count.
+// Writes out[0..k), descending.
+template <int V, bool FULL>
+__device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
+                                         int* out, RowsWaveLds& L) {
+  auto valid = [&](int j) __attribute__((always_inline)) {
+    return FULL || lane() + kWave * j < n;
+  };
+  // 2. The bound.
+  int mx = x[0];
+#pragma unroll
+  for (int j = 1; j < V; ++j) mx = max(mx, x[j]);
+  const int hi = wave_max(mx);
+  auto row_min = [&]() __attribute__((always_inline)) {
+    int mn = kI32Max;
+#pragma unroll
+    for (int j = 0; j < V; ++j) mn = min(mn, valid(j) ? x[j] : kI32Max);
+    return wave_min(mn);
+  };
+  int T;
+  if (k <= kWave) {
+    const unsigned bm[1] = {bias(mx)};
+    T = unbias(radix_lower_bound(bias(wave_min(mx)), bias(hi), k, 8,
+                                 RegCount<1>{bm}));
+  } else {
+    T = unbias(radix_lower_bound(bias(row_min()), bias(hi), k, 8,
+                                 RowCount<V, FULL>{x, n}));
+  }
+
+  // 3. Candidates: elements >= T (T > INT_MIN keeps the padding out); at
+  // least k of them, since T is certified.
+  const int m = T > kI32Min ? compact<V, false>(x, T, L.buf, kRowCap)
+                            : kRowCap + 1;
+
+  if (m <= 32) {
+    // 4. The usual case: at most 32 candidates, one per lane of the lower
+    // half, sorted there; lanes 0..k-1 then hold the result in order.
+    const int v = wave_sort_desc<32>(lane() < m ? L.buf[lane()] : kI32Min);
+    if (lane() < k) out[lane()] = v;
+  } else if (m <= kWave) {
+    const int v = wave_sort_desc<kWave>(lane() < m ? L.buf[lane()] : kI32Min);
+    if (lane() < k) out[lane()] = v;
+  } else if (m <= kRowCap) {
+    // 4'. Up to kRowCap candidates: rank by counting.
+    wave_rank_out(L.buf, m, k, out);
+  } else {
+    // Exact path: the k-th largest g by radix selection over the row, the
+    // elements above g (fewer than k) ranked, then copies of g.
+    const int g = unbias(radix_select(bias(row_min()), bias(hi), k,
+                                      RowCount<V, FULL>{x, n}));
+    const int ngt = compact<V, true>(x, g, L.buf, kRowCap);
+    wave_rank_out(L.buf, ngt, k, out);
+    for (int j = ngt + lane(); j < k; j += kWave) out[j] = g;
+  }
+  // The buffer is reused by the next row: finish reading it first.
+  __builtin_amdgcn_wave_barrier();
+}
+
+// FULL: every row has exactly 64 * V elements and starts on a 16-byte
+// boundary, so lane l loads 16-byte vectors l, l + 64, ... (each wave
+// instruction reads 1 KiB of consecutive bytes) with no masks, and for
+// rows of up to 1024 elements the next row's loads are issued before the
+// current row is processed.
+// Otherwise lane l loads single elements l, l + 64, ... clamped to the row
+// (each wave instruction reads 256 consecutive bytes), for any row length,
+// start and stride.
+template <int V, bool FULL>
 __global__ __launch_bounds__(kBlock) void topk_rows_kernel(RowsParams p) {
   __shared__ RowsWaveLds lds[kWaves];
   const int w = threadIdx.x / kWave;
   RowsWaveLds& L = lds[w];
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int n = p.n, k = p.k;
+  int64_t r = (int64_t)blockIdx.x * kWaves + w;
 
-  for (int64_t r = (int64_t)blockIdx.x * kWaves + w; r < p.rows;
-       r += nwaves) {
-    const int* __restrict__ src = p.in + r * p.ld;
-    int* dst = p.out + r * k;
-
-    // 1. The row, lane-strided; slots past n hold INT_MIN (the loads are
-    // clamped to the last element, so none is skipped or out of range).
-    int x[V];
+  if constexpr (FULL) {
+    static_assert(V % 4 == 0, "whole 16-byte vectors per lane");
+    constexpr int Q = V / 4;
+    // Longer rows keep enough bytes in flight per wave without a second
+    // buffer (and need the registers).
+    constexpr bool kPrefetch = V <= 16;
+    auto load = [&](int64_t row, v4i (&d)[Q]) __attribute__((always_inline)) {
+      const v4i* src = reinterpret_cast<const v4i*>(p.in + row * p.ld);
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int idx = lane() + kWave * j;
-      const int v = __builtin_nontemporal_load(src + (idx < n ? idx : n - 1));
-      x[j] = idx < n ? v : kI32Min;
-    }
-
-    // 2. The bound.
-    int mx = x[0], mn = kI32Max;
+      for (int q = 0; q < Q; ++q)
+        d[q] = __builtin_nontemporal_load(src + lane() + kWave * q);
+    };
+    v4i cur[Q];
+    if (kPrefetch && r < p.rows) load(r, cur);
+    for (; r < p.rows; r += nwaves) {
+      v4i nxt[Q];
+      const bool more = kPrefetch && r + nwaves < p.rows;
+      if (more) load(r + nwaves, nxt);
+      if (!kPrefetch) load(r, cur);
+      int x[V];
 #pragma unroll
-    for (int j = 1; j < V; ++j) mx = max(mx, x[j]);
+      for (int q = 0; q < Q; ++q) {
+        x[4 * q + 0] = cur[q].x;
+        x[4 * q + 1] = cur[q].y;
+        x[4 * q + 2] = cur[q].z;
+        x[4 * q + 3] = cur[q].w;
+      }
+      row_topk<V, true>(x, n, k, p.out + r * k, L);
+      if (more) {
 #pragma unroll
-    for (int j = 0; j < V; ++j)
-      mn = min(mn, lane() + kWave * j < n ? x[j] : kI32Max);
-    const int hi = wave_max(mx);
-    const int lo = wave_min(mn);
-    int T;
-    if (k <= kWave) {
-      const unsigned bm[1] = {bias(mx)};
-      T = unbias(radix_lower_bound(bias(wave_min(mx)), bias(hi), k, 8,
-                                   RegCount<1>{bm}));
-    } else {
-      unsigned u[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) u[j] = bias(x[j]);
-      // Padding counts only at INT_MIN, where real elements already
-      // number n >= k.
-      T = unbias(radix_lower_bound(bias(lo), bias(hi), k, 8,
-                                   RegCount<V>{u}));
-    }
-
-    // 3. Candidates: elements >= T.  T > INT_MIN keeps the padding out.
-    int m = kRowCap + 1;
-    if (T > kI32Min) {
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < V; ++j) c += x[j] >= T;
-      const int incl = wave_scan_incl(c, m);
-      if (m <= kRowCap) {
-        int off = incl - c;
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const bool q = x[j] >= T;
-          L.buf[q ? off : kRowDump + lane()] = x[j];
-          off += q;
-        }
-        __builtin_amdgcn_wave_barrier();
+        for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
       }
     }
-
-    if (m <= kRowCap) {
-      // 4. Rank by counting.
-      wave_rank_out(L.buf, m, k, dst);
-    } else {
-      // Exact path: the k-th largest g by radix selection over the row,
-      // the elements above g (fewer than k) ranked, then copies of g.
-      unsigned u[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j)
-        u[j] = lane() + kWave * j < n ? bias(x[j]) : 0u;
-      // Padding is biased to 0 and only counts at 0 (INT_MIN), where the
-      // n >= k real elements already reach it.
-      const int g = unbias(radix_select(bias(lo), bias(hi), k,
-                                        RegCount<V>{u}));
-      int c = 0;
-#pragma unroll
-      for (int j = 0; j < V; ++j) c += x[j] > g;
-      int ngt;
-      int off = wave_scan_incl(c, ngt) - c;
+  } else {
+    for (; r < p.rows; r += nwaves) {
+      const int* __restrict__ src = p.in + r * p.ld;
+      // Opaque copy of n: keeps the compiler from hoisting the V clamped
+      // addresses out of the loop, where they would hold 2 V registers.
+      int nn = n;
+      asm volatile("" : "+s"(nn));
+      int x[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const bool q = x[j] > g;
-        L.buf[q ? off : kRowDump + lane()] = x[j];
-        off += q;
+        const int idx = lane() + kWave * j;
+        const int v =
+            __builtin_nontemporal_load(src + (idx < nn ? idx : nn - 1));
+        x[j] = idx < nn ? v : kI32Min;
       }
-      __builtin_amdgcn_wave_barrier();
-      wave_rank_out(L.buf, ngt, k, dst);
-      for (int j = ngt + lane(); j < k; j += kWave) dst[j] = g;
+      row_topk<V, false>(x, n, k, p.out + r * k, L);
     }
-    // The buffer is reused by the next row: finish reading it first.
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

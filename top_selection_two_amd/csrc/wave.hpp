@@ -64,28 +64,29 @@ __device__ __forceinline__ int unbias(unsigned u) {
 // Wave-wide max / min with DPP row shifts and row broadcasts: after the
 // four row_shr steps lane 15 of every 16-lane row holds that row's
 // reduction, the two broadcasts carry it across rows, and lane 63 ends with
-// the result of the whole wave.  Lanes without a source keep their own value
-// (old = v), which max and min ignore.
-#define LTK_DPP(v, ctrl, rows) \
-  __builtin_amdgcn_update_dpp((v), (v), (ctrl), (rows), 0xf, false)
+// the result of the whole wave.  Lanes without a source (or in a row the
+// row mask leaves out) read the operator's identity, so the compiler can
+// fold each move into the max or min as a DPP operand.
+#define LTK_DPP(id, v, ctrl, rows) \
+  __builtin_amdgcn_update_dpp((id), (v), (ctrl), (rows), 0xf, false)
 
 __device__ __forceinline__ int wave_max(int v) {
-  v = max(v, LTK_DPP(v, 0x111, 0xf));  // row_shr:1
-  v = max(v, LTK_DPP(v, 0x112, 0xf));  // row_shr:2
-  v = max(v, LTK_DPP(v, 0x114, 0xf));  // row_shr:4
-  v = max(v, LTK_DPP(v, 0x118, 0xf));  // row_shr:8
-  v = max(v, LTK_DPP(v, 0x142, 0xa));  // row_bcast:15 into rows 1, 3
-  v = max(v, LTK_DPP(v, 0x143, 0xc));  // row_bcast:31 into rows 2, 3
+  v = max(v, LTK_DPP(kI32Min, v, 0x111, 0xf));  // row_shr:1
+  v = max(v, LTK_DPP(kI32Min, v, 0x112, 0xf));  // row_shr:2
+  v = max(v, LTK_DPP(kI32Min, v, 0x114, 0xf));  // row_shr:4
+  v = max(v, LTK_DPP(kI32Min, v, 0x118, 0xf));  // row_shr:8
+  v = max(v, LTK_DPP(kI32Min, v, 0x142, 0xa));  // row_bcast:15 into rows 1, 3
+  v = max(v, LTK_DPP(kI32Min, v, 0x143, 0xc));  // row_bcast:31 into rows 2, 3
   return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ int wave_min(int v) {
-  v = min(v, LTK_DPP(v, 0x111, 0xf));
-  v = min(v, LTK_DPP(v, 0x112, 0xf));
-  v = min(v, LTK_DPP(v, 0x114, 0xf));
-  v = min(v, LTK_DPP(v, 0x118, 0xf));
-  v = min(v, LTK_DPP(v, 0x142, 0xa));
-  v = min(v, LTK_DPP(v, 0x143, 0xc));
+  v = min(v, LTK_DPP(kI32Max, v, 0x111, 0xf));
+  v = min(v, LTK_DPP(kI32Max, v, 0x112, 0xf));
+  v = min(v, LTK_DPP(kI32Max, v, 0x114, 0xf));
+  v = min(v, LTK_DPP(kI32Max, v, 0x118, 0xf));
+  v = min(v, LTK_DPP(kI32Max, v, 0x142, 0xa));
+  v = min(v, LTK_DPP(kI32Max, v, 0x143, 0xc));
   return __builtin_amdgcn_readlane(v, 63);
 }
 
