@@ -69,6 +69,9 @@ class Oracle:
         lib.oracle_topk_merge_i32.argtypes = [p, ctypes.c_int64,
                                               ctypes.c_int32, ctypes.c_int32, p]
         lib.oracle_topk_merge_i32.restype = ctypes.c_int
+        lib.oracle_histogram_i32.argtypes = [p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, p]
+        lib.oracle_histogram_i32.restype = ctypes.c_int
         for name in ("oracle_topk_kv_i32", "oracle_topk_kv_f32"):
             fn = getattr(lib, name)
             fn.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, p]
@@ -162,6 +165,18 @@ class Oracle:
                              "(m=%d, len=%d, k=%d)" % (m, ln, k))
         return out
 
+    def histogram(self, x, lo: int, shift: int, nbins: int) -> np.ndarray:
+        """int64 counts of x in nbins bins of width 2**shift from lo."""
+        a = _as_i32(x)
+        out = np.zeros(max(nbins, 0), dtype=np.int64)
+        rc = self.lib.oracle_histogram_i32(a.ctypes.data if a.size else None,
+                                           a.size, lo, shift, nbins,
+                                           out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_histogram_i32: invalid arguments "
+                             "(shift=%d, nbins=%d)" % (shift, nbins))
+        return out
+
     def check_topk(self, x, k: int, cand) -> int:
         """0 if cand is exactly the descending top-k of x, else 1/2/3."""
         a = _as_i32(x)
@@ -208,6 +223,10 @@ def stats(x) -> dict:
 
 def topk_kv(x, k: int):
     return default().topk_kv(x, k)
+
+
+def histogram(x, lo: int, shift: int, nbins: int) -> np.ndarray:
+    return default().histogram(x, lo, shift, nbins)
 
 
 def topk_batched(x, k: int, cols: int | None = None) -> np.ndarray:

@@ -86,6 +86,18 @@
  *                     last k backwards.  A list that is not in descending
  *                     order is a caller error, reported as such.
  *
+ *   oracle_histogram_i32
+ *                     counts of the values falling into equal-width bins
+ *                     ([TopK] §6: histogram computation as a use of the
+ *                     two-stage reduction; "GPU基数排序优化：10亿级数据处理与
+ *                     性能调优" §3.3: per-warp histograms merged at the end).
+ *                     Bin b covers the integers lo + b * 2^shift up to
+ *                     lo + (b + 1) * 2^shift - 1; values outside all nbins
+ *                     bins are not counted.  Definition: one loop over the
+ *                     input, each value's bin found by subtracting lo (in
+ *                     64-bit arithmetic, so nothing wraps) and dividing by
+ *                     the bin width.
+ *
  *   oracle_check_topk a second, sort-free characterisation of the top-k
  *                     multiset, linear in n.  It is used to check results
  *                     at sizes where sorting is too slow, and as an
@@ -317,6 +329,29 @@ int oracle_topk_merge_i32(const int32_t *lists, int64_t m, int32_t len,
     std::sort(v.begin(), v.end());
     for (int32_t i = 0; i < k; ++i)
         out[i] = v[(size_t)(total - 1 - i)];
+    return 0;
+}
+
+/* out[b] for b < nbins: how many values v of in[0..n) have
+ * lo + b * 2^shift <= v < lo + (b + 1) * 2^shift.  Returns 0, or -1 on
+ * invalid arguments (null pointers, n < 0, shift outside 0..31, nbins < 1). */
+int oracle_histogram_i32(const int32_t *in, int64_t n, int32_t lo,
+                         int32_t shift, int32_t nbins, int64_t *out)
+{
+    if (!out || n < 0 || (n > 0 && !in) || shift < 0 || shift > 31 ||
+        nbins < 1)
+        return -1;
+    const int64_t width = (int64_t)1 << shift;
+    for (int32_t b = 0; b < nbins; ++b)
+        out[b] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t d = (int64_t)in[i] - (int64_t)lo;
+        if (d < 0)
+            continue;
+        const int64_t b = d / width;
+        if (b < nbins)
+            ++out[b];
+    }
     return 0;
 }
 

@@ -351,10 +351,53 @@ def pin_topk_merge(o, rng):
         assert o.topk_merge(tops, kk).tolist() == whole.tolist()
 
 
+def pin_histogram(o, rng):
+    """Histogram: hand examples, numpy's own histogram with integer bin
+    edges (a library routine sharing nothing with the oracle's loop),
+    closed forms over permutations, the extremes of int32, and brute force
+    over tiny inputs."""
+    x = np.array([0, 1, 1, 2, 255, 256, -1, 7, 7, 7], np.int32)
+    assert o.histogram(x, 0, 0, 256)[[0, 1, 2, 7, 255]].tolist() == \
+        [1, 2, 1, 3, 1]
+    assert o.histogram(x, 0, 0, 256).sum() == 8        # -1 and 256 fall out
+    assert o.histogram(x, 0, 3, 2).tolist() == [7, 0]  # [0, 8) and [8, 16)
+    assert o.histogram(x, -1, 8, 2).tolist() == [8, 2]  # [-1, 255), [255, 511)
+    assert o.histogram(np.zeros(0, np.int32), 0, 0, 4).tolist() == [0] * 4
+    full = np.array([I32_MIN, -1, 0, I32_MAX], np.int32)
+    assert o.histogram(full, I32_MIN, 31, 2).tolist() == [2, 2]
+    assert o.histogram(full, I32_MAX, 0, 1).tolist() == [1]
+    assert o.histogram(full, I32_MIN, 0, 1).tolist() == [1]
+    for trial in range(40):
+        n = int(rng.integers(0, 3000))
+        spread = int(rng.choice([10, 1000, 2 ** 31]))
+        a = rng.integers(-spread, spread, size=n, dtype=np.int64)
+        a = a.astype(np.int32)
+        lo = int(rng.integers(-spread, spread))
+        shift = int(rng.integers(0, 24))
+        nbins = int(rng.integers(1, 5000))
+        edges = lo + (np.arange(nbins + 1, dtype=np.float64) * 2.0 ** shift)
+        want, _ = np.histogram(a.astype(np.float64), bins=edges - 0.5)
+        assert o.histogram(a, lo, shift, nbins).tolist() == want.tolist()
+    for s in (0, 3, 10):
+        n = 5000
+        perm = rng.permutation(n).astype(np.int32)
+        h = o.histogram(perm, 0, s, (n >> s) + 2)
+        w = 1 << s
+        assert h[: n // w].tolist() == [w] * (n // w)
+        assert h.sum() == n
+    for xs in itertools.product([I32_MIN, -3, 0, 5, I32_MAX], repeat=3):
+        a = np.array(xs, np.int32)
+        for lo, shift, nbins in ((-4, 1, 5), (I32_MIN, 30, 4), (0, 0, 6)):
+            want = [sum(1 for v in xs
+                        if lo + b * 2 ** shift <= v < lo + (b + 1) * 2 ** shift)
+                    for b in range(nbins)]
+            assert o.histogram(a, lo, shift, nbins).tolist() == want
+
+
 BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
            pin_empty_identities, pin_int64_sum, pin_closed_forms,
            pin_invariants, pin_checker_rejects, pin_stats, pin_topk_kv,
-           pin_topk_batched, pin_topk_merge]
+           pin_topk_batched, pin_topk_merge, pin_histogram]
 
 
 def run_battery(o, seed=7):
@@ -441,6 +484,14 @@ MUTANTS = {
     "merge_accepts_unsorted": (r"return -2;", "(void)0;"),
     "merge_ascending": (r"out\[i\] = v\[\(size_t\)\(total - 1 - i\)\];",
                         "out[i] = v[(size_t)(total - k + i)];"),
+    "histogram_off_by_one_bin": (r"const int64_t b = d / width;",
+                                 "const int64_t b = (d + 1) / width;"),
+    "histogram_keeps_last_edge": (r"if \(b < nbins\)\n            \+\+out\[b\];",
+                                  "if (b <= nbins - 1 || d == nbins * width)\n"
+                                  "            ++out[b < nbins ? b : nbins - 1];"),
+    "histogram_wraps_in_32_bits": (
+        r"const int64_t d = \(int64_t\)in\[i\] - \(int64_t\)lo;",
+        "const int64_t d = (int32_t)((uint32_t)in[i] - (uint32_t)lo);"),
 }
 
 
