@@ -24,8 +24,9 @@
  *    nothing is launched and the output is untouched.  Launch and
  *    allocation failures are reported as LIBTOPK_ERR_HIP / _NOMEM; a fault
  *    inside a kernel surfaces at the caller's next synchronisation.
- *  - The library owns a small scratch area per (device, stream): 512 KiB of
- *    per-block candidates plus a few KiB of counters.  It is allocated by the
+ *  - The library owns a small scratch area per (device, stream), about
+ *    1.6 MiB: per-block candidates (1.5 MiB, int32 and key-value), partial
+ *    results, histogram counters and tickets.  It is allocated by the
  *    first call on that pair (so do that first call before capturing the
  *    stream into a HIP graph), kept for reuse, and freed by
  *    libtopk_release() or at process exit.  Every call leaves it ready for
@@ -53,7 +54,7 @@ typedef struct ihipStream_t *libtopk_stream_t;
 enum {
     LIBTOPK_OK = 0,
     LIBTOPK_ERR_INVALID = 1,     /* bad pointer, size, k or op            */
-    LIBTOPK_ERR_UNSUPPORTED = 2, /* k above libtopk_max_k()               */
+    LIBTOPK_ERR_UNSUPPORTED = 2, /* k above the call's supported maximum  */
     LIBTOPK_ERR_NOMEM = 3,       /* scratch allocation failed             */
     LIBTOPK_ERR_HIP = 4          /* no device, or a HIP call / launch failed */
 };
@@ -61,8 +62,15 @@ enum {
 /* Reduction operators for reduce_i32. */
 enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
 
-/* Largest supported k. */
+/* Largest k of every top-k entry point (the register-list path). */
 #define LIBTOPK_MAX_K 128
+
+/* Largest k of topk_i32, which takes k above LIBTOPK_MAX_K through radix
+ * selection. */
+#define LIBTOPK_MAX_K_SELECT 16384
+
+/* Most bins of histogram_i32. */
+#define LIBTOPK_MAX_BINS 4096
 
 /*
  * topk_i32 — the k largest values of in[0..n), written to out[0..k) in
@@ -72,16 +80,23 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
  * two-stage design: §2.1 each thread keeps a descending local top-k list
  * over a grid-stride share of the input, and the block merges the lists;
  * §2.2 a second, single-block stage merges the per-block candidates; the
- * result must be identical to the CPU's).  Here both stages run in one
- * launch: the last workgroup to finish stage 1 performs stage 2.
+ * result must be identical to the CPU's).  For k <= LIBTOPK_MAX_K both
+ * stages run in one launch: the last workgroup to finish stage 1 performs
+ * stage 2.  Larger k, up to LIBTOPK_MAX_K_SELECT, goes through radix
+ * selection ("GPU基数排序优化：10亿级数据处理与性能调优" §3.2–3.3: 8-bit digit
+ * histograms kept per warp in shared memory): up to four digit passes find
+ * the k-th largest value, a gather pass collects the values above it, and
+ * one workgroup sorts the k results; six stream-ordered launches, reading
+ * the input up to five times.
  *
- *   in   device, int32[n], read once
+ *   in   device, int32[n], read once (k <= LIBTOPK_MAX_K)
  *   n    number of elements, 1 <= n <= 2^32
- *   k    1 <= k <= min(n, LIBTOPK_MAX_K)
+ *   k    1 <= k <= min(n, LIBTOPK_MAX_K_SELECT)
  *   out  device, int32[k], written in full
  *
  * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, n out of
- * range, k < 1 or k > n; LIBTOPK_ERR_UNSUPPORTED for k > LIBTOPK_MAX_K.
+ * range, k < 1 or k > n; LIBTOPK_ERR_UNSUPPORTED for
+ * k > LIBTOPK_MAX_K_SELECT.
  */
 int topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out,
              libtopk_stream_t stream);
@@ -222,6 +237,33 @@ int topk_batched_i32(const int32_t *in, int64_t rows, int64_t cols,
  */
 int topk_merge_i32(const int32_t *lists, int64_t m, int32_t len, int32_t k,
                    int32_t *out, libtopk_stream_t stream);
+
+/*
+ * histogram_i32 — counts of the values of in[0..n) in nbins equal bins:
+ * out[b] = the number of elements v with
+ *     lo + b * 2^shift <= v <= lo + (b + 1) * 2^shift - 1
+ * (bounds taken in exact integer arithmetic); values outside all bins are
+ * not counted.
+ *
+ * Operation: [TopK] §6 (histogram computation as a use of the two-stage
+ * reduction) and "GPU基数排序优化：10亿级数据处理与性能调优" §3.3 (one
+ * shared-memory histogram per warp, merged at the end, rather than global
+ * atomics per element).  One launch: per-wave histograms in LDS, per-block
+ * totals added into device counters, and the last workgroup to finish
+ * writes the result and clears the counters.
+ *
+ *   in     device, int32[n] (may be NULL when n == 0)
+ *   n      0 <= n <= 2^32
+ *   lo     the first bin's lowest value (any int32)
+ *   shift  bin width 2^shift, 0 <= shift <= 31
+ *   nbins  1 <= nbins <= LIBTOPK_MAX_BINS
+ *   out    device, int64[nbins], 8-byte aligned, written in full
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, n, shift
+ * or nbins out of range, or overlapping in and out.
+ */
+int histogram_i32(const int32_t *in, int64_t n, int32_t lo, int32_t shift,
+                  int32_t nbins, int64_t *out, libtopk_stream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *libtopk_strerror(int status);

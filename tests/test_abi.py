@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"topk_i32", "reduce_i32", "reduce_stats_i32", "topk_kv_i32",
             "topk_kv_f32", "topk_batched_i32", "topk_merge_i32",
+            "histogram_i32",
             "libtopk_strerror",
             "libtopk_max_k", "libtopk_set_grid", "libtopk_grid_for",
             "libtopk_release"} <= set(names)
@@ -53,6 +54,9 @@ def test_constants_match_header():
                       ("LIBTOPK_MAX", 1), ("LIBTOPK_MIN", 2)]:
         assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text), name
     assert re.search(r"#define LIBTOPK_MAX_K 128\b", text)
+    assert re.search(r"#define LIBTOPK_MAX_K_SELECT %d\b" % ltk.MAX_K_SELECT,
+                     text)
+    assert re.search(r"#define LIBTOPK_MAX_BINS %d\b" % ltk.MAX_BINS, text)
     assert ltk.max_k() == 128
 
 
@@ -74,7 +78,7 @@ def test_strerror():
     ((FAKE, 100, 0, FAKE * 4), ltk.ERR_INVALID),           # k = 0
     ((FAKE, 100, -3, FAKE * 4), ltk.ERR_INVALID),          # k < 0
     ((FAKE, 10, 11, FAKE * 4), ltk.ERR_INVALID),           # k > n
-    ((FAKE, 1000, 129, FAKE * 4), ltk.ERR_UNSUPPORTED),    # k above max
+    ((FAKE, 100000, 16385, FAKE * 64), ltk.ERR_UNSUPPORTED),  # k above max
     ((FAKE, 1000, 20, FAKE + 400), ltk.ERR_INVALID),       # out inside in
     ((FAKE, 1000, 20, FAKE - 40), ltk.ERR_INVALID),        # out overlaps in
 ])
@@ -179,6 +183,24 @@ def test_topk_merge_rejects_invalid_arguments(args, status):
     assert ltk.topk_merge_raw(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    # (in, n, lo, shift, nbins, out)
+    ((FAKE, 100, 0, 0, 16, 0), ltk.ERR_INVALID),                 # NULL output
+    ((FAKE, 100, 0, 0, 16, FAKE * 64 + 4), ltk.ERR_INVALID),     # out not 8-aligned
+    ((FAKE + 2, 100, 0, 0, 16, FAKE * 64), ltk.ERR_INVALID),     # misaligned in
+    ((0, 100, 0, 0, 16, FAKE * 64), ltk.ERR_INVALID),            # NULL in, n > 0
+    ((FAKE, -1, 0, 0, 16, FAKE * 64), ltk.ERR_INVALID),          # n < 0
+    ((FAKE, (1 << 32) + 1, 0, 0, 16, 1 << 40), ltk.ERR_INVALID), # n > 2^32
+    ((FAKE, 100, 0, -1, 16, FAKE * 64), ltk.ERR_INVALID),        # shift < 0
+    ((FAKE, 100, 0, 32, 16, FAKE * 64), ltk.ERR_INVALID),        # shift > 31
+    ((FAKE, 100, 0, 0, 0, FAKE * 64), ltk.ERR_INVALID),          # nbins = 0
+    ((FAKE, 100, 0, 0, 4097, FAKE * 64), ltk.ERR_INVALID),       # nbins > max
+    ((FAKE, 100, 0, 0, 16, FAKE + 64), ltk.ERR_INVALID),         # out inside in
+])
+def test_histogram_rejects_invalid_arguments(args, status):
+    assert ltk.histogram_raw(*args) == status
+
+
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
@@ -192,6 +214,9 @@ def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_batched_raw(FAKE, 4, 100, 100, 5, FAKE * 64) == \
         ltk.ERR_HIP
     assert ltk.topk_merge_raw(FAKE, 8, 20, 20, FAKE * 64) == ltk.ERR_HIP
+    assert ltk.histogram_raw(FAKE, 100, 0, 0, 16, FAKE * 64) == ltk.ERR_HIP
+    assert ltk.histogram_raw(0, 0, 0, 0, 16, FAKE * 64) == ltk.ERR_HIP
+    assert ltk.topk_raw(FAKE, 100000, 5000, FAKE * 64) == ltk.ERR_HIP
 
 
 def test_grid_setting():

@@ -20,6 +20,9 @@ if the library is not built, importing this package raises.
     topk_merge(lists, k)
                     -> int32 tensor [k]: the k largest of the union of the
                        rows of lists (each row in descending order)
+    histogram(x, lo, shift, nbins)
+                    -> int64 tensor [nbins]: counts of x in bins of width
+                       2**shift starting at lo
 """
 from __future__ import annotations
 
@@ -30,6 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_HERE, "libtopk.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_NOMEM, ERR_HIP = 0, 1, 2, 3, 4
+MAX_K_SELECT = 16384   # LIBTOPK_MAX_K_SELECT: largest k of topk()
+MAX_BINS = 4096        # LIBTOPK_MAX_BINS
 SUM, MAX, MIN = 0, 1, 2
 OPS = {"sum": SUM, "max": MAX, "min": MIN}
 
@@ -50,6 +55,8 @@ SIGNATURES = {
                          ctypes.c_int),
     "topk_merge_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                         _VP, _VP], ctypes.c_int),
+    "histogram_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int32, _VP, _VP], ctypes.c_int),
     "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "libtopk_max_k": ([], ctypes.c_int),
     "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
@@ -149,6 +156,13 @@ def topk_merge_raw(lists_ptr: int, m: int, length: int, k: int, out_ptr: int,
     """Call topk_merge_i32 on raw device pointers; returns the status."""
     return lib.topk_merge_i32(lists_ptr or None, m, length, k,
                               out_ptr or None, stream or None)
+
+
+def histogram_raw(in_ptr: int, n: int, lo: int, shift: int, nbins: int,
+                  out_ptr: int, stream: int = 0) -> int:
+    """Call histogram_i32 on raw device pointers; returns the status."""
+    return lib.histogram_i32(in_ptr or None, n, lo, shift, nbins,
+                             out_ptr or None, stream or None)
 
 
 # ---------------------------------------------------------------- tensors
@@ -326,4 +340,27 @@ def topk_merge(lists, k: int, out=None):
                                 stream or None)
     if rc != OK:
         raise LibtopkError(rc, "topk_merge_i32")
+    return out
+
+
+def histogram(x, lo: int, shift: int, nbins: int, out=None):
+    """int64 counts of the int32 device tensor x in nbins bins of width
+    2**shift starting at lo (see histogram_i32)."""
+    import torch
+    _check_input(x)
+    if out is None:
+        out = torch.empty(max(int(nbins), 0), dtype=torch.int64,
+                          device=x.device)
+    elif (out.dtype != torch.int64 or out.device != x.device
+          or out.numel() != nbins or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int64 [nbins] tensor on "
+                         "x's device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.histogram_i32(x.data_ptr() if x.numel() else None,
+                               x.numel(), lo, shift, nbins,
+                               out.data_ptr() if out.numel() else None,
+                               stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "histogram_i32")
     return out

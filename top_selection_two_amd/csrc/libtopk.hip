@@ -20,6 +20,7 @@
 #include <utility>
 
 #include "libtopk.h"
+#include "hist_kernel.hpp"
 #include "reduce_kernel.hpp"
 #include "stats_kernel.hpp"
 #include "topk_kernel.hpp"
@@ -44,6 +45,9 @@ struct Scratch {
   uint64_t* kvcand = nullptr;  // kMaxGrid * kMaxK (key-value candidates)
   uint64_t* kvheads = nullptr; // kMaxGrid
   uint64_t* kvkths = nullptr;  // kMaxGrid
+  unsigned long long* acc = nullptr;  // kMaxBins histogram counters, 0
+                                      // between calls
+  RadixState* rstate = nullptr;       // radix-selection state
   unsigned* ticket = nullptr;  // kMaxGrid words (one per row), 0 between calls
 };
 
@@ -53,10 +57,13 @@ constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
 constexpr size_t kStatBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
 constexpr size_t kKvCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(uint64_t);
 constexpr size_t kKvHeadBytes = (size_t)kMaxGrid * sizeof(uint64_t);
+constexpr size_t kAccBytes = (size_t)kMaxBins * sizeof(unsigned long long);
+constexpr size_t kStateBytes = 256;
 constexpr size_t kTicketBytes = (size_t)kMaxGrid * sizeof(unsigned);
 constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes +
                                  kStatBytes + kKvCandBytes +
-                                 2 * kKvHeadBytes + kTicketBytes;
+                                 2 * kKvHeadBytes + kAccBytes + kStateBytes +
+                                 kTicketBytes;
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Scratch> g_cache;
@@ -128,11 +135,17 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   b += kKvHeadBytes;
   s.kvkths = (uint64_t*)b;
   b += kKvHeadBytes;
+  s.acc = (unsigned long long*)b;
+  b += kAccBytes;
+  s.rstate = (RadixState*)b;
+  b += kStateBytes;
   s.ticket = (unsigned*)b;
-  // A kernel (not a memset) clears the counter, ordered on the caller's
-  // stream before the first real launch.
-  hipLaunchKernelGGL(zero_words, dim3(kMaxGrid / 256), dim3(256), 0, stream,
-                     s.ticket, kMaxGrid);
+  // A kernel (not a memset) clears the histogram counters, the selection
+  // state and the tickets (contiguous), ordered on the caller's stream
+  // before the first real launch.
+  const int zwords = (int)((kAccBytes + kStateBytes + kTicketBytes) / 4);
+  hipLaunchKernelGGL(zero_words, dim3((zwords + 255) / 256), dim3(256), 0,
+                     stream, (unsigned*)s.acc, zwords);
   e = hipGetLastError();
   if (e != hipSuccess) {
     debug_hip("zero_words launch", e);
@@ -253,6 +266,53 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
+// Top-k for LIBTOPK_MAX_K < k <= LIBTOPK_MAX_K_SELECT: four digit passes of
+// radix selection, a gather pass and a one-workgroup sort, all
+// stream-ordered launches on the caller's stream.
+int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
+                hipStream_t s, const Scratch& sc, const Plan& pl) {
+  HistParams hp = {};
+  hp.in = in;
+  hp.n = n;
+  hp.head = pl.head;
+  hp.ntiles = pl.ntiles;
+  hp.covered = pl.covered;
+  hp.grid = pl.grid;
+  hp.st = sc.rstate;
+  hp.k = k;
+  hp.acc = sc.acc;
+  hp.ticket = sc.ticket;
+  for (int pass = 0; pass < 4; ++pass) {
+    hp.dshift = 24 - 8 * pass;
+    hp.first = pass == 0;
+    const int rc =
+        launch((const void*)&hist_kernel<kTileVec, true>, pl.grid, hp, s);
+    if (rc != LIBTOPK_OK) return rc;
+  }
+  GatherParams gp;
+  gp.in = in;
+  gp.n = n;
+  gp.head = pl.head;
+  gp.ntiles = pl.ntiles;
+  gp.covered = pl.covered;
+  gp.grid = pl.grid;
+  gp.k = k;
+  gp.st = sc.rstate;
+  gp.out = out;
+  gp.ticket = sc.ticket;
+  int rc = launch((const void*)&gather_kernel<kTileVec>, pl.grid, gp, s);
+  if (rc != LIBTOPK_OK) return rc;
+  void* args[] = {&out, &k};
+  const hipError_t e = hipLaunchKernel((const void*)&sort_desc_kernel,
+                                       dim3(1), dim3(kSortThreads), args, 0, s);
+  if (e != hipSuccess) {
+    debug_hip("kernel launch", e);
+    (void)hipGetLastError();
+    return LIBTOPK_ERR_HIP;
+  }
+  return LIBTOPK_OK;
+}
+
 const void* reduce_fn(int op) {
   if (op == kOpSum) return (const void*)&reduce_kernel<kOpSum, kTileVec>;
   if (op == kOpMax) return (const void*)&reduce_kernel<kOpMax, kTileVec>;
@@ -331,7 +391,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return LIBTOPK_ERR_INVALID;
   if (n < 1 || n > kMaxN) return LIBTOPK_ERR_INVALID;
   if (k < 1 || (int64_t)k > n) return LIBTOPK_ERR_INVALID;
-  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (k > LIBTOPK_MAX_K_SELECT) return LIBTOPK_ERR_UNSUPPORTED;
   if (overlaps(in, (size_t)n * 4, out, (size_t)k * 4))
     return LIBTOPK_ERR_INVALID;
   int dev = 0;
@@ -347,6 +407,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     cus = compute_units(dev);
   }
   const Plan pl = plan(in, n, cus);
+  if (k > LIBTOPK_MAX_K) return topk_select(in, n, k, out, s, sc, pl);
   TopkParams p;
   p.in = in;
   p.n = n;
@@ -542,6 +603,46 @@ int topk_merge_i32(const int32_t* lists, int64_t m, int32_t len, int32_t k,
   p.ticket = sc.ticket;
   p.out = out;
   return launch((const void*)&topk_merge_kernel, p.groups, p, s);
+}
+
+int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
+                  int32_t nbins, int64_t* out, libtopk_stream_t stream) {
+  if (!out || ((uintptr_t)out & 7u)) return LIBTOPK_ERR_INVALID;
+  if (n < 0 || n > kMaxN) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && (!in || ((uintptr_t)in & 3u))) return LIBTOPK_ERR_INVALID;
+  if (shift < 0 || shift > 31 || nbins < 1 || nbins > LIBTOPK_MAX_BINS)
+    return LIBTOPK_ERR_INVALID;
+  if (n > 0 && overlaps(in, (size_t)n * 4, out, (size_t)nbins * 8))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  // n == 0: a one-block launch with nothing to read writes zero counts.
+  static const int32_t kDummy = 0;
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  HistParams p = {};
+  p.in = in;
+  p.n = n;
+  p.head = pl.head;
+  p.ntiles = pl.ntiles;
+  p.covered = pl.covered;
+  p.grid = pl.grid;
+  p.lo = lo;
+  p.shift = shift;
+  p.nbins = nbins;
+  p.out = out;
+  p.acc = sc.acc;
+  p.ticket = sc.ticket;
+  return launch((const void*)&hist_kernel<kTileVec, false>, pl.grid, p, s);
 }
 
 const char* libtopk_strerror(int status) {

@@ -51,7 +51,7 @@ struct RowsParams {
 constexpr int kRowCap = 256;  // candidates per wave held in LDS
 
 // One wave's LDS: kRowCap candidate slots and 16 slots of padding for the
-// 16-wide ranking reads.
+// ranking reads.
 struct RowsWaveLds {
   alignas(16) int buf[kRowCap + 16];
 };
@@ -60,7 +60,7 @@ struct RowsWaveLds {
 // of rank < k to out.  Slots m .. m rounded up to 16 are first set to
 // INT_MIN, whose keys never exceed a real one (a real INT_MIN sits in a
 // lower slot).  Every lane reads the same 16 bytes at a time (an LDS
-// broadcast).
+// broadcast); the reads stop at m rounded up to 4.
 __device__ __forceinline__ void wave_rank_out(int* buf, int m, int k,
                                               int* out) {
   const int m16 = (m + 15) & ~15;
@@ -72,45 +72,97 @@ __device__ __forceinline__ void wave_rank_out(int* buf, int m, int k,
     const int v = i < m ? buf[i] : kI32Min;
     const uint64_t ki = ((uint64_t)bias(v) << 32) | (uint32_t)~i;
     int r = 0;
-    for (int j0 = 0; j0 < m; j0 += 16) {
-      v4i o4[4];
+    for (int j0 = 0; j0 < m; j0 += 4) {
+      const v4i o4 = q[j0 / 4];
+      const int o[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) o4[t] = q[j0 / 4 + t];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int o[4] = {o4[t].x, o4[t].y, o4[t].z, o4[t].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = j0 + 4 * t + e;
-          r += (((uint64_t)bias(o[e]) << 32) | (uint32_t)~j) > ki;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        r += (((uint64_t)bias(o[e]) << 32) | (uint32_t)~j) > ki;
       }
     }
     if (i < m && r < k) out[r] = v;
   }
 }
 
-// The value of lane (this lane ^ s), s a power of two below 64, without
-// LDS: quad permutes for 1 and 2, row rotations for 4 and 8 (dst lane i of
-// a 16-lane row reads lane (i - r) mod 16 for row_ror:r), and the gfx950
-// row swaps for 16 and 32 (which return both halves of the exchange).
-__device__ __forceinline__ int xor_lane(int v, int s) {
-  if (s == 1) return __builtin_amdgcn_update_dpp(v, v, 0xb1, 0xf, 0xf, false);
-  if (s == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4e, 0xf, 0xf, false);
-  if (s == 4) {
-    const int a = __builtin_amdgcn_update_dpp(v, v, 0x124, 0xf, 0xf, false);
-    const int b = __builtin_amdgcn_update_dpp(v, v, 0x12c, 0xf, 0xf, false);
-    return (lane() & 4) ? a : b;
+// Lanes whose bit is set in `mask` take a, the others b: one v_cndmask
+// whose condition is a constant lane mask held in a scalar register pair.
+__device__ __forceinline__ int pick_lanes(uint64_t mask, int a, int b) {
+  int r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+  return r;
+}
+
+// Lanes l with (l & bit) != 0.
+constexpr uint64_t lanes_with(int bit) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (l & bit) m |= 1ull << l;
+  return m;
+}
+
+// Lanes that keep the larger value of their pair in the bitonic step with
+// partner distance s inside runs of `size`: the lower lane of a pair in a
+// run sorted descending, the upper lane in an ascending one.
+constexpr uint64_t keep_max_lanes(int size, int s) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & s) == 0) == ((l & size) == 0)) m |= 1ull << l;
+  return m;
+}
+
+// DPP controls: quad permutes [1,0,3,2] and [2,3,0,1], row rotations by 4,
+// 8 and 12 (dst lane i of a 16-lane row reads lane (i - r) mod 16).
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor12 = 0x12c;
+
+// One compare-exchange step of a bitonic network across the wave: every
+// lane meets the lane at distance s (l ^ s) and keeps the max or the min.
+// For s = 1, 2, 8 the partner arrives as a DPP operand of the max and of the
+// min themselves (the identity as `old` lets the compiler fold the moves);
+// for s = 4 two bank-masked row rotations build it (banks 1 and 3 of a row
+// read 4 lanes down, banks 0 and 2 read 4 lanes up); for 16 and 32 the
+// gfx950 row swaps return both halves of the exchange.
+template <int SIZE, int S>
+__device__ __forceinline__ int bitonic_step(int v) {
+  constexpr uint64_t keep = keep_max_lanes(SIZE, S);
+  int hi, lo;
+  if constexpr (S == 1 || S == 2 || S == 8) {
+    constexpr int c = S == 1 ? kQuadXor1 : S == 2 ? kQuadXor2 : kRowRor8;
+    hi = max(v, __builtin_amdgcn_update_dpp(kI32Min, v, c, 0xf, 0xf, false));
+    lo = min(v, __builtin_amdgcn_update_dpp(kI32Max, v, c, 0xf, 0xf, false));
+  } else {
+    int o;
+    if constexpr (S == 4) {
+      const int t =
+          __builtin_amdgcn_update_dpp(0, v, kRowRor4, 0xf, 0xa, false);
+      o = __builtin_amdgcn_update_dpp(t, v, kRowRor12, 0xf, 0x5, false);
+    } else {
+      const auto r =
+          S == 16 ? __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v,
+                                                     false, false)
+                  : __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v,
+                                                     false, false);
+      o = pick_lanes(lanes_with(S), (int)r[0], (int)r[1]);
+    }
+    hi = max(v, o);
+    lo = min(v, o);
   }
-  if (s == 8) return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xf, 0xf, false);
-  if (s == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v,
-                                                    false, false);
-    return (int)((lane() & 16) ? r[0] : r[1]);
-  }
-  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v,
-                                                  false, false);
-  return (int)((lane() & 32) ? r[0] : r[1]);
+  return pick_lanes(keep, hi, lo);
+}
+
+template <int SIZE, int S>
+__device__ __forceinline__ int bitonic_merge(int v) {
+  v = bitonic_step<SIZE, S>(v);
+  if constexpr (S > 1) v = bitonic_merge<SIZE, S / 2>(v);
+  return v;
+}
+
+template <int SIZE, int W>
+__device__ __forceinline__ int bitonic_sort(int v) {
+  v = bitonic_merge<SIZE, SIZE / 2>(v);
+  if constexpr (SIZE < W) v = bitonic_sort<SIZE * 2, W>(v);
+  return v;
 }
 
 // Bitonic sort of one value per lane, descending, within aligned groups of
@@ -118,28 +170,16 @@ __device__ __forceinline__ int xor_lane(int v, int s) {
 // log2(W) (log2(W) + 1) / 2 compare-exchange steps, all in registers.
 template <int W>
 __device__ __forceinline__ int wave_sort_desc(int v) {
-  const int l = lane();
-#pragma unroll
-  for (int size = 2; size <= W; size <<= 1) {
-#pragma unroll
-    for (int s = size / 2; s > 0; s >>= 1) {
-      const int o = xor_lane(v, s);
-      // The lower lane of a pair keeps the larger value in a run that is
-      // being sorted descending, the smaller in an ascending one.
-      const bool keep_max = ((l & s) == 0) == ((l & size) == 0);
-      v = keep_max ? max(v, o) : min(v, o);
-    }
-  }
-  return v;
+  return bitonic_sort<2, W>(v);
 }
 
 // Append the elements that pass (x[j] > t, or >= t) to buf, one ballot per
 // register slot, at offsets from a wave-uniform count; nothing is written
-// past cap.  Returns the number that pass (it may exceed cap).  Slots
-// past n (when not FULL) never pass: callers use t > INT_MIN, or strict.
+// past kRowCap.  Returns the number that pass (it may exceed kRowCap).
+// Slots past n (when not FULL) never pass: callers use t > INT_MIN, or
+// strict.
 template <int V, bool STRICT>
-__device__ __forceinline__ int compact(const int (&x)[V], int t, int* buf,
-                                       int cap) {
+__device__ __forceinline__ int compact(const int (&x)[V], int t, int* buf) {
   int m = 0;  // wave-uniform
 #pragma unroll
   for (int j = 0; j < V; ++j) {
@@ -147,7 +187,7 @@ __device__ __forceinline__ int compact(const int (&x)[V], int t, int* buf,
     const uint64_t b = ballot(q);
     if (b != 0) {
       const int c = popc(b);
-      if (q && m + c <= cap) buf[m + lanes_below(b)] = x[j];
+      if (q && m + c <= kRowCap) buf[m + lanes_below(b)] = x[j];
       m += c;
     }
   }
@@ -205,8 +245,7 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
 
   // 3. Candidates: elements >= T (T > INT_MIN keeps the padding out); at
   // least k of them, since T is certified.
-  const int m = T > kI32Min ? compact<V, false>(x, T, L.buf, kRowCap)
-                            : kRowCap + 1;
+  const int m = T > kI32Min ? compact<V, false>(x, T, L.buf) : kRowCap + 1;
 
   if (m <= 32) {
     // 4. The usual case: at most 32 candidates, one per lane of the lower
@@ -224,7 +263,7 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
     // elements above g (fewer than k) ranked, then copies of g.
     const int g = unbias(radix_select(bias(row_min()), bias(hi), k,
                                       RowCount<V, FULL>{x, n}));
-    const int ngt = compact<V, true>(x, g, L.buf, kRowCap);
+    const int ngt = compact<V, true>(x, g, L.buf);
     wave_rank_out(L.buf, ngt, k, out);
     for (int j = ngt + lane(); j < k; j += kWave) out[j] = g;
   }
