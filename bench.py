@@ -1,7 +1,8 @@
 """Benchmark: Top-20 over 1e8 int32 on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--path topk|stats|kv|batched|batched_short]
+                    [--path topk|stats|kv|batched|batched_short|hist|
+                            topk_large]
 
 One step is one full library call (both stages; a single kernel launch)
 over a resident synthetic input (seeded SplitMix64).  The default path,
@@ -16,7 +17,11 @@ by position), on the same 1e8 array as `topk`.  `--path batched` and
 the same array viewed as 1000 rows of 100,000 (streaming kernel, one
 workgroup per row) or as 97,656 rows of 1,024 (one wave per row); the same
 run also times topk_merge_i32 merging the rows' lists into the top-20 of
-the whole, reported in `config.merge`.
+the whole, reported in `config.merge`.  `--path hist` measures
+histogram_i32: 256 bins of width 2^24 over the same 1e8 array (its top
+byte, the digit histogram of a radix pass).  `--path topk_large` measures
+topk_i32 with k = 1000 on that array, which takes the radix-selection path
+(several launches per call; the event time covers the whole call).
 
 The input sits in HBM before timing starts.  W untimed calls, then K timed
 back-to-back calls bracketed by device synchronisation and by a pair of HIP
@@ -114,6 +119,36 @@ PATHS = {
         "summary": "topk_batched_1000x100000_k20.md",
         "out_bytes": 4 * K * 1000,
         "oracle_what": "per-row top-20 by copy + std::sort of each row",
+    },
+    "hist": {
+        "metric": ("Histogram (256 bins of width 2^24) over 1e8 int32: "
+                   "elements/s, HBM GB/s as % of 8 TB/s peak"),
+        "workload": "full_1e8",
+        "describe": ("256-bin histogram (bins of width 2^24 from INT32_MIN: "
+                     "the top byte) of 1e8 int32 uniform over the full int32 "
+                     "range (SplitMix64 seed 3), resident in HBM"),
+        "short": "256-bin histogram of 1e8 int32, uniform full range, seed 3",
+        "kernel": "hist_kernel",
+        "sources": ["wave.hpp", "hist_kernel.hpp", "libtopk.hip"],
+        "counters": "hist_counters_full_1e8_256.json",
+        "summary": "hist_full_1e8_256.md",
+        "out_bytes": 8 * 256,
+        "oracle_what": "the 256 counts by one loop",
+    },
+    "topk_large": {
+        "metric": ("Top-1000 over 1e8 int32 (radix selection): elements/s, "
+                   "HBM GB/s as % of 8 TB/s peak"),
+        "workload": "full_1e8",
+        "describe": ("top-1000 of 1e8 int32, uniform over the full int32 "
+                     "range (SplitMix64 seed 3), resident in HBM"),
+        "short": "top-1000 of 1e8 int32, uniform full range, seed 3",
+        "kernel": "hist_kernel",
+        "sources": ["wave.hpp", "hist_kernel.hpp", "libtopk.hip"],
+        "counters": "topk_large_counters_full_1e8_k1000.json",
+        "summary": "topk_large_full_1e8_k1000.md",
+        "out_bytes": 4 * 1000,
+        "oracle_what": "top-1000 by copy + std::sort",
+        "k": 1000,
     },
     "batched_short": {
         "metric": ("Per-row Top-20 over 1e8 int32 as 97,656 rows x 1,024: "
@@ -378,6 +413,16 @@ def main():
 
         def call():
             return ltk.topk_kv(xd, K, out=outs)
+    elif args.path == "hist":
+        out = torch.empty(256, dtype=torch.int64, device=dev)
+
+        def call():
+            return ltk.histogram(xd, -2 ** 31, 24, 256, out=out)
+    elif args.path == "topk_large":
+        out = torch.empty(P["k"], dtype=torch.int32, device=dev)
+
+        def call():
+            return ltk.topk(xd, P["k"], out=out)
     else:
         out = torch.empty(6, dtype=torch.int64, device=dev)
 
@@ -405,9 +450,14 @@ def main():
         want = oracle.topk_batched(x2, K)
         t_rows = time.perf_counter() - t_rows   # the baseline: one call
         ok = np.array_equal(got, want)
-    elif args.path == "topk":
+    elif args.path in ("topk", "topk_large"):
+        kk = P.get("k", K)
         got = call().cpu().numpy()
-        want = oracle.topk(x, K)
+        want = oracle.topk(x, kk)
+        ok = np.array_equal(got, want)
+    elif args.path == "hist":
+        got = call().cpu().numpy()
+        want = oracle.histogram(x, -2 ** 31, 24, 256)
         ok = np.array_equal(got, want)
     elif args.path == "kv":
         gv, gi = call()
@@ -487,8 +537,14 @@ def main():
             t_med, reps = t_rows, 1
             what = "the full workload (%d x %d int32, seed 3)" % (
                 P["rows"], P["cols"])
-        elif args.path == "topk":
-            t_med, reps = time_oracle(lambda: oracle.topk(x, K))
+        elif args.path in ("topk", "topk_large"):
+            kk = P.get("k", K)
+            t_med, reps = time_oracle(lambda: oracle.topk(x, kk))
+            what = "the full workload (1e8 int32, seed 3)"
+        elif args.path == "hist":
+            t_med, reps = time_oracle(
+                lambda: oracle.histogram(x, -2 ** 31, 24, 256), budget_s=10.0,
+                max_reps=50)
             what = "the full workload (1e8 int32, seed 3)"
         elif args.path == "kv":
             t_med, reps = t_kv, 1
@@ -515,6 +571,11 @@ def main():
                        "merge": merge})
     if args.path in ("topk", "kv"):
         config["k"] = K
+    if args.path == "topk_large":
+        config["k"] = P["k"]
+        config["launches_per_call"] = 6
+    if args.path == "hist":
+        config.update({"lo": -2 ** 31, "shift": 24, "nbins": 256})
     if "rows" not in P:
         config["grid"] = ltk.grid_for(n)
     config.update({
