@@ -26,7 +26,9 @@
  *    inside a kernel surfaces at the caller's next synchronisation.
  *  - The library owns a small scratch area per (device, stream), about
  *    1.6 MiB: per-block candidates (1.5 MiB, int32 and key-value), partial
- *    results, histogram counters and tickets.  It is allocated by the
+ *    results, histogram counters and tickets; the first topk_i32 call with
+ *    k > LIBTOPK_MAX_K on the pair adds a 16 MiB candidate buffer.  It is
+ *    allocated by the
  *    first call on that pair (so do that first call before capturing the
  *    stream into a HIP graph), kept for reuse, and freed by
  *    libtopk_release() or at process exit.  Every call leaves it ready for
@@ -84,10 +86,11 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
  * stages run in one launch: the last workgroup to finish stage 1 performs
  * stage 2.  Larger k, up to LIBTOPK_MAX_K_SELECT, goes through radix
  * selection ("GPU基数排序优化：10亿级数据处理与性能调优" §3.2–3.3: 8-bit digit
- * histograms kept per warp in shared memory): up to four digit passes find
- * the k-th largest value, a gather pass collects the values above it, and
- * one workgroup sorts the k results; six stream-ordered launches, reading
- * the input up to five times.
+ * histograms kept per warp in shared memory): four digit passes find the
+ * k-th largest value, a gather pass collects the values above it, and one
+ * workgroup sorts the k results; six stream-ordered launches.  Once a
+ * digit leaves fewer than 2^22 candidates they are copied aside and the
+ * remaining passes read only them, so the input is usually read twice.
  *
  *   in   device, int32[n], read once (k <= LIBTOPK_MAX_K)
  *   n    number of elements, 1 <= n <= 2^32

@@ -21,15 +21,24 @@
 // so no memset is ever enqueued.
 //
 // Radix selection of the k-th largest value g ([Radix] §3.2's digits, used
-// for selection instead of sorting): pass p histograms digit p (bits
+// for selection instead of sorting): pass p counts digit p (bits
 // 31 - 8p .. 24 - 8p of the order-preserving biased value) over the
-// elements whose higher digits equal the prefix chosen so far; the last
-// workgroup picks the digit holding the k-th largest and updates the
-// prefix.  After four passes the prefix is g.  If a pass finds that every
-// element of the chosen bucket is needed, selection stops early.  A gather
-// pass then appends the elements above the bucket (and, when stopped
-// early, the bucket itself) to the output; copies of g fill the rest, and
-// one workgroup sorts the k values in LDS.
+// elements whose higher digits equal the prefix chosen so far (the
+// bucket); the last workgroup picks the digit holding the k-th largest and
+// updates the prefix.  After four passes the prefix is g.  Everything
+// between passes is decided on the device, from a state the last
+// workgroup writes:
+//  * once a pass leaves a bucket of fewer than kCandCap elements, the next
+//    pass over the input also splits it: values above the bucket go
+//    straight to the output (they are all in the top-k), the bucket's
+//    values to a candidate buffer, and the remaining passes read only
+//    that buffer;
+//  * if every element of the chosen bucket is needed, selection stops
+//    early (later passes return at once).
+// A gather pass then appends what is still missing (values above the final
+// bucket, or the whole bucket when selection stopped early) from the input
+// or the candidate buffer, copies of g fill the rest, and one workgroup
+// sorts the k values in LDS.
 #pragma once
 
 #include "wave.hpp"
@@ -41,6 +50,8 @@ constexpr int kWaveHistBins = 256; // per-wave copies up to this many bins
 constexpr int kDigitBins = 256;
 constexpr int kMaxKSelect = 16384; // largest k of the radix-select path
 
+constexpr int kCandCap = 1 << 22;  // candidate buffer, elements
+
 // Selection state in device memory, written by the last workgroup of each
 // pass and read by every workgroup of the next.
 struct RadixState {
@@ -48,21 +59,36 @@ struct RadixState {
   unsigned mask;    // the bits they cover
   int kleft;        // top-k elements still to be found inside the bucket
   int done;         // every element of the bucket is in the top-k
-  unsigned gcount;  // elements appended by the gather pass
+  int bucket;       // elements in the bucket (exact when < kCandCap)
+  int src;          // 0: passes read the input; 1: the candidate buffer
+  int split;        // the next pass over the input splits the bucket off
+  unsigned gcount;  // values appended to the output so far
+  unsigned ccount;  // values appended to the candidate buffer
 };
 
+// histogram_i32: bins of width 2^shift from lo.
 struct HistParams {
   const int* in;
   int64_t n, head, ntiles, covered;
   int grid;
-  // histogram_i32: bins of width 2^shift from lo
   int lo, shift, nbins;
-  int64_t* out;  // [nbins]
-  // radix selection: digit at bit `dshift`; the first pass starts from an
-  // empty prefix and kleft = k instead of reading the state
-  RadixState* st;
-  int dshift, first, k;
+  int64_t* out;             // [nbins]
   unsigned long long* acc;  // [kMaxBins] device counters, zero between calls
+  unsigned* ticket;
+};
+
+// One digit pass of radix selection, or the gather.
+struct SelectParams {
+  const int* in;
+  int64_t n, head, ntiles, covered;
+  int grid;
+  int dshift;   // the digit's lowest bit
+  int first;    // the first pass: start from an empty prefix, kleft = k
+  int k;
+  RadixState* st;
+  int* cand;    // [kCandCap] candidate buffer
+  int* out;     // [k]
+  unsigned long long* acc;  // [256] device counters, zero between calls
   unsigned* ticket;
 };
 
@@ -132,53 +158,15 @@ __device__ __forceinline__ void for_each_element(const int* in, int64_t n,
   }
 }
 
-// The bin of x, or -1 when x is not counted.
-template <bool DIGIT>
-struct Binner {
-  int lo;
-  unsigned shift, nbins;    // range bins
-  unsigned prefix, mask;    // digit bins: elements in the bucket only
-  __device__ __forceinline__ int operator()(int x) const {
-    if (DIGIT) {
-      const unsigned u = bias(x);
-      return (u & mask) == prefix ? (int)((u >> shift) & (kDigitBins - 1))
-                                  : -1;
-    }
-    // x >= lo makes x - lo exact in 32 unsigned bits.
-    const unsigned d = ((unsigned)x - (unsigned)lo) >> shift;
-    return (x >= lo && d < nbins) ? (int)d : -1;
-  }
-};
-
-template <int U, bool DIGIT>
+template <int U>
 __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
   __shared__ unsigned h[kMaxBins];
-  __shared__ int scan[kWaves];
   __shared__ int is_last;
   const int w = threadIdx.x / kWave;
-
-  Binner<DIGIT> bin;
-  int kleft = p.k;
-  if (DIGIT) {
-    unsigned prefix = 0u, mask = 0u;
-    if (!p.first) {
-      const RadixState s = *p.st;
-      if (s.done) return;  // selection already finished: nothing to count
-      prefix = s.prefix;
-      mask = s.mask;
-      kleft = s.kleft;
-    }
-    bin.prefix = prefix;
-    bin.mask = mask;
-    bin.shift = (unsigned)p.dshift;
-  } else {
-    bin.lo = p.lo;
-    bin.shift = (unsigned)p.shift;
-    bin.nbins = (unsigned)p.nbins;
-  }
-  const int nb = DIGIT ? kDigitBins : p.nbins;
-  // Per-wave copies when they fit (fewer same-address collisions), else one.
-  // The copies sit kWaveHistBins apart: clear all of them.
+  const int lo = p.lo, nb = p.nbins;
+  const unsigned shift = (unsigned)p.shift;
+  // Per-wave copies kWaveHistBins apart when they fit (fewer same-address
+  // collisions), else one copy for the workgroup; clear what is used.
   const bool per_wave = nb <= kWaveHistBins;
   const int used = per_wave ? kWaves * kWaveHistBins : nb;
   for (int i = threadIdx.x; i < used; i += kBlock) h[i] = 0u;
@@ -187,8 +175,10 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
 
   for_each_element<U>(p.in, p.n, p.head, p.ntiles, p.covered, p.grid,
                       [&](int x, bool ok) __attribute__((always_inline)) {
-                        const int b = bin(x);
-                        if (ok && b >= 0) atomicAdd(&hw[b], 1u);
+                        // x >= lo makes x - lo exact in 32 unsigned bits.
+                        const unsigned d = ((unsigned)x - (unsigned)lo) >> shift;
+                        if (ok && x >= lo && d < (unsigned)nb)
+                          atomicAdd(&hw[d], 1u);
                       });
   __syncthreads();
 
@@ -203,77 +193,195 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
   }
 
   if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
-
-  if (!DIGIT) {
-    for (int b = threadIdx.x; b < nb; b += kBlock) {
-      p.out[b] = (int64_t)ld_agent(p.acc + b);
-      st_agent(p.acc + b, 0ull);
-    }
-    if (threadIdx.x == 0) st_agent(p.ticket, 0u);
-    return;
+  for (int b = threadIdx.x; b < nb; b += kBlock) {
+    p.out[b] = (int64_t)ld_agent(p.acc + b);
+    st_agent(p.acc + b, 0ull);
   }
+  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
+}
+
+// Append the lanes where q holds to dst at a device counter (one atomic per
+// wave); positions at or past cap are dropped (they never occur while the
+// selection state is sound: the bound only guards the buffers).
+__device__ __forceinline__ void append(bool q, int x, unsigned* counter,
+                                       int* dst, unsigned cap) {
+  const uint64_t b = ballot(q);
+  if (b == 0) return;
+  unsigned base = 0;
+  if (lane() == 0) base = atomicAdd(counter, (unsigned)popc(b));
+  base = uni(base);
+  const unsigned pos = base + (unsigned)lanes_below(b);
+  if (q && pos < cap) dst[pos] = x;
+}
+
+// The elements a selection pass reads: the input, or the candidate buffer
+// (16-byte aligned, `count` elements, no head peel).
+template <int U, class F>
+__device__ __forceinline__ void for_each_source(const SelectParams& p,
+                                                const RadixState& s, F&& f) {
+  if (s.src == 0) {
+    for_each_element<U>(p.in, p.n, p.head, p.ntiles, p.covered, p.grid, f);
+  } else {
+    const int64_t n = s.bucket;
+    const int64_t ntiles = n / ((int64_t)kBlock * U * 4);
+    for_each_element<U>(p.cand, n, 0, ntiles, ntiles * kBlock * U * 4,
+                        p.grid, f);
+  }
+}
+
+// A wave's LDS staging area for the values a split copies to the
+// candidate buffer: the wave appends with ballots (no atomics) and copies a
+// whole batch out with one device atomic when the area is nearly full and
+// at the end, so the shared counter sees about one atomic per wave instead
+// of one per wave and element slot.
+constexpr int kStage = 512;
+
+struct Stager {
+  int* buf;        // this wave's kStage LDS slots
+  int cnt;         // wave-uniform fill level
+  unsigned* counter;
+  int* dst;
+  unsigned cap;    // dst slots; positions past it are dropped (a guard)
+  __device__ __forceinline__ void flush() {
+    if (cnt == 0) return;
+    unsigned base = 0;
+    if (lane() == 0) base = atomicAdd(counter, (unsigned)cnt);
+    base = uni(base);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane(); i < cnt; i += kWave) {
+      const unsigned pos = base + (unsigned)i;
+      if (pos < cap) dst[pos] = buf[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    cnt = 0;
+  }
+  __device__ __forceinline__ void put(bool q, int x) {
+    const uint64_t b = ballot(q);
+    if (b == 0) return;
+    if (q) buf[cnt + lanes_below(b)] = x;
+    cnt += popc(b);
+    if (cnt > kStage - kWave) flush();
+  }
+};
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
+  __shared__ unsigned h[kWaves * kDigitBins];
+  __shared__ int stage[kWaves][kStage];
+  __shared__ int scan[kWaves];
+  __shared__ int is_last;
+  const int w = threadIdx.x / kWave;
+
+  RadixState s;
+  if (p.first) {
+    s.prefix = 0u;
+    s.mask = 0u;
+    s.kleft = p.k;
+    s.done = 0;
+    s.bucket = 0;
+    s.src = 0;
+    s.split = 0;
+    s.gcount = 0u;
+    s.ccount = 0u;
+  } else {
+    s = *p.st;
+    if (s.done) return;  // selection already finished: nothing to count
+  }
+  const bool split = s.split && s.src == 0;
+  for (int i = threadIdx.x; i < kWaves * kDigitBins; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  unsigned* hw = h + w * kDigitBins;
+  const unsigned prefix = s.prefix, mask = s.mask;
+  const unsigned dshift = (unsigned)p.dshift;
+
+  Stager stg{stage[w], 0, &p.st->ccount, p.cand, (unsigned)kCandCap};
+  for_each_source<U>(p, s, [&](int x, bool ok) __attribute__((always_inline)) {
+    const unsigned u = bias(x);
+    const unsigned key = u & mask;
+    // One vote guards the rest: most elements lie below the bucket.
+    const bool ge = ok && key >= prefix;
+    if (ballot(ge) == 0) return;
+    const bool in_bucket = ge && key == prefix;
+    if (in_bucket) atomicAdd(&hw[(u >> dshift) & (kDigitBins - 1)], 1u);
+    if (split) {
+      // Values above the bucket are few (fewer than k): direct appends.
+      append(ge && key > prefix, x, &p.st->gcount, p.out, (unsigned)p.k);
+      stg.put(in_bucket, x);
+    }
+  });
+  if (split) stg.flush();
+  __syncthreads();
+  for (int b = threadIdx.x; b < kDigitBins; b += kBlock) {
+    unsigned c = h[b];
+#pragma unroll
+    for (int j = 1; j < kWaves; ++j) c += h[j * kDigitBins + b];
+    if (c) atomicAdd(p.acc + b, (unsigned long long)c);
+  }
+
+  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
 
   // Pick the digit holding the k-th largest: thread t looks at bin 255 - t,
   // so an inclusive prefix sum over threads is the count of the bucket's
-  // elements at or above that bin.  Counts are capped at 2^20 (> any k),
-  // which keeps the sums in 32 bits and leaves every comparison with kleft
-  // unchanged: the first bin whose capped sum reaches kleft is reached by
-  // exact counts.
+  // elements at or above that bin.  Counts are capped at kCandCap, which
+  // keeps the sums in 32 bits and leaves every comparison with kleft
+  // (<= 16384) unchanged: the first bin whose capped sum reaches kleft is
+  // reached by exact counts.
   const int t = threadIdx.x;
   const int b = kDigitBins - 1 - t;
   const unsigned long long raw = ld_agent(p.acc + b);
   st_agent(p.acc + b, 0ull);
-  const int c = raw > (1ull << 20) ? (1 << 20) : (int)raw;
+  const int c = raw > (unsigned long long)kCandCap ? kCandCap : (int)raw;
   const int incl_w = wave_scan_incl(c);
   if (lane() == kWave - 1) scan[w] = incl_w;
   __syncthreads();
   int incl = incl_w;
   for (int j = 0; j < w; ++j) incl += scan[j];
   const int above = incl - c;
-  if (incl >= kleft && above < kleft) {
-    RadixState s;
-    s.prefix = bin.prefix | ((unsigned)b << p.dshift);
-    s.mask = bin.mask | ((unsigned)(kDigitBins - 1) << p.dshift);
-    s.kleft = kleft - above;
-    s.done = c == s.kleft;  // the whole bucket is needed
-    s.gcount = 0u;
-    *p.st = s;
+  if (incl >= s.kleft && above < s.kleft) {
+    RadixState n = s;
+    n.prefix = prefix | ((unsigned)b << dshift);
+    n.mask = mask | ((unsigned)(kDigitBins - 1) << dshift);
+    n.kleft = s.kleft - above;
+    n.done = c == n.kleft;  // the whole bucket is needed
+    if (split) n.src = 1;   // later passes read the candidate buffer
+    // The candidate buffer holds the bucket chosen before this pass; it
+    // keeps that size (its elements are filtered by prefix from now on).
+    n.bucket = split || s.src == 1 ? s.bucket : c;
+    n.split = !n.done && n.src == 0 && c < kCandCap;
+    // gcount and ccount are left as the pass's appends made them (both
+    // start at 0 with the first pass; only one pass ever splits).
+    p.st->prefix = n.prefix;
+    p.st->mask = n.mask;
+    p.st->kleft = n.kleft;
+    p.st->done = n.done;
+    p.st->bucket = n.bucket;
+    p.st->src = n.src;
+    p.st->split = n.split;
+    if (p.first) {
+      p.st->gcount = 0u;
+      p.st->ccount = 0u;
+    }
   }
   if (t == 0) st_agent(p.ticket, 0u);
 }
 
-struct GatherParams {
-  const int* in;
-  int64_t n, head, ntiles, covered;
-  int grid, k;
-  RadixState* st;
-  int* out;  // [k]
-  unsigned* ticket;
-};
-
-// Append the elements of the top-k that lie above the final bucket (and,
-// when selection stopped early, the bucket itself) to out; the last
-// workgroup fills the remaining slots with copies of g.  Order is
-// arbitrary here; the sort kernel follows.
+// Append what the top-k still misses -- the values above the final bucket
+// (and, when selection stopped early, the bucket itself) -- from the input
+// or the candidate buffer; the last workgroup fills the remaining slots
+// with copies of g.  Order is arbitrary here; the sort kernel follows.
 template <int U>
-__global__ __launch_bounds__(kBlock) void gather_kernel(GatherParams p) {
+__global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
+  __shared__ int stage[kWaves][kStage];
   __shared__ int is_last;
   const RadixState s = *p.st;
-  for_each_element<U>(
-      p.in, p.n, p.head, p.ntiles, p.covered, p.grid,
-      [&](int x, bool ok) __attribute__((always_inline)) {
-        const unsigned key = bias(x) & s.mask;
-        const bool q = ok && (key > s.prefix || (s.done && key == s.prefix));
-        const uint64_t b = ballot(q);
-        if (b == 0) return;
-        unsigned base = 0;
-        if (lane() == 0) base = atomicAdd(&p.st->gcount, (unsigned)popc(b));
-        base = uni(base);
-        // Exactly k - kleft values pass (k when stopped early); the bound
-        // only guards the output against a selection state gone wrong.
-        const unsigned pos = base + (unsigned)lanes_below(b);
-        if (q && pos < (unsigned)p.k) p.out[pos] = x;
-      });
+  const int w = threadIdx.x / kWave;
+  // Staged like the split's copies: one device atomic per wave and batch.
+  Stager stg{stage[w], 0, &p.st->gcount, p.out, (unsigned)p.k};
+  for_each_source<U>(p, s, [&](int x, bool ok) __attribute__((always_inline)) {
+    const unsigned key = bias(x) & s.mask;
+    stg.put(ok && (key > s.prefix || (s.done && key == s.prefix)), x);
+  });
+  stg.flush();
   if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
   if (!s.done) {
     const int g = unbias(s.prefix);

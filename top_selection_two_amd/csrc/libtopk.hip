@@ -48,6 +48,8 @@ struct Scratch {
   unsigned long long* acc = nullptr;  // kMaxBins histogram counters, 0
                                       // between calls
   RadixState* rstate = nullptr;       // radix-selection state
+  int* rcand = nullptr;               // kCandCap candidates, allocated by
+                                      // the first top-k call with k > 128
   unsigned* ticket = nullptr;  // kMaxGrid words (one per row), 0 between calls
 };
 
@@ -266,41 +268,55 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
+// The candidate buffer of radix selection (kCandCap int32), allocated once
+// per (device, stream) on first use.
+int get_rcand(int dev, hipStream_t stream, int** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& sc = g_cache[std::make_pair(dev, (void*)stream)];
+  if (!sc.rcand) {
+    if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
+    void* p = nullptr;
+    const hipError_t e = hipMalloc(&p, (size_t)kCandCap * sizeof(int));
+    if (e != hipSuccess) {
+      debug_hip("hipMalloc(candidates)", e);
+      (void)hipGetLastError();
+      return LIBTOPK_ERR_NOMEM;
+    }
+    sc.rcand = (int*)p;
+  }
+  *out = sc.rcand;
+  return LIBTOPK_OK;
+}
+
 // Top-k for LIBTOPK_MAX_K < k <= LIBTOPK_MAX_K_SELECT: four digit passes of
-// radix selection, a gather pass and a one-workgroup sort, all
+// radix selection (the second of which usually also splits the bucket off
+// into the candidate buffer), a gather pass and a one-workgroup sort, all
 // stream-ordered launches on the caller's stream.
 int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
-                hipStream_t s, const Scratch& sc, const Plan& pl) {
-  HistParams hp = {};
-  hp.in = in;
-  hp.n = n;
-  hp.head = pl.head;
-  hp.ntiles = pl.ntiles;
-  hp.covered = pl.covered;
-  hp.grid = pl.grid;
-  hp.st = sc.rstate;
-  hp.k = k;
-  hp.acc = sc.acc;
-  hp.ticket = sc.ticket;
+                hipStream_t s, int dev, const Scratch& sc, const Plan& pl) {
+  int* rcand = nullptr;
+  int rc = get_rcand(dev, s, &rcand);
+  if (rc != LIBTOPK_OK) return rc;
+  SelectParams sp;
+  sp.in = in;
+  sp.n = n;
+  sp.head = pl.head;
+  sp.ntiles = pl.ntiles;
+  sp.covered = pl.covered;
+  sp.grid = pl.grid;
+  sp.k = k;
+  sp.st = sc.rstate;
+  sp.cand = rcand;
+  sp.out = out;
+  sp.acc = sc.acc;
+  sp.ticket = sc.ticket;
   for (int pass = 0; pass < 4; ++pass) {
-    hp.dshift = 24 - 8 * pass;
-    hp.first = pass == 0;
-    const int rc =
-        launch((const void*)&hist_kernel<kTileVec, true>, pl.grid, hp, s);
+    sp.dshift = 24 - 8 * pass;
+    sp.first = pass == 0;
+    rc = launch((const void*)&select_pass_kernel<kTileVec>, pl.grid, sp, s);
     if (rc != LIBTOPK_OK) return rc;
   }
-  GatherParams gp;
-  gp.in = in;
-  gp.n = n;
-  gp.head = pl.head;
-  gp.ntiles = pl.ntiles;
-  gp.covered = pl.covered;
-  gp.grid = pl.grid;
-  gp.k = k;
-  gp.st = sc.rstate;
-  gp.out = out;
-  gp.ticket = sc.ticket;
-  int rc = launch((const void*)&gather_kernel<kTileVec>, pl.grid, gp, s);
+  rc = launch((const void*)&gather_kernel<kTileVec>, pl.grid, sp, s);
   if (rc != LIBTOPK_OK) return rc;
   void* args[] = {&out, &k};
   const hipError_t e = hipLaunchKernel((const void*)&sort_desc_kernel,
@@ -407,7 +423,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     cus = compute_units(dev);
   }
   const Plan pl = plan(in, n, cus);
-  if (k > LIBTOPK_MAX_K) return topk_select(in, n, k, out, s, sc, pl);
+  if (k > LIBTOPK_MAX_K) return topk_select(in, n, k, out, s, dev, sc, pl);
   TopkParams p;
   p.in = in;
   p.n = n;
@@ -629,7 +645,7 @@ int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
   // n == 0: a one-block launch with nothing to read writes zero counts.
   static const int32_t kDummy = 0;
   const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
-  HistParams p = {};
+  HistParams p;
   p.in = in;
   p.n = n;
   p.head = pl.head;
@@ -642,7 +658,7 @@ int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
   p.out = out;
   p.acc = sc.acc;
   p.ticket = sc.ticket;
-  return launch((const void*)&hist_kernel<kTileVec, false>, pl.grid, p, s);
+  return launch((const void*)&hist_kernel<kTileVec>, pl.grid, p, s);
 }
 
 const char* libtopk_strerror(int status) {
@@ -685,6 +701,7 @@ void libtopk_release(void) {
     if (hipSetDevice(kv.first.first) == hipSuccess) {
       (void)hipDeviceSynchronize();
       (void)hipFree(kv.second.base);
+      if (kv.second.rcand) (void)hipFree(kv.second.rcand);
     }
   }
   g_cache.clear();
