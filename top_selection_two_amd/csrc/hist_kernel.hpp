@@ -391,36 +391,84 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
   if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
-// Sort out[0..k) (k <= kMaxKSelect) descending in one workgroup: the values
-// go to LDS padded with INT_MIN to a power of two, a bitonic network runs
-// over them with a barrier per step, and they are written back.
+// Sort out[0..k) (k <= kMaxKSelect) descending in one workgroup of 1024
+// threads: a bitonic network over m = k rounded up to a power of two (at
+// least 1024; padding INT_MIN).  Thread t holds elements t + 1024 j,
+// j < V = m / 1024, in registers, so a compare-exchange step of distance
+// d costs: d < 64, a lane exchange inside the wave; d >= 1024, a swap
+// between two of the thread's registers; 64 <= d < 1024, a round trip
+// through LDS with two barriers (only these need the workgroup).
 constexpr int kSortThreads = 1024;
+
+template <int V>
+__device__ __forceinline__ void sort_desc_block(int* out, int k, int* lds) {
+  constexpr int m = V * kSortThreads;
+  const int t = threadIdx.x;
+  int v[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = j * kSortThreads + t;
+    v[j] = i < k ? out[i] : kI32Min;
+  }
+  // Keep the max at position i of a pair when i is the lower index of a
+  // pair in a run sorted descending, or the upper in an ascending one.
+  auto keep_max = [](int i, int d, int size) __attribute__((always_inline)) {
+    return ((i & d) == 0) == ((i & size) == 0);
+  };
+  for (int size = 2; size <= m; size <<= 1) {
+    for (int d = size >> 1; d > 0; d >>= 1) {
+      if (d >= kSortThreads) {
+#pragma unroll
+        for (int js = 1; js < V; js <<= 1) {
+          if (d == js * kSortThreads) {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+              if ((j & js) == 0) {
+                const int i = j * kSortThreads + t;
+                const int a = v[j], b = v[j | js];
+                const bool desc = (i & size) == 0;
+                v[j] = desc ? max(a, b) : min(a, b);
+                v[j | js] = desc ? min(a, b) : max(a, b);
+              }
+            }
+          }
+        }
+      } else if (d >= kWave) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) lds[j * kSortThreads + t] = v[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int i = j * kSortThreads + t;
+          const int o = lds[i ^ d];
+          v[j] = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
+        }
+        __syncthreads();
+      } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const int i = j * kSortThreads + t;
+          const int o = __shfl_xor(v[j], d, kWave);
+          v[j] = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = j * kSortThreads + t;
+    if (i < k) out[i] = v[j];
+  }
+}
 
 __global__ __launch_bounds__(kSortThreads) void sort_desc_kernel(int* out,
                                                                  int k) {
-  __shared__ int s[kMaxKSelect];
-  int m = 1;
-  while (m < k) m <<= 1;
-  for (int i = threadIdx.x; i < m; i += kSortThreads)
-    s[i] = i < k ? out[i] : kI32Min;
-  __syncthreads();
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < m / 2; i += kSortThreads) {
-        // The i-th pair: lower index a (bit `stride` clear), partner a + stride.
-        const int a = 2 * i - (i & (stride - 1));
-        const int b2 = a + stride;
-        const int x = s[a], y = s[b2];
-        const bool desc = (a & size) == 0;
-        if (desc ? x < y : x > y) {
-          s[a] = y;
-          s[b2] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = threadIdx.x; i < k; i += kSortThreads) out[i] = s[i];
+  __shared__ int lds[kMaxKSelect];
+  if (k <= kSortThreads) sort_desc_block<1>(out, k, lds);
+  else if (k <= 2 * kSortThreads) sort_desc_block<2>(out, k, lds);
+  else if (k <= 4 * kSortThreads) sort_desc_block<4>(out, k, lds);
+  else if (k <= 8 * kSortThreads) sort_desc_block<8>(out, k, lds);
+  else sort_desc_block<16>(out, k, lds);
 }
 
 }  // namespace ltk
