@@ -212,10 +212,15 @@ def test_repeated_calls_and_two_streams(ltk):
         assert int(s.cpu()[0]) == sums[i]
 
 
-def test_unsupported_k_raises(ltk):
-    x = dev(synth.fill(1, 1000))
+def test_k_limits(ltk):
+    """k up to 128 takes the register lists, 129 .. 16384 radix selection;
+    above that the call is unsupported, and k > n is invalid."""
+    xs = synth.fill(1, 20000)
+    x = dev(xs)
+    assert np.array_equal(ltk.topk(x, 129).cpu().numpy(), oracle.topk(xs, 129))
     with pytest.raises(ltk.LibtopkError) as e:
-        ltk.topk(x, 129)
+        ltk.topk(x, ltk.MAX_K_SELECT + 1)
     assert e.value.status == ltk.ERR_UNSUPPORTED
-    with pytest.raises(ltk.LibtopkError):
-        ltk.topk(x, 1001)
+    with pytest.raises(ltk.LibtopkError) as e:
+        ltk.topk(dev(xs[:1000]), 1001)
+    assert e.value.status == ltk.ERR_INVALID
