@@ -32,7 +32,11 @@ namespace {
 using namespace ltk;
 
 constexpr int kTileVec = 4;         // 16-byte loads per lane per tile (U)
-constexpr int kRefreshPeriod = 8;   // tiles between bound refreshes
+// Tiles between bound refreshes: every 16th for short lists (k <= 32),
+// every 8th for longer ones, whose insertions cost more and profit more
+// from a tighter bound (measured on 1e8 elements: k = 20, 32 faster at 16;
+// k = 64, 100 faster at 8).
+int refresh_period(int k) { return k <= 32 ? 16 : 8; }
 constexpr int64_t kMaxN = (int64_t)1 << 32;
 
 struct Scratch {
@@ -257,7 +261,7 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
   p.covered = pl.covered;
   p.k = k;
   p.grid = pl.grid;
-  p.refresh = kRefreshPeriod;
+  p.refresh = refresh_period(k);
   p.cand = sc.kvcand;
   p.heads = sc.kvheads;
   p.kths = sc.kvkths;
@@ -430,7 +434,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   p.ld = n;  // one row
   p.k = k;
   p.grid = pl.grid;
-  p.refresh = kRefreshPeriod;
+  p.refresh = refresh_period(k);
   p.cand = sc.cand;
   p.heads = sc.heads;
   p.kths = sc.kths;
@@ -575,7 +579,7 @@ int topk_batched_i32(const int32_t* in, int64_t rows, int64_t cols,
   p.ld = ld;
   p.k = k;
   p.grid = gr;
-  p.refresh = kRefreshPeriod;
+  p.refresh = refresh_period(k);
   p.cand = sc.cand;
   p.heads = sc.heads;
   p.kths = sc.kths;

@@ -134,15 +134,22 @@ struct TopkShared {
 // lane threshold.  Lanes whose x does not exceed L[k8-1] leave their list
 // unchanged (and return x).
 //
-// FIT: the capacity is exactly k8, so every slot is used and the bubble has
-// no branches at all.  Otherwise (large k) the slots beyond k8 stay INT_MIN
-// and whole chunks of 8 are skipped with one wave-uniform branch each.
+// The bubble stops early, after any chunk of 8 slots, once no lane carries
+// a value >= `floor`, a certified bound of the workgroup: a value below it
+// is never among the top-k (see the filter in consume), and the value
+// carried down only decreases, so dropping it there loses nothing.  The
+// slots below keep their old, still valid, entries.
+//
+// FIT: the capacity is exactly k8, so every slot is used.  Otherwise (large
+// k) the slots beyond k8 stay INT_MIN and whole chunks of 8 are skipped
+// with one wave-uniform branch each.
 template <int KCAP, bool FIT>
-__device__ __forceinline__ int list_insert(int (&L)[KCAP], int x, int k) {
+__device__ __forceinline__ int list_insert(int (&L)[KCAP], int x, int k,
+                                           int floor) {
   static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
 #pragma unroll
   for (int c = 0; c < KCAP; c += 8) {
-    if (FIT || c < k) {
+    if ((FIT || c < k) && (c == 0 || ballot(x >= floor))) {
 #pragma unroll
       for (int i = c; i < c + 8; ++i) {
         const int lo = min(L[i], x);
@@ -208,7 +215,7 @@ template <int KCAP, bool FIT>
 __device__ __forceinline__ void admit(int (&L)[KCAP], int x, int k, int tsh,
                                       int& thr) {
   if (ballot(x > thr)) {
-    const int evicted = list_insert<KCAP, FIT>(L, x, k);
+    const int evicted = list_insert<KCAP, FIT>(L, x, k, tsh);
     thr = max(thr, max(evicted, tsh));
   }
 }
@@ -254,7 +261,7 @@ __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
     // The threshold may have risen since the element was marked; a lane
     // with nothing to insert inserts INT_MIN, which changes nothing.
     const int x = (pend != 0 && a[0] > thr) ? a[0] : kI32Min;
-    const int evicted = list_insert<KCAP, FIT>(L, x, k);
+    const int evicted = list_insert<KCAP, FIT>(L, x, k, tsh);
     thr = max(thr, max(evicted, tsh));
     pend &= pend - 1;
   } while (ballot(pend != 0));
