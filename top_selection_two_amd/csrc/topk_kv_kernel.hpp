@@ -110,13 +110,18 @@ struct KvList {
 // block's first tile has supplied 4096 keys that beat it (smaller
 // positions, values >= INT_MIN), and k <= 128.  Otherwise (the head and
 // tail elements visited last) whole keys are compared.
+//
+// As in list_insert, the bubble stops after a chunk of 8 slots once no lane
+// carries a value above `tsk` (T - 1 for the certified bound T, see
+// kv_tsk): a key whose value is below T is never among the top-k, and the
+// key carried down only decreases.
 template <int KCAP, bool FIT, bool LANE_ORDER>
 __device__ __forceinline__ void kv_list_insert(KvList<KCAP>& L, int& xv,
-                                               uint32_t& xw, int k) {
+                                               uint32_t& xw, int k, int tsk) {
   static_assert(KCAP % 8 == 0, "list capacity must be a multiple of 8");
 #pragma unroll
   for (int c = 0; c < KCAP; c += 8) {
-    if (FIT || c < k) {
+    if ((FIT || c < k) && (c == 0 || ballot(xv > tsk))) {
 #pragma unroll
       for (int i = c; i < c + 8; ++i) {
         const int lv = L.v[i];
@@ -197,7 +202,7 @@ __device__ __forceinline__ void kv_consume(KvList<KCAP>& L, const v4i (&d)[U],
     const bool act = pend != 0 && a[0] > thr;
     int xv = act ? a[0] : kI32Min;
     uint32_t xw = act ? ~pos : 0u;
-    kv_list_insert<KCAP, FIT, true>(L, xv, xw, k);
+    kv_list_insert<KCAP, FIT, true>(L, xv, xw, k, tsk);
     // An evicted key bounds every later element of this lane (they come at
     // larger positions).
     thr = max(thr, max(xv, tsk));
@@ -659,7 +664,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       if (ballot(q)) {
         int xv = q ? s : kI32Min;
         uint32_t xw = q ? ~(uint32_t)pos : 0u;
-        kv_list_insert<KCAP, FIT, false>(L, xv, xw, k);
+        kv_list_insert<KCAP, FIT, false>(L, xv, xw, k, kv_tsk(tsh));
       }
     }
   }
