@@ -354,6 +354,70 @@ def summarize(run_dir: str, out_dir: str, path: str) -> None:
     print("wrote summaries to", out_dir)
 
 
+BUSY_PASSES = (
+    ("busy", "VALUBusy SALUBusy"),
+    ("insts", "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVES"),
+    ("stall", "MemUnitStalled VALUUtilization"),
+)
+
+
+def busy_commands(path: str):
+    flag = "" if path == "topk" else " --path %s" % path
+    return ["rocprofv3 --pmc %s -d <run>/%s -o %s --output-format csv -- "
+            "python3 bench.py --mode counters%s" % (c, d, d, flag)
+            for d, c in BUSY_PASSES]
+
+
+def summarize_busy(run_dir: str, out_dir: str, path: str) -> None:
+    """Issue counters of the measured kernel (rocprofv3 --pmc, one pass per
+    line of BUSY_PASSES over --mode counters) into a short summary."""
+    import csv
+    import glob
+
+    P = PATHS[path]
+    kern = P["kernel"]
+    n = workload_size(P)
+    vals = {}
+    for d, _ in BUSY_PASSES:
+        files = glob.glob(os.path.join(run_dir, d, "**",
+                                       "*counter_collection.csv"),
+                          recursive=True)
+        if not files:
+            raise SystemExit("missing the %s pass under %s" % (d, run_dir))
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                if kern in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    avg = {c: sum(v) / len(v) for c, v in vals.items()}
+    lines = [
+        "# Issue counters: %s on %s" % (kern, P["short"]),
+        "",
+        "From the repository root, one rocprofv3 pass per line:",
+        "",
+    ] + ["    " + c for c in busy_commands(path)] + [
+        "",
+        "| counter | per dispatch (mean) |",
+        "|---|---|",
+    ]
+    for c in sorted(avg):
+        lines.append("| %s | %.2f |" % (c, avg[c]))
+    if "SQ_INSTS_VALU" in avg:
+        lines += [
+            "",
+            "VALU instructions per input element: %.3f (wave instructions x "
+            "64 lanes / elements: %.2f lane-ops per element)."
+            % (avg["SQ_INSTS_VALU"] / n, avg["SQ_INSTS_VALU"] * 64 / n),
+            "SALU instructions per input element: %.3f."
+            % (avg.get("SQ_INSTS_SALU", 0.0) / n),
+        ]
+    lines.append("")
+    name = P["summary"].replace(".md", "_issue.md")
+    with open(os.path.join(out_dir, name), "w") as f:
+        f.write("\n".join(lines))
+    print("wrote", name)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -391,10 +455,18 @@ def main():
     ap.add_argument("--summarize", metavar="RUN_DIR",
                     help="write profiles/ summaries from rocprofv3 output "
                          "(CPU only)")
+    ap.add_argument("--summarize-busy", metavar="RUN_DIR",
+                    help="write the issue-counter summary (VALUBusy, "
+                         "instructions per element) from rocprofv3 output "
+                         "(CPU only)")
     args = ap.parse_args()
     P = PATHS[args.path]
     if args.summarize:
         summarize(args.summarize, os.path.join(ROOT, "profiles"), args.path)
+        return
+    if args.summarize_busy:
+        summarize_busy(args.summarize_busy, os.path.join(ROOT, "profiles"),
+                       args.path)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
