@@ -64,6 +64,7 @@ struct RadixState {
   int split;        // the next pass over the input splits the bucket off
   unsigned gcount;  // values appended to the output so far
   unsigned ccount;  // values appended to the candidate buffer
+  int guess;        // top digit the first pass copies from (sample kernel)
 };
 
 // histogram_i32: bins of width 2^shift from lo.
@@ -84,6 +85,8 @@ struct SelectParams {
   int grid;
   int dshift;   // the digit's lowest bit
   int first;    // the first pass: start from an empty prefix, kleft = k
+  int use_guess;  // the first pass also copies values whose top digit is
+                  // >= the sampled guess to the candidate buffer
   int k;
   RadixState* st;
   int* cand;    // [kCandCap] candidate buffer
@@ -104,25 +107,20 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
   return v;
 }
 
-// Call f(x, true) for every element this workgroup owns: its round-robin
-// tiles through two alternating register buffers (both always filled, so
-// each tile's wait is for that tile alone), then, in the last workgroup,
-// the unaligned head and the tail, kBlock at a time, where lanes past the
-// end call f(INT_MIN, false) so that f may use wave-wide votes.
-template <int U, class F>
-__device__ __forceinline__ void for_each_element(const int* in, int64_t n,
-                                                 int64_t head, int64_t ntiles,
-                                                 int64_t covered, int grid,
-                                                 F&& f) {
-  const int blk = blockIdx.x;
+// Visit every element this workgroup owns: its round-robin tiles through
+// two alternating register buffers (both always filled, so each tile's
+// wait is for that tile alone), as fv(v4i) per 16-byte vector; then, in
+// the last workgroup, the unaligned head and the tail, kBlock at a time,
+// as fe(x, ok), where lanes past the end pass (INT_MIN, false) so that fe
+// may use wave-wide votes.
+template <int U, class FV, class FE>
+__device__ __forceinline__ void for_each_vector(const int* in, int64_t n,
+                                                int64_t head, int64_t ntiles,
+                                                int64_t covered, int grid,
+                                                int blk, FV&& fv, FE&& fe) {
   auto tile = [&](const v4i (&d)[U]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f(d[u].x, true);
-      f(d[u].y, true);
-      f(d[u].z, true);
-      f(d[u].w, true);
-    }
+    for (int u = 0; u < U; ++u) fv(d[u]);
   };
   const v4i* __restrict__ body = reinterpret_cast<const v4i*>(in + head);
   const int64_t cnt = tiles_of(ntiles, blk, grid);
@@ -153,9 +151,67 @@ __device__ __forceinline__ void for_each_element(const int* in, int64_t n,
     for (int64_t base = 0; base < left; base += kBlock) {
       const int64_t i = base + threadIdx.x;
       const bool ok = i < left;
-      f(ok ? in[i < head ? i : covered + i] : kI32Min, ok);
+      fe(ok ? in[i < head ? i : covered + i] : kI32Min, ok);
     }
   }
+}
+
+// The same with f(x, true) for every element of the tiles too.
+template <int U, class F>
+__device__ __forceinline__ void for_each_element(const int* in, int64_t n,
+                                                 int64_t head, int64_t ntiles,
+                                                 int64_t covered, int grid,
+                                                 F&& f) {
+  for_each_vector<U>(
+      in, n, head, ntiles, covered, grid, (int)blockIdx.x,
+      [&](const v4i& d) __attribute__((always_inline)) {
+        f(d.x, true);
+        f(d.y, true);
+        f(d.z, true);
+        f(d.w, true);
+      },
+      f);
+}
+
+// Device counters are kept in kAccCopies interleaved copies when the
+// histogram is small enough: workgroup b adds into copy b % kAccCopies, so
+// each counter address sees an eighth of the workgroups' atomics (they
+// serialise at the L2), and the last workgroup sums the copies.
+constexpr int kAccCopies = 8;
+
+__device__ __forceinline__ int acc_copies(int nbins) {
+  return nbins * kAccCopies <= kMaxBins ? kAccCopies : 1;
+}
+
+// Add this workgroup's nonzero count for bin b.
+__device__ __forceinline__ void acc_add(unsigned long long* acc, int nbins,
+                                        int b, unsigned c) {
+  if (!c) return;
+  const int copies = acc_copies(nbins);
+  const int copy = copies > 1 ? (int)(blockIdx.x % kAccCopies) : 0;
+  atomicAdd(acc + copy * nbins + b, (unsigned long long)c);
+}
+
+// Read bin b summed over the copies and clear it (last workgroup only).
+// All copies are loaded before any is used, so the device-coherent loads
+// overlap.
+__device__ __forceinline__ unsigned long long acc_take(unsigned long long* acc,
+                                                       int nbins, int b) {
+  if (acc_copies(nbins) == 1) {
+    const unsigned long long t = ld_agent(acc + b);
+    st_agent(acc + b, 0ull);
+    return t;
+  }
+  unsigned long long v[kAccCopies];
+#pragma unroll
+  for (int j = 0; j < kAccCopies; ++j) v[j] = ld_agent(acc + j * nbins + b);
+  unsigned long long t = 0;
+#pragma unroll
+  for (int j = 0; j < kAccCopies; ++j) {
+    t += v[j];
+    st_agent(acc + j * nbins + b, 0ull);
+  }
+  return t;
 }
 
 template <int U>
@@ -189,14 +245,12 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
 #pragma unroll
       for (int j = 1; j < kWaves; ++j) c += h[j * kWaveHistBins + b];
     }
-    if (c) atomicAdd(p.acc + b, (unsigned long long)c);
+    acc_add(p.acc, nb, b, c);
   }
 
   if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
-  for (int b = threadIdx.x; b < nb; b += kBlock) {
-    p.out[b] = (int64_t)ld_agent(p.acc + b);
-    st_agent(p.acc + b, 0ull);
-  }
+  for (int b = threadIdx.x; b < nb; b += kBlock)
+    p.out[b] = (int64_t)acc_take(p.acc, nb, b);
   if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
@@ -214,18 +268,30 @@ __device__ __forceinline__ void append(bool q, int x, unsigned* counter,
   if (q && pos < cap) dst[pos] = x;
 }
 
+// Workgroups that take part in a pass: all of them over the input; over
+// the candidate buffer (16-byte aligned, no head peel) only as many as it
+// has tiles (at least one).  The others return before the ticket.
+template <int U>
+__device__ __forceinline__ int pass_grid(const SelectParams& p,
+                                         const RadixState& s) {
+  if (s.src == 0) return p.grid;
+  const int64_t ntiles = (int64_t)s.bucket / ((int64_t)kBlock * U * 4);
+  return (int)min((int64_t)p.grid, max(ntiles, (int64_t)1));
+}
+
 // The elements a selection pass reads: the input, or the candidate buffer
-// (16-byte aligned, `count` elements, no head peel).
+// (`bucket` elements), spread over pass_grid workgroups.
 template <int U, class F>
 __device__ __forceinline__ void for_each_source(const SelectParams& p,
-                                                const RadixState& s, F&& f) {
+                                                const RadixState& s, int grid,
+                                                F&& f) {
   if (s.src == 0) {
-    for_each_element<U>(p.in, p.n, p.head, p.ntiles, p.covered, p.grid, f);
+    for_each_element<U>(p.in, p.n, p.head, p.ntiles, p.covered, grid, f);
   } else {
     const int64_t n = s.bucket;
     const int64_t ntiles = n / ((int64_t)kBlock * U * 4);
-    for_each_element<U>(p.cand, n, 0, ntiles, ntiles * kBlock * U * 4,
-                        p.grid, f);
+    for_each_element<U>(p.cand, n, 0, ntiles, ntiles * kBlock * U * 4, grid,
+                        f);
   }
 }
 
@@ -288,6 +354,13 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     if (s.done) return;  // selection already finished: nothing to count
   }
   const bool split = s.split && s.src == 0;
+  const int grid = pass_grid<U>(p, s);
+  if ((int)blockIdx.x >= grid) return;
+  // First pass with a sampled guess: copy every value whose top digit is
+  // at or above it (a superset of the top-k when the guess is at most the
+  // digit the pass selects, which the last workgroup checks).
+  const bool pre = p.first && p.use_guess;
+  const unsigned guess = pre ? (unsigned)p.st->guess : 256u;
   for (int i = threadIdx.x; i < kWaves * kDigitBins; i += kBlock) h[i] = 0u;
   __syncthreads();
   unsigned* hw = h + w * kDigitBins;
@@ -295,30 +368,57 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   const unsigned dshift = (unsigned)p.dshift;
 
   Stager stg{stage[w], 0, &p.st->ccount, p.cand, (unsigned)kCandCap};
-  for_each_source<U>(p, s, [&](int x, bool ok) __attribute__((always_inline)) {
-    const unsigned u = bias(x);
-    const unsigned key = u & mask;
-    // One vote guards the rest: most elements lie below the bucket.
-    const bool ge = ok && key >= prefix;
-    if (ballot(ge) == 0) return;
-    const bool in_bucket = ge && key == prefix;
-    if (in_bucket) atomicAdd(&hw[(u >> dshift) & (kDigitBins - 1)], 1u);
-    if (split) {
-      // Values above the bucket are few (fewer than k): direct appends.
-      append(ge && key > prefix, x, &p.st->gcount, p.out, (unsigned)p.k);
-      stg.put(in_bucket, x);
-    }
-  });
-  if (split) stg.flush();
+  if (pre) {
+    // Every element counts in the first pass; copies are rare, so one vote
+    // per 16-byte vector decides whether its four values need a look.
+    auto one = [&](int x, bool ok) __attribute__((always_inline)) {
+      const unsigned u = bias(x);
+      if (ok) atomicAdd(&hw[u >> 24], 1u);
+      stg.put(ok && (u >> 24) >= guess, x);
+    };
+    for_each_vector<U>(
+        p.in, p.n, p.head, p.ntiles, p.covered, grid, (int)blockIdx.x,
+        [&](const v4i& d) __attribute__((always_inline)) {
+          atomicAdd(&hw[bias(d.x) >> 24], 1u);
+          atomicAdd(&hw[bias(d.y) >> 24], 1u);
+          atomicAdd(&hw[bias(d.z) >> 24], 1u);
+          atomicAdd(&hw[bias(d.w) >> 24], 1u);
+          const int m = max(max(d.x, d.y), max(d.z, d.w));
+          if (ballot((bias(m) >> 24) >= guess) == 0) return;
+          stg.put((bias(d.x) >> 24) >= guess, d.x);
+          stg.put((bias(d.y) >> 24) >= guess, d.y);
+          stg.put((bias(d.z) >> 24) >= guess, d.z);
+          stg.put((bias(d.w) >> 24) >= guess, d.w);
+        },
+        one);
+  }
+  if (!pre) {
+    for_each_source<U>(p, s, grid, [&](int x, bool ok)
+                                       __attribute__((always_inline)) {
+      const unsigned u = bias(x);
+      const unsigned key = u & mask;
+      // One vote guards the rest: most elements lie below the bucket.
+      const bool ge = ok && key >= prefix;
+      if (ballot(ge) == 0) return;
+      const bool in_bucket = ge && key == prefix;
+      if (in_bucket) atomicAdd(&hw[(u >> dshift) & (kDigitBins - 1)], 1u);
+      if (split) {
+        // Values above the bucket are few (fewer than k): direct appends.
+        append(ge && key > prefix, x, &p.st->gcount, p.out, (unsigned)p.k);
+        stg.put(in_bucket, x);
+      }
+    });
+  }
+  if (split || pre) stg.flush();
   __syncthreads();
   for (int b = threadIdx.x; b < kDigitBins; b += kBlock) {
     unsigned c = h[b];
 #pragma unroll
     for (int j = 1; j < kWaves; ++j) c += h[j * kDigitBins + b];
-    if (c) atomicAdd(p.acc + b, (unsigned long long)c);
+    acc_add(p.acc, kDigitBins, b, c);
   }
 
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, grid, &is_last)) return;
 
   // Pick the digit holding the k-th largest: thread t looks at bin 255 - t,
   // so an inclusive prefix sum over threads is the count of the bucket's
@@ -328,8 +428,7 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   // reached by exact counts.
   const int t = threadIdx.x;
   const int b = kDigitBins - 1 - t;
-  const unsigned long long raw = ld_agent(p.acc + b);
-  st_agent(p.acc + b, 0ull);
+  const unsigned long long raw = acc_take(p.acc, kDigitBins, b);
   const int c = raw > (unsigned long long)kCandCap ? kCandCap : (int)raw;
   const int incl_w = wave_scan_incl(c);
   if (lane() == kWave - 1) scan[w] = incl_w;
@@ -347,6 +446,15 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     // The candidate buffer holds the bucket chosen before this pass; it
     // keeps that size (its elements are filtered by prefix from now on).
     n.bucket = split || s.src == 1 ? s.bucket : c;
+    if (pre) {
+      // The copy holds every value of top digit >= guess; it covers the
+      // top-k if the chosen digit is >= guess, and is whole if it fit.
+      const unsigned copied = ld_agent(&p.st->ccount);
+      if ((unsigned)b >= guess && copied <= (unsigned)kCandCap) {
+        n.src = 1;
+        n.bucket = (int)copied;
+      }
+    }
     n.split = !n.done && n.src == 0 && c < kCandCap;
     // gcount and ccount are left as the pass's appends made them (both
     // start at 0 with the first pass; only one pass ever splits).
@@ -365,6 +473,73 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   if (t == 0) st_agent(p.ticket, 0u);
 }
 
+// The sampled guess of the first digit for top-k with large n: S values
+// spread evenly over the input (U 16-byte vectors per thread, `stride`
+// vectors apart) are counted by top digit, and the last workgroup picks the
+// largest digit d such that at least `need` sampled values have a top digit
+// >= d (need covers k scaled to the sample with a wide margin).  The guess
+// only decides what the first pass copies aside; a wrong guess costs time,
+// never correctness.
+struct SampleParams {
+  const v4i* body;   // the 16-byte-aligned body of the input
+  int64_t nvec;      // vectors in it
+  int64_t stride;    // vectors between consecutive samples
+  int need;
+  RadixState* st;
+  unsigned long long* acc;  // [256] device counters, zero between calls
+  unsigned* ticket;
+  int grid;
+};
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void sample_kernel(SampleParams p) {
+  __shared__ unsigned h[kWaves * kDigitBins];
+  __shared__ int scan[kWaves];
+  __shared__ int is_last;
+  const int w = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kWaves * kDigitBins; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  unsigned* hw = h + w * kDigitBins;
+  const int64_t first =
+      ((int64_t)blockIdx.x * kBlock + threadIdx.x) * U;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t v = (first + u) * p.stride;
+    if (v < p.nvec) {
+      const v4i d = __builtin_nontemporal_load(p.body + v);
+      atomicAdd(&hw[bias(d.x) >> 24], 1u);
+      atomicAdd(&hw[bias(d.y) >> 24], 1u);
+      atomicAdd(&hw[bias(d.z) >> 24], 1u);
+      atomicAdd(&hw[bias(d.w) >> 24], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kDigitBins; b += kBlock) {
+    unsigned c = h[b];
+#pragma unroll
+    for (int j = 1; j < kWaves; ++j) c += h[j * kDigitBins + b];
+    acc_add(p.acc, kDigitBins, b, c);
+  }
+  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  // Suffix counts over digits, as in the selection passes.
+  const int t = threadIdx.x;
+  const int b = kDigitBins - 1 - t;
+  const unsigned long long raw = acc_take(p.acc, kDigitBins, b);
+  const int c = raw > (unsigned long long)kCandCap ? kCandCap : (int)raw;
+  const int incl_w = wave_scan_incl(c);
+  if (lane() == kWave - 1) scan[w] = incl_w;
+  __syncthreads();
+  int incl = incl_w;
+  for (int j = 0; j < w; ++j) incl += scan[j];
+  // The largest digit whose suffix reaches `need`; digit 0 if none does.
+  if ((incl >= p.need && incl - c < p.need) || (b == 0 && incl < p.need))
+    p.st->guess = b;
+  if (t == 0) {
+    p.st->ccount = 0u;
+    st_agent(p.ticket, 0u);
+  }
+}
+
 // Append what the top-k still misses -- the values above the final bucket
 // (and, when selection stopped early, the bucket itself) -- from the input
 // or the candidate buffer; the last workgroup fills the remaining slots
@@ -376,13 +551,16 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
   const RadixState s = *p.st;
   const int w = threadIdx.x / kWave;
   // Staged like the split's copies: one device atomic per wave and batch.
+  const int grid = pass_grid<U>(p, s);
+  if ((int)blockIdx.x >= grid) return;
   Stager stg{stage[w], 0, &p.st->gcount, p.out, (unsigned)p.k};
-  for_each_source<U>(p, s, [&](int x, bool ok) __attribute__((always_inline)) {
+  for_each_source<U>(p, s, grid, [&](int x, bool ok)
+                                     __attribute__((always_inline)) {
     const unsigned key = bias(x) & s.mask;
     stg.put(ok && (key > s.prefix || (s.done && key == s.prefix)), x);
   });
   stg.flush();
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, grid, &is_last)) return;
   if (!s.done) {
     const int g = unbias(s.prefix);
     for (int j = p.k - s.kleft + (int)threadIdx.x; j < p.k; j += kBlock)

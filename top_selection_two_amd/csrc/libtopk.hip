@@ -272,6 +272,9 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
+// Inputs from this size on are sampled for a first-digit guess.
+constexpr int64_t kSampleMinN = (int64_t)1 << 24;
+
 // The candidate buffer of radix selection (kCandCap int32), allocated once
 // per (device, stream) on first use.
 int get_rcand(int dev, hipStream_t stream, int** out) {
@@ -314,6 +317,31 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   sp.out = out;
   sp.acc = sc.acc;
   sp.ticket = sc.ticket;
+  sp.use_guess = 0;
+  // Large inputs: sample 2^18 values for a first-digit guess, so that
+  // the first pass can copy the candidates aside and no later pass reads
+  // the input again.
+  const int64_t nvec = (n - pl.head) / 4;
+  if (n >= kSampleMinN && nvec > 0) {
+    constexpr int kSampleU = 1, kSampleGrid = 256;
+    const int64_t nsamp = (int64_t)kSampleGrid * kBlock * kSampleU;
+    SampleParams q;
+    q.body = reinterpret_cast<const v4i*>(in + pl.head);
+    q.nvec = nvec;
+    q.stride = nvec / nsamp > 0 ? nvec / nsamp : 1;
+    // 4x the sampled share of k, plus 64: the guess stays far below the
+    // digit of the k-th largest unless the data is strongly skewed.
+    const int64_t sampled = 4 * (nvec / q.stride < nsamp ? nvec / q.stride
+                                                         : nsamp);
+    q.need = (int)(4 * (int64_t)k * sampled / n + 64);
+    q.st = sc.rstate;
+    q.acc = sc.acc;
+    q.ticket = sc.ticket;
+    q.grid = kSampleGrid;
+    rc = launch((const void*)&sample_kernel<kSampleU>, kSampleGrid, q, s);
+    if (rc != LIBTOPK_OK) return rc;
+    sp.use_guess = 1;
+  }
   for (int pass = 0; pass < 4; ++pass) {
     sp.dshift = 24 - 8 * pass;
     sp.first = pass == 0;
