@@ -142,18 +142,21 @@ PATHS = {
         "describe": ("top-1000 of 1e8 int32, uniform over the full int32 "
                      "range (SplitMix64 seed 3), resident in HBM"),
         "short": "top-1000 of 1e8 int32, uniform full range, seed 3",
-        "kernel": "select_pass_kernel",
+        "kernel": "filter_kernel",
         "sources": ["wave.hpp", "hist_kernel.hpp", "libtopk.hip"],
         "counters": "topk_large_counters_full_1e8_k1000.json",
         "summary": "topk_large_full_1e8_k1000.md",
         "out_bytes": 4 * 1000,
         "oracle_what": "top-1000 by copy + std::sort",
         "k": 1000,
-        # One call is six launches: four selection passes, the gather and
-        # the sort (once per call); summaries are per call.
-        "call_kernels": ["select_pass_kernel", "gather_kernel",
-                         "sort_desc_kernel"],
-        "once_per_call": "sort_desc_kernel",
+        # One call is eight launches: the sample, the filter pass, four
+        # selection passes and the gather (these return at once after a
+        # small filter copy) and the finish kernel (once per call);
+        # summaries are per call.
+        "call_kernels": ["sample_kernel", "filter_kernel",
+                         "select_pass_kernel", "gather_kernel",
+                         "select_finish_kernel"],
+        "once_per_call": "select_finish_kernel",
     },
     "batched_short": {
         "metric": ("Per-row Top-20 over 1e8 int32 as 97,656 rows x 1,024: "
@@ -670,7 +673,7 @@ def main():
         config["k"] = K
     if args.path == "topk_large":
         config["k"] = P["k"]
-        config["launches_per_call"] = 6
+        config["launches_per_call"] = 8
     if args.path == "hist":
         config.update({"lo": -2 ** 31, "shift": 24, "nbins": 256})
     if "rows" not in P:

@@ -51,6 +51,9 @@ constexpr int kDigitBins = 256;
 constexpr int kMaxKSelect = 16384; // largest k of the radix-select path
 
 constexpr int kCandCap = 1 << 22;  // candidate buffer, elements
+// Candidates one workgroup selects from after the filter pass; larger
+// copies go through the multi-workgroup selection passes.
+constexpr int kFinishMax = 1 << 20;
 
 // Selection state in device memory, written by the last workgroup of each
 // pass and read by every workgroup of the next.
@@ -64,7 +67,9 @@ struct RadixState {
   int split;        // the next pass over the input splits the bucket off
   unsigned gcount;  // values appended to the output so far
   unsigned ccount;  // values appended to the candidate buffer
-  int guess;        // top digit the first pass copies from (sample kernel)
+  int thresh;       // sampled threshold of the filter pass
+  int fast;         // the filter's copy is small: one workgroup finishes
+  unsigned eqcount; // values equal to the threshold (filter pass)
 };
 
 // histogram_i32: bins of width 2^shift from lo.
@@ -85,8 +90,6 @@ struct SelectParams {
   int grid;
   int dshift;   // the digit's lowest bit
   int first;    // the first pass: start from an empty prefix, kleft = k
-  int use_guess;  // the first pass also copies values whose top digit is
-                  // >= the sampled guess to the candidate buffer
   int k;
   RadixState* st;
   int* cand;    // [kCandCap] candidate buffer
@@ -351,16 +354,12 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     s.ccount = 0u;
   } else {
     s = *p.st;
-    if (s.done) return;  // selection already finished: nothing to count
+    // Selection already finished, or left to the finish kernel.
+    if (s.done || s.fast) return;
   }
   const bool split = s.split && s.src == 0;
   const int grid = pass_grid<U>(p, s);
   if ((int)blockIdx.x >= grid) return;
-  // First pass with a sampled guess: copy every value whose top digit is
-  // at or above it (a superset of the top-k when the guess is at most the
-  // digit the pass selects, which the last workgroup checks).
-  const bool pre = p.first && p.use_guess;
-  const unsigned guess = pre ? (unsigned)p.st->guess : 256u;
   for (int i = threadIdx.x; i < kWaves * kDigitBins; i += kBlock) h[i] = 0u;
   __syncthreads();
   unsigned* hw = h + w * kDigitBins;
@@ -368,48 +367,22 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   const unsigned dshift = (unsigned)p.dshift;
 
   Stager stg{stage[w], 0, &p.st->ccount, p.cand, (unsigned)kCandCap};
-  if (pre) {
-    // Every element counts in the first pass; copies are rare, so one vote
-    // per 16-byte vector decides whether its four values need a look.
-    auto one = [&](int x, bool ok) __attribute__((always_inline)) {
-      const unsigned u = bias(x);
-      if (ok) atomicAdd(&hw[u >> 24], 1u);
-      stg.put(ok && (u >> 24) >= guess, x);
-    };
-    for_each_vector<U>(
-        p.in, p.n, p.head, p.ntiles, p.covered, grid, (int)blockIdx.x,
-        [&](const v4i& d) __attribute__((always_inline)) {
-          atomicAdd(&hw[bias(d.x) >> 24], 1u);
-          atomicAdd(&hw[bias(d.y) >> 24], 1u);
-          atomicAdd(&hw[bias(d.z) >> 24], 1u);
-          atomicAdd(&hw[bias(d.w) >> 24], 1u);
-          const int m = max(max(d.x, d.y), max(d.z, d.w));
-          if (ballot((bias(m) >> 24) >= guess) == 0) return;
-          stg.put((bias(d.x) >> 24) >= guess, d.x);
-          stg.put((bias(d.y) >> 24) >= guess, d.y);
-          stg.put((bias(d.z) >> 24) >= guess, d.z);
-          stg.put((bias(d.w) >> 24) >= guess, d.w);
-        },
-        one);
-  }
-  if (!pre) {
-    for_each_source<U>(p, s, grid, [&](int x, bool ok)
-                                       __attribute__((always_inline)) {
-      const unsigned u = bias(x);
-      const unsigned key = u & mask;
-      // One vote guards the rest: most elements lie below the bucket.
-      const bool ge = ok && key >= prefix;
-      if (ballot(ge) == 0) return;
-      const bool in_bucket = ge && key == prefix;
-      if (in_bucket) atomicAdd(&hw[(u >> dshift) & (kDigitBins - 1)], 1u);
-      if (split) {
-        // Values above the bucket are few (fewer than k): direct appends.
-        append(ge && key > prefix, x, &p.st->gcount, p.out, (unsigned)p.k);
-        stg.put(in_bucket, x);
-      }
-    });
-  }
-  if (split || pre) stg.flush();
+  for_each_source<U>(p, s, grid, [&](int x, bool ok)
+                                     __attribute__((always_inline)) {
+    const unsigned u = bias(x);
+    const unsigned key = u & mask;
+    // One vote guards the rest: most elements lie below the bucket.
+    const bool ge = ok && key >= prefix;
+    if (ballot(ge) == 0) return;
+    const bool in_bucket = ge && key == prefix;
+    if (in_bucket) atomicAdd(&hw[(u >> dshift) & (kDigitBins - 1)], 1u);
+    if (split) {
+      // Values above the bucket are few (fewer than k): direct appends.
+      append(ge && key > prefix, x, &p.st->gcount, p.out, (unsigned)p.k);
+      stg.put(in_bucket, x);
+    }
+  });
+  if (split) stg.flush();
   __syncthreads();
   for (int b = threadIdx.x; b < kDigitBins; b += kBlock) {
     unsigned c = h[b];
@@ -446,15 +419,6 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     // The candidate buffer holds the bucket chosen before this pass; it
     // keeps that size (its elements are filtered by prefix from now on).
     n.bucket = split || s.src == 1 ? s.bucket : c;
-    if (pre) {
-      // The copy holds every value of top digit >= guess; it covers the
-      // top-k if the chosen digit is >= guess, and is whole if it fit.
-      const unsigned copied = ld_agent(&p.st->ccount);
-      if ((unsigned)b >= guess && copied <= (unsigned)kCandCap) {
-        n.src = 1;
-        n.bucket = (int)copied;
-      }
-    }
     n.split = !n.done && n.src == 0 && c < kCandCap;
     // gcount and ccount are left as the pass's appends made them (both
     // start at 0 with the first pass; only one pass ever splits).
@@ -468,74 +432,259 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     if (p.first) {
       p.st->gcount = 0u;
       p.st->ccount = 0u;
+      p.st->fast = 0;
     }
   }
   if (t == 0) st_agent(p.ticket, 0u);
 }
 
-// The sampled guess of the first digit for top-k with large n: S values
-// spread evenly over the input (U 16-byte vectors per thread, `stride`
-// vectors apart) are counted by top digit, and the last workgroup picks the
-// largest digit d such that at least `need` sampled values have a top digit
-// >= d (need covers k scaled to the sample with a wide margin).  The guess
-// only decides what the first pass copies aside; a wrong guess costs time,
-// never correctness.
+// The filter threshold for top-k with large n.  kSampleGrid workgroups
+// read S = kSampleVecs 16-byte vectors spread evenly over the input (one
+// per thread); t is to be the value of rank `need` among the S * 4 sampled
+// values (`need` is k scaled to the sample, with a wide margin).  Each
+// workgroup finds the value of rank `need` among its own samples and
+// publishes its `need` largest; the last workgroup finds the value of rank
+// `need` in the union of those lists, which is that of the whole sample.
+// Both use block_rank: three histogram levels in LDS (the top 12 bits of
+// the biased value, the next 12, the last 8).  The filter pass then copies
+// every value above t aside and counts those equal to it: when at least k
+// values are >= t, the top-k lies among them, whatever t is, so a poor
+// sample costs time, never correctness.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleGrid = 16;
+constexpr int kSampleVecs = kSampleThreads * kSampleGrid;
+constexpr int kSampleVals = 4 * kSampleVecs;
+constexpr int kNeedMax = 256;     // largest `need`
+constexpr int kThreshBins = 4096;
+
 struct SampleParams {
   const v4i* body;   // the 16-byte-aligned body of the input
   int64_t nvec;      // vectors in it
   int64_t stride;    // vectors between consecutive samples
-  int need;
+  int need;          // 1 <= need <= kNeedMax
   RadixState* st;
-  unsigned long long* acc;  // [256] device counters, zero between calls
+  int* samp;         // [kSampleGrid * kNeedMax] the published lists
   unsigned* ticket;
-  int grid;
 };
 
-template <int U>
-__global__ __launch_bounds__(kBlock) void sample_kernel(SampleParams p) {
-  __shared__ unsigned h[kWaves * kDigitBins];
-  __shared__ int scan[kWaves];
-  __shared__ int is_last;
-  const int w = threadIdx.x / kWave;
-  for (int i = threadIdx.x; i < kWaves * kDigitBins; i += kBlock) h[i] = 0u;
-  __syncthreads();
-  unsigned* hw = h + w * kDigitBins;
-  const int64_t first =
-      ((int64_t)blockIdx.x * kBlock + threadIdx.x) * U;
+struct RankShared {
+  unsigned h[kThreshBins];
+  int scan[kSampleThreads / kWave];
+  int pick[2];
+  int cnt;
+  int is_last;
+};
+
+// Thread t owns bins kThreshBins - 1 - 4t - i, i < 4 (top bin first); find
+// the highest bin whose suffix count reaches `need` (bin 0 if none does)
+// and the count above it.  h is cleared on the way.
+__device__ __forceinline__ void sample_pick(RankShared& sh, int need) {
+  constexpr int kPer = kThreshBins / kSampleThreads;
+  const int t = threadIdx.x, w = t / kWave;
+  int c[kPer], local = 0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t v = (first + u) * p.stride;
-    if (v < p.nvec) {
-      const v4i d = __builtin_nontemporal_load(p.body + v);
-      atomicAdd(&hw[bias(d.x) >> 24], 1u);
-      atomicAdd(&hw[bias(d.y) >> 24], 1u);
-      atomicAdd(&hw[bias(d.z) >> 24], 1u);
-      atomicAdd(&hw[bias(d.w) >> 24], 1u);
+  for (int i = 0; i < kPer; ++i) {
+    c[i] = (int)sh.h[kThreshBins - 1 - kPer * t - i];
+    local += c[i];
+  }
+  const int incl_w = wave_scan_incl(local);
+  if (lane() == kWave - 1) sh.scan[w] = incl_w;
+  __syncthreads();
+  int run = incl_w - local;
+  for (int j = 0; j < w; ++j) run += sh.scan[j];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int b = kThreshBins - 1 - kPer * t - i;
+    const int before = run;
+    run += c[i];
+    if ((run >= need && before < need) || (b == 0 && run < need)) {
+      sh.pick[0] = b;
+      sh.pick[1] = before;
+    }
+    sh.h[b] = 0u;
+  }
+  __syncthreads();
+}
+
+// The biased value v of rank `need` (1 = the largest) among the PER values
+// each thread of the workgroup holds (slot j only where bit j of `valid`
+// is set), and in *above the number of values greater than v.  There are
+// at least `need` valid values.  sh.h is zero on entry and on return.
+template <int PER>
+__device__ __forceinline__ unsigned block_rank(const unsigned (&u)[PER],
+                                               unsigned valid, int need,
+                                               RankShared& sh, int* above) {
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (valid & (1u << j)) atomicAdd(&sh.h[u[j] >> 20], 1u);
+  __syncthreads();
+  sample_pick(sh, need);
+  const unsigned b1 = (unsigned)sh.pick[0];
+  int a = sh.pick[1];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if ((valid & (1u << j)) && (u[j] >> 20) == b1)
+      atomicAdd(&sh.h[(u[j] >> 8) & 0xfffu], 1u);
+  __syncthreads();
+  sample_pick(sh, need - a);
+  const unsigned b12 = (b1 << 12) | (unsigned)sh.pick[0];
+  a += sh.pick[1];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if ((valid & (1u << j)) && (u[j] >> 8) == b12)
+      atomicAdd(&sh.h[u[j] & 0xffu], 1u);
+  __syncthreads();
+  sample_pick(sh, need - a);
+  const unsigned v = (b12 << 8) | (unsigned)sh.pick[0];
+  *above = a + sh.pick[1];
+  return v;
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
+  __shared__ RankShared sh;
+  const int t = threadIdx.x;
+  for (int i = t; i < kThreshBins; i += kSampleThreads) sh.h[i] = 0u;
+  if (t == 0) sh.cnt = 0;
+  unsigned u[4];
+  {
+    const int64_t v = ((int64_t)blockIdx.x * kSampleThreads + t) * p.stride;
+    // Vectors past the end (none while S * stride <= nvec) count as
+    // INT_MIN, never above a real threshold's rank.
+    const v4i d = v < p.nvec ? __builtin_nontemporal_load(p.body + v)
+                             : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
+    u[0] = bias(d.x);
+    u[1] = bias(d.y);
+    u[2] = bias(d.z);
+    u[3] = bias(d.w);
+  }
+  __syncthreads();
+  int a;
+  const unsigned v = block_rank<4>(u, 0xfu, p.need, sh, &a);
+  // Publish this workgroup's `need` largest: the a values above v (one
+  // LDS atomic per wave and slot), then need - a copies of v.
+  int* mine = p.samp + blockIdx.x * kNeedMax;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool q = u[j] > v;
+    const uint64_t b = ballot(q);
+    if (b == 0) continue;
+    int base = 0;
+    if (lane() == 0) base = atomicAdd(&sh.cnt, popc(b));
+    base = uni(base);
+    const int pos = base + lanes_below(b);
+    if (q && pos < kNeedMax) st_agent(mine + pos, (int)u[j]);
+  }
+  for (int i = a + t; i < p.need; i += kSampleThreads) st_agent(mine + i, (int)v);
+  if (!last_to_finish(p.ticket, kSampleGrid, &sh.is_last)) return;
+
+  // The union of the lists: kSampleGrid * need <= 4 * kSampleThreads
+  // values.
+  unsigned w[4], valid = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = j * kSampleThreads + t;
+    const int g = i / p.need, r = i - g * p.need;
+    w[j] = 0u;
+    if (g < kSampleGrid) {
+      w[j] = (unsigned)ld_agent(p.samp + g * kNeedMax + r);
+      valid |= 1u << j;
     }
   }
+  int a2;
+  const unsigned tv = block_rank<4>(w, valid, p.need, sh, &a2);
+  if (t == 0) {
+    p.st->thresh = unbias(tv);
+    p.st->ccount = 0u;
+    p.st->eqcount = 0u;
+    st_agent(p.ticket, 0u);
+  }
+}
+
+// Copy every value above the sampled threshold t to the candidate buffer
+// (one vote per 16-byte vector, staged appends) and count the values
+// equal to t, then let the last workgroup decide, with gt values copied
+// and eq equal to t:
+//  * gt + eq >= k and gt <= kFinishMax: the top-k is the top-k of the
+//    copy, completed with copies of t when gt < k; the finish kernel
+//    selects it alone (fast);
+//  * otherwise gt >= k and the copy holds all of them: the selection
+//    passes read the copy;
+//  * otherwise they read the input.
+// Either way it writes the state the selection starts from.
+// What the waves still hold at the end goes out with one device atomic per
+// workgroup, not per wave: a stream's end puts every wave's last flush on
+// the one counter at about the same time.
+__device__ __forceinline__ void flush_block(Stager& stg, int (*stage)[kStage],
+                                            int* wcnt) {
+  const int w = threadIdx.x / kWave;
+  if (lane() == 0) wcnt[w] = stg.cnt;
   __syncthreads();
-  for (int b = threadIdx.x; b < kDigitBins; b += kBlock) {
-    unsigned c = h[b];
-#pragma unroll
-    for (int j = 1; j < kWaves; ++j) c += h[j * kDigitBins + b];
-    acc_add(p.acc, kDigitBins, b, c);
+  if (threadIdx.x == 0) {
+    int total = 0;
+    for (int j = 0; j < kWaves; ++j) total += wcnt[j];
+    wcnt[kWaves] = total ? (int)atomicAdd(stg.counter, (unsigned)total) : 0;
+  }
+  __syncthreads();
+  unsigned base = (unsigned)wcnt[kWaves];
+  for (int j = 0; j < w; ++j) base += (unsigned)wcnt[j];
+  for (int i = lane(); i < stg.cnt; i += kWave) {
+    const unsigned pos = base + (unsigned)i;
+    if (pos < stg.cap) stg.dst[pos] = stage[w][i];
+  }
+  stg.cnt = 0;
+}
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void filter_kernel(SelectParams p) {
+  __shared__ int stage[kWaves][kStage];
+  __shared__ int wcnt[kWaves + 1];
+  __shared__ unsigned weq[kWaves];
+  __shared__ int is_last;
+  const int w = threadIdx.x / kWave;
+  const int t = p.st->thresh;
+  Stager stg{stage[w], 0, &p.st->ccount, p.cand, (unsigned)kCandCap};
+  unsigned eq = 0;  // wave-uniform count of values equal to t
+  auto one = [&](int x, bool ok) __attribute__((always_inline)) {
+    stg.put(ok && x > t, x);
+    eq += (unsigned)popc(ballot(ok && x == t));
+  };
+  for_each_vector<U>(
+      p.in, p.n, p.head, p.ntiles, p.covered, p.grid, (int)blockIdx.x,
+      [&](const v4i& d) __attribute__((always_inline)) {
+        if (ballot(max(max(d.x, d.y), max(d.z, d.w)) >= t) == 0) return;
+        one(d.x, true);
+        one(d.y, true);
+        one(d.z, true);
+        one(d.w, true);
+      },
+      one);
+  flush_block(stg, stage, wcnt);
+  if (lane() == 0) weq[w] = eq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned e = 0;
+    for (int j = 0; j < kWaves; ++j) e += weq[j];
+    if (e) atomicAdd(&p.st->eqcount, e);
   }
   if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
-  // Suffix counts over digits, as in the selection passes.
-  const int t = threadIdx.x;
-  const int b = kDigitBins - 1 - t;
-  const unsigned long long raw = acc_take(p.acc, kDigitBins, b);
-  const int c = raw > (unsigned long long)kCandCap ? kCandCap : (int)raw;
-  const int incl_w = wave_scan_incl(c);
-  if (lane() == kWave - 1) scan[w] = incl_w;
-  __syncthreads();
-  int incl = incl_w;
-  for (int j = 0; j < w; ++j) incl += scan[j];
-  // The largest digit whose suffix reaches `need`; digit 0 if none does.
-  if ((incl >= p.need && incl - c < p.need) || (b == 0 && incl < p.need))
-    p.st->guess = b;
-  if (t == 0) {
-    p.st->ccount = 0u;
+  if (threadIdx.x == 0) {
+    const unsigned gt = ld_agent(&p.st->ccount);
+    const unsigned eqs = ld_agent(&p.st->eqcount);
+    const unsigned k = (unsigned)p.k;
+    const bool fast = gt <= (unsigned)kFinishMax && (gt >= k || eqs >= k - gt);
+    const bool copy = !fast && gt >= k && gt <= (unsigned)kCandCap;
+    RadixState& s = *p.st;
+    s.prefix = 0u;
+    s.mask = 0u;
+    s.kleft = p.k;
+    s.done = 0;
+    s.bucket = fast || copy ? (int)gt : 0;
+    s.src = copy ? 1 : 0;
+    s.split = 0;
+    s.gcount = 0u;
+    s.ccount = 0u;
+    s.eqcount = 0u;
+    s.fast = fast;
     st_agent(p.ticket, 0u);
   }
 }
@@ -549,6 +698,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
   __shared__ int stage[kWaves][kStage];
   __shared__ int is_last;
   const RadixState s = *p.st;
+  if (s.fast) return;  // the finish kernel gathers from its own copy
   const int w = threadIdx.x / kWave;
   // Staged like the split's copies: one device atomic per wave and batch.
   const int grid = pass_grid<U>(p, s);
@@ -569,32 +719,39 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
   if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
-// Sort out[0..k) (k <= kMaxKSelect) descending in one workgroup of 1024
-// threads: a bitonic network over m = k rounded up to a power of two (at
-// least 1024; padding INT_MIN).  Thread t holds elements t + 1024 j,
-// j < V = m / 1024, in registers, so a compare-exchange step of distance
-// d costs: d < 64, a lane exchange inside the wave; d >= 1024, a swap
-// between two of the thread's registers; 64 <= d < 1024, a round trip
-// through LDS with two barriers (only these need the workgroup).
+// Sort src[0..k) (k <= kMaxKSelect) descending into dst[0..k) in one
+// workgroup of 1024 threads (src may be lds, and dst src): a bitonic
+// network over m = k rounded up to a power of two (at least 1024; padding
+// INT_MIN).  Thread t holds elements t + 1024 j, j < V = m / 1024, in
+// registers, so a compare-exchange step of distance d costs: d < 64, a
+// lane exchange inside the wave (DPP and row swaps, in registers); d >=
+// 1024, a swap between two of the thread's registers; 64 <= d < 1024, a
+// round trip through LDS with two barriers (only these need the
+// workgroup).
 constexpr int kSortThreads = 1024;
 
 template <int V>
-__device__ __forceinline__ void sort_desc_block(int* out, int k, int* lds) {
+__device__ __forceinline__ void sort_desc_block(const int* src, int* dst,
+                                                int k, int* lds) {
   constexpr int m = V * kSortThreads;
   const int t = threadIdx.x;
   int v[V];
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int i = j * kSortThreads + t;
-    v[j] = i < k ? out[i] : kI32Min;
+    v[j] = i < k ? src[i] : kI32Min;
   }
+  __syncthreads();  // every read of src is done before lds is written
   // Keep the max at position i of a pair when i is the lower index of a
   // pair in a run sorted descending, or the upper in an ascending one.
   auto keep_max = [](int i, int d, int size) __attribute__((always_inline)) {
     return ((i & d) == 0) == ((i & size) == 0);
   };
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int d = size >> 1; d > 0; d >>= 1) {
+  // Runs of up to 32: directions follow the lane bits.
+#pragma unroll
+  for (int j = 0; j < V; ++j) v[j] = bitonic_sort<2, 32>(v[j]);
+  for (int size = 64; size <= m; size <<= 1) {
+    for (int d = size >> 1; d >= kWave; d >>= 1) {
       if (d >= kSortThreads) {
 #pragma unroll
         for (int js = 1; js < V; js <<= 1) {
@@ -611,7 +768,7 @@ __device__ __forceinline__ void sort_desc_block(int* out, int k, int* lds) {
             }
           }
         }
-      } else if (d >= kWave) {
+      } else {
 #pragma unroll
         for (int j = 0; j < V; ++j) lds[j * kSortThreads + t] = v[j];
         __syncthreads();
@@ -622,31 +779,362 @@ __device__ __forceinline__ void sort_desc_block(int* out, int k, int* lds) {
           v[j] = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
         }
         __syncthreads();
-      } else {
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-          const int i = j * kSortThreads + t;
-          const int o = __shfl_xor(v[j], d, kWave);
-          v[j] = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
-        }
       }
     }
+    // Distances 32 .. 1: the run's direction is the same for the wave.
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      v[j] = merge_dir<32>(v[j], ((j * kSortThreads + t) & size) == 0);
   }
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const int i = j * kSortThreads + t;
-    if (i < k) out[i] = v[j];
+    if (i < k) dst[i] = v[j];
   }
 }
 
-__global__ __launch_bounds__(kSortThreads) void sort_desc_kernel(int* out,
-                                                                 int k) {
-  __shared__ int lds[kMaxKSelect];
-  if (k <= kSortThreads) sort_desc_block<1>(out, k, lds);
-  else if (k <= 2 * kSortThreads) sort_desc_block<2>(out, k, lds);
-  else if (k <= 4 * kSortThreads) sort_desc_block<4>(out, k, lds);
-  else if (k <= 8 * kSortThreads) sort_desc_block<8>(out, k, lds);
-  else sort_desc_block<16>(out, k, lds);
+__device__ __forceinline__ void sort_desc(const int* src, int* dst, int k,
+                                          int* lds) {
+  if (k <= kSortThreads) sort_desc_block<1>(src, dst, k, lds);
+  else if (k <= 2 * kSortThreads) sort_desc_block<2>(src, dst, k, lds);
+  else if (k <= 4 * kSortThreads) sort_desc_block<4>(src, dst, k, lds);
+  else if (k <= 8 * kSortThreads) sort_desc_block<8>(src, dst, k, lds);
+  else sort_desc_block<16>(src, dst, k, lds);
+}
+
+// The last step of radix selection, one workgroup of 1024 threads.
+//
+// After the selection passes and the gather (state.fast == 0), out holds
+// the top-k unordered: sort it.
+//
+// After a small filter copy (state.fast == 1) of m values above the
+// threshold t: when m < k, they and k - m copies of t are the top-k.
+// Otherwise select from the m candidates (m <= kFinishMax) here, with
+// barriers instead of device counters between digits.  Every candidate is
+// above t, so all of them share the leading one bits of bias(t): those
+// bits start the prefix, and 8-bit digits below them follow ([Radix]
+// §3.2's digits, one LDS histogram per wave).  When the copy fits in LDS
+// (kFinBucketCap) the first digit pass copies it there and later passes
+// read LDS; otherwise passes read the copy until a chosen bucket fits,
+// and that pass keeps the bucket in LDS and the values above it as known
+// members of the top-k.  The values above the final bucket (or the whole
+// bucket, when it is needed entire), copies of g for what is left, and a
+// bitonic sort in LDS finish the top-k.
+constexpr int kFinThreads = kSortThreads;
+constexpr int kFinWaves = kFinThreads / kWave;
+constexpr int kFinBucketCap = 16384;
+
+struct FinishShared {
+  int top[kMaxKSelect];  // known top-k members; then the sort's exchange
+  int bucket[kFinBucketCap];
+  unsigned h[kFinWaves * kDigitBins];
+  int scan[kFinWaves];
+  int ntop, nbucket;
+  int pick[3];  // digit, count above it, count in it
+};
+
+// Visit cand[0..m) as f(x, ok, i), kFinRound 16-byte vectors per thread
+// and round; every thread takes part in every round (ok false where
+// nothing is left), so f may use wave votes.
+constexpr int kFinRound = 8;
+
+template <class F>
+__device__ __forceinline__ void fin_visit_copy(const int* cand, int m, F&& f) {
+  const v4i* cv = reinterpret_cast<const v4i*>(cand);
+  const int nv = m >> 2, t = threadIdx.x;
+  for (int base = 0; base < nv; base += kFinRound * kFinThreads) {
+    v4i d[kFinRound];
+    bool ok[kFinRound];
+#pragma unroll
+    for (int u = 0; u < kFinRound; ++u) {
+      const int i = base + u * kFinThreads + t;
+      ok[u] = i < nv;
+      d[u] = ok[u] ? cv[i] : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
+    }
+#pragma unroll
+    for (int u = 0; u < kFinRound; ++u) {
+      const int i = 4 * (base + u * kFinThreads + t);
+      f(d[u].x, ok[u], i);
+      f(d[u].y, ok[u], i + 1);
+      f(d[u].z, ok[u], i + 2);
+      f(d[u].w, ok[u], i + 3);
+    }
+  }
+  const int rest = m & 3;
+  if (rest) {
+    const bool ok = t < rest;
+    const int i = (nv << 2) + t;
+    f(ok ? cand[i] : kI32Min, ok, i);
+  }
+}
+
+// Two compactions from one pass over the copy (qa into a, qb into b), in
+// rounds: each thread counts what passes among its slots of the round,
+// one exclusive scan over the workgroup (both counts packed in one word)
+// places the slots after what earlier rounds appended, and the thread
+// writes them.  hist(x) sees every element on the way.  Positions at or
+// past a cap are dropped (a guard); the counts come back in *na, *nb.
+template <int N, class H, class QA, class QB>
+__device__ __forceinline__ void fin_round(const int (&x)[N], const bool (&ok)[N],
+                                          H&& hist, QA&& qa, QB&& qb, int* a,
+                                          int cap_a, int* b, int cap_b,
+                                          int& na, int& nb, int* scan) {
+  const int t = threadIdx.x, w = t / kWave;
+  int ca = 0, cb = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (ok[j]) {
+      hist(x[j]);
+      ca += qa(x[j]) ? 1 : 0;
+      cb += qb(x[j]) ? 1 : 0;
+    }
+  }
+  // Per round at most N * kFinThreads <= 2^15 of each: no carry.
+  const int packed = ca | (cb << 16);
+  const int incl_w = wave_scan_incl(packed);
+  if (lane() == kWave - 1) scan[w] = incl_w;
+  __syncthreads();
+  int before = incl_w - packed, total = 0;
+  for (int j = 0; j < kFinWaves; ++j) {
+    if (j < w) before += scan[j];
+    total += scan[j];
+  }
+  int pa = na + (before & 0xffff), pb = nb + (before >> 16);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (ok[j] && qa(x[j])) {
+      if (pa < cap_a) a[pa] = x[j];
+      ++pa;
+    }
+    if (ok[j] && qb(x[j])) {
+      if (pb < cap_b) b[pb] = x[j];
+      ++pb;
+    }
+  }
+  na += total & 0xffff;
+  nb += total >> 16;
+  __syncthreads();  // scan is reused by the next round
+}
+
+template <class H, class QA, class QB>
+__device__ __forceinline__ void fin_copy_compact(const int* cand, int m,
+                                                 H&& hist, QA&& qa, QB&& qb,
+                                                 int* a, int cap_a, int* b,
+                                                 int cap_b, int* na_out,
+                                                 int* nb_out, int* scan) {
+  const v4i* cv = reinterpret_cast<const v4i*>(cand);
+  const int nv = m >> 2, t = threadIdx.x;
+  int na = 0, nb = 0;
+  for (int base = 0; base < nv; base += kFinRound * kFinThreads) {
+    int x[4 * kFinRound];
+    bool ok[4 * kFinRound];
+#pragma unroll
+    for (int u = 0; u < kFinRound; ++u) {
+      const int i = base + u * kFinThreads + t;
+      const bool in = i < nv;
+      const v4i d = in ? cv[i] : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
+      x[4 * u] = d.x;
+      x[4 * u + 1] = d.y;
+      x[4 * u + 2] = d.z;
+      x[4 * u + 3] = d.w;
+      ok[4 * u] = ok[4 * u + 1] = ok[4 * u + 2] = ok[4 * u + 3] = in;
+    }
+    fin_round(x, ok, hist, qa, qb, a, cap_a, b, cap_b, na, nb, scan);
+  }
+  const int rest = m & 3;
+  if (rest) {
+    const bool in = t < rest;
+    const int x[1] = {in ? cand[(nv << 2) + t] : kI32Min};
+    const bool ok[1] = {in};
+    fin_round(x, ok, hist, qa, qb, a, cap_a, b, cap_b, na, nb, scan);
+  }
+  *na_out = na;
+  *nb_out = nb;
+}
+
+template <class F>
+__device__ __forceinline__ void fin_visit_lds(const int* b, int nb, F&& f) {
+  for (int base = 0; base < nb; base += kFinThreads) {
+    const int i = base + (int)threadIdx.x;
+    const bool ok = i < nb;
+    f(ok ? b[i] : kI32Min, ok, i);
+  }
+}
+
+// The digit holding the kleft-th largest of the histogram (waves' copies
+// summed; thread t < 256 looks at bin 255 - t); clears the histogram.
+__device__ __forceinline__ void fin_pick(FinishShared& sh, int kleft) {
+  const int t = threadIdx.x, w = t / kWave;
+  const int b = kDigitBins - 1 - t;
+  int c = 0, incl_w = 0;
+  if (t < kDigitBins) {
+#pragma unroll
+    for (int j = 0; j < kFinWaves; ++j) c += (int)sh.h[j * kDigitBins + b];
+    incl_w = wave_scan_incl(c);
+    if (lane() == kWave - 1) sh.scan[w] = incl_w;
+  }
+  __syncthreads();
+  if (t < kDigitBins) {
+    int incl = incl_w;
+    for (int j = 0; j < w; ++j) incl += sh.scan[j];
+    const int above = incl - c;
+    if (incl >= kleft && above < kleft) {
+      sh.pick[0] = b;
+      sh.pick[1] = above;
+      sh.pick[2] = c;
+    }
+  }
+  for (int i = t; i < kFinWaves * kDigitBins; i += kFinThreads) sh.h[i] = 0u;
+  __syncthreads();
+}
+
+// Append the elements of the LDS bucket b[0..nb) for which q holds to
+// dst[base..), in bucket order: each thread counts its own contiguous
+// share, an exclusive scan over the workgroup places the shares.
+template <class Q>
+__device__ __forceinline__ void fin_compact(const int* b, int nb, int* dst,
+                                            int base, int cap, int* scan,
+                                            Q&& q) {
+  const int t = threadIdx.x, w = t / kWave;
+  const int per = (nb + kFinThreads - 1) / kFinThreads;
+  const int lo = min(t * per, nb), hi = min(lo + per, nb);
+  int c = 0;
+  for (int i = lo; i < hi; ++i) c += q(b[i]) ? 1 : 0;
+  const int incl_w = wave_scan_incl(c);
+  if (lane() == kWave - 1) scan[w] = incl_w;
+  __syncthreads();
+  int pos = base + incl_w - c;
+  for (int j = 0; j < w; ++j) pos += scan[j];
+  for (int i = lo; i < hi; ++i) {
+    const int x = b[i];
+    if (q(x)) {
+      if (pos < cap) dst[pos] = x;
+      ++pos;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
+    SelectParams p) {
+  __shared__ FinishShared sh;
+  const int t = threadIdx.x, w = t / kWave, k = p.k;
+  const RadixState s = *p.st;
+  if (!s.fast) {
+    sort_desc(p.out, p.out, k, sh.top);
+    return;
+  }
+  const int m = s.bucket;
+  if (m < k) {
+    // Fewer than k values above t: all of them, then copies of t.
+    const int* cand = p.cand;
+    for (int i = t; i < m; i += kFinThreads) sh.top[i] = cand[i];
+    for (int i = m + t; i < k; i += kFinThreads) sh.top[i] = s.thresh;
+    __syncthreads();
+    sort_desc(sh.top, p.out, k, sh.top);
+    if (t == 0) p.st->fast = 0;
+    return;
+  }
+  for (int i = t; i < kFinWaves * kDigitBins; i += kFinThreads) sh.h[i] = 0u;
+  if (t == 0) {
+    sh.ntop = 0;
+    sh.nbucket = 0;
+  }
+  __syncthreads();
+  unsigned* hw = sh.h + w * kDigitBins;
+  const unsigned ut = bias(s.thresh);
+  // The leading one bits of bias(t) are shared by every candidate.
+  const int lead = ~ut == 0u ? 32 : __builtin_clz(~ut);
+  unsigned mask = lead == 0 ? 0u : ~0u << (32 - lead);
+  unsigned prefix = mask;
+  int rem = 32 - lead;  // bits below the prefix
+  int kleft = k, count = m, nb = 0;
+  bool done = false, in_lds = false;
+  while (rem > 0 && !done) {
+    const int nbits = rem < 8 ? rem : 8;
+    const unsigned dshift = (unsigned)(rem - nbits);
+    const unsigned dmask = (1u << nbits) - 1u;
+    if (in_lds) {
+      fin_visit_lds(sh.bucket, nb, [&](int x, bool ok, int)
+                                       __attribute__((always_inline)) {
+        const unsigned u = bias(x);
+        if (ok && (u & mask) == prefix)
+          atomicAdd(&hw[(u >> dshift) & dmask], 1u);
+      });
+    } else if (count == m && m <= kFinBucketCap) {
+      // The whole copy is the bucket and fits: copy it to LDS as it is.
+      fin_visit_copy(p.cand, m, [&](int x, bool ok, int i)
+                                    __attribute__((always_inline)) {
+        if (ok) {
+          sh.bucket[i] = x;
+          atomicAdd(&hw[(bias(x) >> dshift) & dmask], 1u);
+        }
+      });
+      in_lds = true;
+      nb = m;
+    } else if (count <= kFinBucketCap) {
+      // The bucket fits now: keep it in LDS, and the values above it (all
+      // in the top-k) in top.
+      int na, nt;
+      fin_copy_compact(
+          p.cand, m,
+          [&](int x) __attribute__((always_inline)) {
+            const unsigned u = bias(x);
+            if ((u & mask) == prefix) atomicAdd(&hw[(u >> dshift) & dmask], 1u);
+          },
+          [&](int x) __attribute__((always_inline)) {
+            return (bias(x) & mask) == prefix;
+          },
+          [&](int x) __attribute__((always_inline)) {
+            return (bias(x) & mask) > prefix;
+          },
+          sh.bucket, kFinBucketCap, sh.top, k, &na, &nt, sh.scan);
+      in_lds = true;
+      nb = min(na, kFinBucketCap);
+      if (t == 0) sh.ntop = nt;
+    } else {
+      fin_visit_copy(p.cand, m, [&](int x, bool ok, int)
+                                    __attribute__((always_inline)) {
+        const unsigned u = bias(x);
+        if (ok && (u & mask) == prefix)
+          atomicAdd(&hw[(u >> dshift) & dmask], 1u);
+      });
+    }
+    __syncthreads();
+    fin_pick(sh, kleft);
+    const unsigned d = (unsigned)sh.pick[0];
+    const int above = sh.pick[1];
+    count = sh.pick[2];
+    prefix |= d << dshift;
+    mask |= dmask << dshift;
+    kleft -= above;
+    done = count == kleft;  // the whole bucket is needed
+    rem -= nbits;
+  }
+  // The rest of the top-k: values above the final bucket (or in it, when
+  // it is needed whole) from wherever the bucket is held; k - kleft
+  // values in all.
+  auto wanted = [&](int x) __attribute__((always_inline)) {
+    const unsigned key = bias(x) & mask;
+    return key > prefix || (done && key == prefix);
+  };
+  if (in_lds) {
+    fin_compact(sh.bucket, nb, sh.top, sh.ntop, k, sh.scan, wanted);
+  } else {
+    int na, nn;
+    fin_copy_compact(
+        p.cand, m, [](int) {}, wanted, [](int) { return false; }, sh.top, k,
+        sh.bucket, 0, &na, &nn, sh.scan);
+  }
+  if (!done) {
+    // All 32 bits are resolved: the prefix is g, and kleft copies of it
+    // complete the top-k.
+    const int g = unbias(prefix);
+    for (int j = k - kleft + t; j < k; j += kFinThreads) sh.top[j] = g;
+  }
+  __syncthreads();
+  sort_desc(sh.top, p.out, k, sh.top);
+  if (t == 0) p.st->fast = 0;
 }
 
 }  // namespace ltk

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <map>
@@ -52,8 +53,9 @@ struct Scratch {
   unsigned long long* acc = nullptr;  // kMaxBins histogram counters, 0
                                       // between calls
   RadixState* rstate = nullptr;       // radix-selection state
-  int* rcand = nullptr;               // kCandCap candidates, allocated by
-                                      // the first top-k call with k > 128
+  int* rcand = nullptr;               // kCandCap candidates + sample
+                                      // lists, allocated by the first
+                                      // top-k call with k > 128
   unsigned* ticket = nullptr;  // kMaxGrid words (one per row), 0 between calls
 };
 
@@ -192,16 +194,22 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 template <class P>
-int launch(const void* fn, int grid, P params, hipStream_t stream) {
+int launch_threads(const void* fn, int grid, int threads, P params,
+                   hipStream_t stream) {
   void* args[] = {&params};
   const hipError_t e =
-      hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+      hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) {
     debug_hip("kernel launch", e);
     (void)hipGetLastError();
     return LIBTOPK_ERR_HIP;
   }
   return LIBTOPK_OK;
+}
+
+template <class P>
+int launch(const void* fn, int grid, P params, hipStream_t stream) {
+  return launch_threads(fn, grid, kBlock, params, stream);
 }
 
 // List capacity: exactly k rounded up to 8 while that is small (the list
@@ -272,18 +280,21 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
-// Inputs from this size on are sampled for a first-digit guess.
+// Inputs from this size on are sampled for a filter threshold.
 constexpr int64_t kSampleMinN = (int64_t)1 << 24;
 
-// The candidate buffer of radix selection (kCandCap int32), allocated once
-// per (device, stream) on first use.
+// The candidate buffer of radix selection (kCandCap int32) and, after it,
+// the published sample lists (kSampleGrid * kNeedMax int32), allocated
+// once per (device, stream) on first use.
 int get_rcand(int dev, hipStream_t stream, int** out) {
   std::lock_guard<std::mutex> lock(g_mu);
   Scratch& sc = g_cache[std::make_pair(dev, (void*)stream)];
   if (!sc.rcand) {
     if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
     void* p = nullptr;
-    const hipError_t e = hipMalloc(&p, (size_t)kCandCap * sizeof(int));
+    const hipError_t e =
+        hipMalloc(&p, (size_t)(kCandCap + kSampleGrid * kNeedMax) *
+                          sizeof(int));
     if (e != hipSuccess) {
       debug_hip("hipMalloc(candidates)", e);
       (void)hipGetLastError();
@@ -317,48 +328,41 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   sp.out = out;
   sp.acc = sc.acc;
   sp.ticket = sc.ticket;
-  sp.use_guess = 0;
-  // Large inputs: sample 2^18 values for a first-digit guess, so that
-  // the first pass can copy the candidates aside and no later pass reads
-  // the input again.
+  // Large inputs: a sample sets a threshold, and a filter pass copies
+  // every value above it aside; one workgroup selects from a small copy,
+  // the selection passes from a larger one (or, if the copy cannot hold the
+  // top-k, from the input).
+  bool filtered = false;
   const int64_t nvec = (n - pl.head) / 4;
-  if (n >= kSampleMinN && nvec > 0) {
-    constexpr int kSampleU = 1, kSampleGrid = 256;
-    const int64_t nsamp = (int64_t)kSampleGrid * kBlock * kSampleU;
+  if (n >= kSampleMinN && nvec >= kSampleVecs) {
     SampleParams q;
     q.body = reinterpret_cast<const v4i*>(in + pl.head);
     q.nvec = nvec;
-    q.stride = nvec / nsamp > 0 ? nvec / nsamp : 1;
-    // 4x the sampled share of k, plus 64: the guess stays far below the
-    // digit of the k-th largest unless the data is strongly skewed.
-    const int64_t sampled = 4 * (nvec / q.stride < nsamp ? nvec / q.stride
-                                                         : nsamp);
-    q.need = (int)(4 * (int64_t)k * sampled / n + 64);
+    q.stride = nvec / kSampleVecs;
+    // The sample's share of k, plus four standard deviations and 4.
+    const double ks = (double)k * kSampleVals / (double)n;
+    q.need = (int)std::ceil(ks + 4.0 * std::sqrt(ks) + 4.0);
+    if (q.need > kNeedMax) q.need = kNeedMax;
     q.st = sc.rstate;
-    q.acc = sc.acc;
+    q.samp = rcand + kCandCap;
     q.ticket = sc.ticket;
-    q.grid = kSampleGrid;
-    rc = launch((const void*)&sample_kernel<kSampleU>, kSampleGrid, q, s);
+    rc = launch_threads((const void*)&sample_kernel, kSampleGrid,
+                        kSampleThreads, q, s);
     if (rc != LIBTOPK_OK) return rc;
-    sp.use_guess = 1;
+    rc = launch((const void*)&filter_kernel<kTileVec>, pl.grid, sp, s);
+    if (rc != LIBTOPK_OK) return rc;
+    filtered = true;
   }
   for (int pass = 0; pass < 4; ++pass) {
     sp.dshift = 24 - 8 * pass;
-    sp.first = pass == 0;
+    sp.first = pass == 0 && !filtered;  // the filter wrote the first state
     rc = launch((const void*)&select_pass_kernel<kTileVec>, pl.grid, sp, s);
     if (rc != LIBTOPK_OK) return rc;
   }
   rc = launch((const void*)&gather_kernel<kTileVec>, pl.grid, sp, s);
   if (rc != LIBTOPK_OK) return rc;
-  void* args[] = {&out, &k};
-  const hipError_t e = hipLaunchKernel((const void*)&sort_desc_kernel,
-                                       dim3(1), dim3(kSortThreads), args, 0, s);
-  if (e != hipSuccess) {
-    debug_hip("kernel launch", e);
-    (void)hipGetLastError();
-    return LIBTOPK_ERR_HIP;
-  }
-  return LIBTOPK_OK;
+  return launch_threads((const void*)&select_finish_kernel, 1, kFinThreads,
+                        sp, s);
 }
 
 const void* reduce_fn(int op) {

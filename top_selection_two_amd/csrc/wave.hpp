@@ -316,4 +316,110 @@ struct RegCount {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Bitonic compare-exchange across a wave, in registers.
+
+// Lanes whose bit is set in `mask` take a, the others b: one v_cndmask
+// whose condition is a constant lane mask held in a scalar register pair.
+__device__ __forceinline__ int pick_lanes(uint64_t mask, int a, int b) {
+  int r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+  return r;
+}
+
+// Lanes l with (l & bit) != 0.
+constexpr uint64_t lanes_with(int bit) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (l & bit) m |= 1ull << l;
+  return m;
+}
+
+// Lanes that keep the larger value of their pair in the bitonic step with
+// partner distance s inside runs of `size`: the lower lane of a pair in a
+// run sorted descending, the upper lane in an ascending one.
+constexpr uint64_t keep_max_lanes(int size, int s) {
+  uint64_t m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & s) == 0) == ((l & size) == 0)) m |= 1ull << l;
+  return m;
+}
+
+// DPP controls: quad permutes [1,0,3,2] and [2,3,0,1], row rotations by 4,
+// 8 and 12 (dst lane i of a 16-lane row reads lane (i - r) mod 16).
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;
+constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128, kRowRor12 = 0x12c;
+
+// One compare-exchange step of a bitonic network across the wave: every
+// lane meets the lane at distance s (l ^ s) and keeps the max (lanes in
+// KEEP) or the min.
+// For s = 1, 2, 8 the partner arrives as a DPP operand of the max and of the
+// min themselves (the identity as `old` lets the compiler fold the moves);
+// for s = 4 two bank-masked row rotations build it (banks 1 and 3 of a row
+// read 4 lanes down, banks 0 and 2 read 4 lanes up); for 16 and 32 the
+// gfx950 row swaps return both halves of the exchange.
+template <int S, uint64_t KEEP>
+__device__ __forceinline__ int cx_keep(int v) {
+  int hi, lo;
+  if constexpr (S == 1 || S == 2 || S == 8) {
+    constexpr int c = S == 1 ? kQuadXor1 : S == 2 ? kQuadXor2 : kRowRor8;
+    hi = max(v, __builtin_amdgcn_update_dpp(kI32Min, v, c, 0xf, 0xf, false));
+    lo = min(v, __builtin_amdgcn_update_dpp(kI32Max, v, c, 0xf, 0xf, false));
+  } else {
+    int o;
+    if constexpr (S == 4) {
+      const int t =
+          __builtin_amdgcn_update_dpp(0, v, kRowRor4, 0xf, 0xa, false);
+      o = __builtin_amdgcn_update_dpp(t, v, kRowRor12, 0xf, 0x5, false);
+    } else {
+      const auto r =
+          S == 16 ? __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v,
+                                                     false, false)
+                  : __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v,
+                                                     false, false);
+      o = pick_lanes(lanes_with(S), (int)r[0], (int)r[1]);
+    }
+    hi = max(v, o);
+    lo = min(v, o);
+  }
+  return pick_lanes(KEEP, hi, lo);
+}
+
+template <int SIZE, int S>
+__device__ __forceinline__ int bitonic_step(int v) {
+  return cx_keep<S, keep_max_lanes(SIZE, S)>(v);
+}
+
+// The last steps of a bitonic merge, partner distances S, S / 2, .., 1, in
+// runs whose direction is the same for the whole wave (runs longer than
+// the wave): descending, or ascending.
+template <int S>
+__device__ __forceinline__ int merge_dir(int v, bool desc) {
+  v = desc ? cx_keep<S, ~lanes_with(S)>(v) : cx_keep<S, lanes_with(S)>(v);
+  if constexpr (S > 1) v = merge_dir<S / 2>(v, desc);
+  return v;
+}
+
+template <int SIZE, int S>
+__device__ __forceinline__ int bitonic_merge(int v) {
+  v = bitonic_step<SIZE, S>(v);
+  if constexpr (S > 1) v = bitonic_merge<SIZE, S / 2>(v);
+  return v;
+}
+
+template <int SIZE, int W>
+__device__ __forceinline__ int bitonic_sort(int v) {
+  v = bitonic_merge<SIZE, SIZE / 2>(v);
+  if constexpr (SIZE < W) v = bitonic_sort<SIZE * 2, W>(v);
+  return v;
+}
+
+// Bitonic sort of one value per lane, descending, within aligned groups of
+// W lanes (W = 32 or 64): lane 0 of a group ends with its largest value.
+// log2(W) (log2(W) + 1) / 2 compare-exchange steps, all in registers.
+template <int W>
+__device__ __forceinline__ int wave_sort_desc(int v) {
+  return bitonic_sort<2, W>(v);
+}
+
 }  // namespace ltk
