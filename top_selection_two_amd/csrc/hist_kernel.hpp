@@ -491,7 +491,10 @@ __device__ __forceinline__ void sample_pick(RankShared& sh, int need) {
   if (lane() == kWave - 1) sh.scan[w] = incl_w;
   __syncthreads();
   int run = incl_w - local;
-  for (int j = 0; j < w; ++j) run += sh.scan[j];
+  // All totals read at once (a fixed count the compiler issues together).
+#pragma unroll
+  for (int j = 0; j < kSampleThreads / kWave; ++j)
+    run += j < w ? sh.scan[j] : 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int b = kThreshBins - 1 - kPer * t - i;
@@ -822,11 +825,13 @@ __device__ __forceinline__ void sort_desc(const int* src, int* dst, int k,
 // bitonic sort in LDS finish the top-k.
 constexpr int kFinThreads = kSortThreads;
 constexpr int kFinWaves = kFinThreads / kWave;
-constexpr int kFinBucketCap = 16384;
+// LDS: top (64 KiB) + bucket (76 KiB) + histograms (16 KiB) fill the
+// 160 KiB a gfx950 workgroup may hold.
+constexpr int kFinBucketCap = 19456;
 
 struct FinishShared {
   int top[kMaxKSelect];  // known top-k members; then the sort's exchange
-  int bucket[kFinBucketCap];
+  alignas(16) int bucket[kFinBucketCap];
   unsigned h[kFinWaves * kDigitBins];
   int scan[kFinWaves];
   int ntop, nbucket;
@@ -835,8 +840,13 @@ struct FinishShared {
 
 // Visit cand[0..m) as f(x, ok, i), kFinRound 16-byte vectors per thread
 // and round; every thread takes part in every round (ok false where
-// nothing is left), so f may use wave votes.
+// nothing is left), so f may use wave votes.  The loads of a round are
+// unconditional, so they issue back to back: the last round reads up to
+// kFinRound * kFinThreads vectors past m, which stay inside the candidate
+// buffer (kCandCap elements, and m <= kFinishMax).
 constexpr int kFinRound = 8;
+static_assert(kFinishMax + 4 * kFinRound * kFinThreads <= kCandCap,
+              "finish rounds must stay inside the candidate buffer");
 
 template <class F>
 __device__ __forceinline__ void fin_visit_copy(const int* cand, int m, F&& f) {
@@ -846,11 +856,9 @@ __device__ __forceinline__ void fin_visit_copy(const int* cand, int m, F&& f) {
     v4i d[kFinRound];
     bool ok[kFinRound];
 #pragma unroll
-    for (int u = 0; u < kFinRound; ++u) {
-      const int i = base + u * kFinThreads + t;
-      ok[u] = i < nv;
-      d[u] = ok[u] ? cv[i] : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
-    }
+    for (int u = 0; u < kFinRound; ++u) d[u] = cv[base + u * kFinThreads + t];
+#pragma unroll
+    for (int u = 0; u < kFinRound; ++u) ok[u] = base + u * kFinThreads + t < nv;
 #pragma unroll
     for (int u = 0; u < kFinRound; ++u) {
       const int i = 4 * (base + u * kFinThreads + t);
@@ -895,9 +903,11 @@ __device__ __forceinline__ void fin_round(const int (&x)[N], const bool (&ok)[N]
   if (lane() == kWave - 1) scan[w] = incl_w;
   __syncthreads();
   int before = incl_w - packed, total = 0;
+#pragma unroll
   for (int j = 0; j < kFinWaves; ++j) {
-    if (j < w) before += scan[j];
-    total += scan[j];
+    const int v = scan[j];
+    before += j < w ? v : 0;
+    total += v;
   }
   int pa = na + (before & 0xffff), pb = nb + (before >> 16);
 #pragma unroll
@@ -926,17 +936,19 @@ __device__ __forceinline__ void fin_copy_compact(const int* cand, int m,
   const int nv = m >> 2, t = threadIdx.x;
   int na = 0, nb = 0;
   for (int base = 0; base < nv; base += kFinRound * kFinThreads) {
+    // Unconditional loads, as in fin_visit_copy.
+    v4i d[kFinRound];
+#pragma unroll
+    for (int u = 0; u < kFinRound; ++u) d[u] = cv[base + u * kFinThreads + t];
     int x[4 * kFinRound];
     bool ok[4 * kFinRound];
 #pragma unroll
     for (int u = 0; u < kFinRound; ++u) {
-      const int i = base + u * kFinThreads + t;
-      const bool in = i < nv;
-      const v4i d = in ? cv[i] : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
-      x[4 * u] = d.x;
-      x[4 * u + 1] = d.y;
-      x[4 * u + 2] = d.z;
-      x[4 * u + 3] = d.w;
+      const bool in = base + u * kFinThreads + t < nv;
+      x[4 * u] = d[u].x;
+      x[4 * u + 1] = d[u].y;
+      x[4 * u + 2] = d[u].z;
+      x[4 * u + 3] = d[u].w;
       ok[4 * u] = ok[4 * u + 1] = ok[4 * u + 2] = ok[4 * u + 3] = in;
     }
     fin_round(x, ok, hist, qa, qb, a, cap_a, b, cap_b, na, nb, scan);
@@ -952,12 +964,22 @@ __device__ __forceinline__ void fin_copy_compact(const int* cand, int m,
   *nb_out = nb;
 }
 
+// Visit b[0..nb) in LDS as f(x, ok, i), kFinRound elements per thread and
+// round; the reads of a round (indices clamped into the array) issue
+// together.
 template <class F>
 __device__ __forceinline__ void fin_visit_lds(const int* b, int nb, F&& f) {
-  for (int base = 0; base < nb; base += kFinThreads) {
-    const int i = base + (int)threadIdx.x;
-    const bool ok = i < nb;
-    f(ok ? b[i] : kI32Min, ok, i);
+  const int t = threadIdx.x;
+  for (int base = 0; base < nb; base += kFinRound * kFinThreads) {
+    int x[kFinRound];
+#pragma unroll
+    for (int j = 0; j < kFinRound; ++j)
+      x[j] = b[min(base + j * kFinThreads + t, nb - 1)];
+#pragma unroll
+    for (int j = 0; j < kFinRound; ++j) {
+      const int i = base + j * kFinThreads + t;
+      f(x[j], i < nb, i);
+    }
   }
 }
 
@@ -989,30 +1011,26 @@ __device__ __forceinline__ void fin_pick(FinishShared& sh, int kleft) {
 }
 
 // Append the elements of the LDS bucket b[0..nb) for which q holds to
-// dst[base..), in bucket order: each thread counts its own contiguous
-// share, an exclusive scan over the workgroup places the shares.
+// dst[base..), kFinRound per thread and round (reads clamped into the
+// array, issued together), placed by fin_round's scan.
 template <class Q>
 __device__ __forceinline__ void fin_compact(const int* b, int nb, int* dst,
                                             int base, int cap, int* scan,
                                             Q&& q) {
-  const int t = threadIdx.x, w = t / kWave;
-  const int per = (nb + kFinThreads - 1) / kFinThreads;
-  const int lo = min(t * per, nb), hi = min(lo + per, nb);
-  int c = 0;
-  for (int i = lo; i < hi; ++i) c += q(b[i]) ? 1 : 0;
-  const int incl_w = wave_scan_incl(c);
-  if (lane() == kWave - 1) scan[w] = incl_w;
-  __syncthreads();
-  int pos = base + incl_w - c;
-  for (int j = 0; j < w; ++j) pos += scan[j];
-  for (int i = lo; i < hi; ++i) {
-    const int x = b[i];
-    if (q(x)) {
-      if (pos < cap) dst[pos] = x;
-      ++pos;
-    }
+  const int t = threadIdx.x;
+  int na = base, nn = 0;
+  for (int r = 0; r < nb; r += kFinRound * kFinThreads) {
+    int x[kFinRound];
+    bool ok[kFinRound];
+#pragma unroll
+    for (int j = 0; j < kFinRound; ++j)
+      x[j] = b[min(r + j * kFinThreads + t, nb - 1)];
+#pragma unroll
+    for (int j = 0; j < kFinRound; ++j) ok[j] = r + j * kFinThreads + t < nb;
+    fin_round(
+        x, ok, [](int) {}, q, [](int) { return false; }, dst, cap,
+        static_cast<int*>(nullptr), 0, na, nn, scan);
   }
-  __syncthreads();
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
@@ -1062,14 +1080,36 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
           atomicAdd(&hw[(u >> dshift) & dmask], 1u);
       });
     } else if (count == m && m <= kFinBucketCap) {
-      // The whole copy is the bucket and fits: copy it to LDS as it is.
-      fin_visit_copy(p.cand, m, [&](int x, bool ok, int i)
-                                    __attribute__((always_inline)) {
-        if (ok) {
-          sh.bucket[i] = x;
-          atomicAdd(&hw[(bias(x) >> dshift) & dmask], 1u);
+      // The whole copy is the bucket and fits: copy it to LDS as it is,
+      // 16 bytes at a time (the bucket array is 16-byte aligned).
+      const v4i* cv = reinterpret_cast<const v4i*>(p.cand);
+      v4i* bv = reinterpret_cast<v4i*>(sh.bucket);
+      const int nv = m >> 2;
+      auto count_digit = [&](int x) __attribute__((always_inline)) {
+        atomicAdd(&hw[(bias(x) >> dshift) & dmask], 1u);
+      };
+      for (int base = 0; base < nv; base += kFinRound * kFinThreads) {
+        v4i d[kFinRound];
+#pragma unroll
+        for (int u = 0; u < kFinRound; ++u)
+          d[u] = cv[base + u * kFinThreads + t];
+#pragma unroll
+        for (int u = 0; u < kFinRound; ++u) {
+          const int i = base + u * kFinThreads + t;
+          if (i < nv) {
+            bv[i] = d[u];
+            count_digit(d[u].x);
+            count_digit(d[u].y);
+            count_digit(d[u].z);
+            count_digit(d[u].w);
+          }
         }
-      });
+      }
+      if (t < (m & 3)) {
+        const int x = p.cand[(nv << 2) + t];
+        sh.bucket[(nv << 2) + t] = x;
+        count_digit(x);
+      }
       in_lds = true;
       nb = m;
     } else if (count <= kFinBucketCap) {
