@@ -27,7 +27,8 @@
  *  - The library owns a small scratch area per (device, stream), about
  *    1.6 MiB: per-block candidates (1.5 MiB, int32 and key-value), partial
  *    results, histogram counters and tickets; the first topk_i32 call with
- *    k > LIBTOPK_MAX_K on the pair adds a 16 MiB candidate buffer.  It is
+ *    k > LIBTOPK_MAX_K on the pair adds a 16 MiB candidate buffer (and
+ *    16 KiB for sample lists).  It is
  *    allocated by the
  *    first call on that pair (so do that first call before capturing the
  *    stream into a HIP graph), kept for reuse, and freed by
@@ -88,9 +89,13 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
  * selection ("GPU基数排序优化：10亿级数据处理与性能调优" §3.2–3.3: 8-bit digit
  * histograms kept per warp in shared memory): four digit passes find the
  * k-th largest value, a gather pass collects the values above it, and one
- * workgroup sorts the k results; six stream-ordered launches.  Once a
- * digit leaves fewer than 2^22 candidates they are copied aside and the
- * remaining passes read only them, so the input is usually read twice.
+ * workgroup sorts the k results.  Once a digit leaves fewer than 2^22
+ * candidates they are copied aside and the remaining passes read only
+ * them.  From n = 2^24 on, a sample first fixes a threshold and a filter
+ * pass copies the values above it aside; when that copy is small (the
+ * usual case) one workgroup selects the top-k from it, the digit passes
+ * return at once, and the input is read once.  Six stream-ordered
+ * launches, eight from n = 2^24 on.
  *
  *   in   device, int32[n], read once (k <= LIBTOPK_MAX_K)
  *   n    number of elements, 1 <= n <= 2^32

@@ -39,6 +39,14 @@
 // bucket, or the whole bucket when selection stopped early) from the input
 // or the candidate buffer, copies of g fill the rest, and one workgroup
 // sorts the k values in LDS.
+//
+// Large inputs first try a shortcut: a sample fixes a threshold t (the
+// value of a small rank in an evenly spaced sample), one filter pass
+// copies the values above t aside and counts those equal to t, and when
+// that copy is small one workgroup selects the top-k from it in LDS
+// (select_finish_kernel); the digit passes then return at once.  When the
+// copy is too large, or cannot hold the top-k, the digit passes run as
+// above, so the sample affects the time only.
 #pragma once
 
 #include "wave.hpp"
