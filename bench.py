@@ -35,7 +35,8 @@ Prints ONE JSON line.  `value` is elements per second (higher is better);
 element plus the output) per launch to its measured duration and the 8 TB/s
 HBM peak; `traffic` is the HBM byte count per launch measured with rocprofv3
 counters (profiles/<path>_counters_*.json), reported only while the kernel
-sources still match the ones the counters were taken on.
+sources (their code; comments and blank lines aside) still match the ones
+the counters were taken on.
 
 Modes for profiling runs (no JSON line): --mode counters runs a few calls
 plus a plain device copy of known size, to calibrate FETCH_SIZE/WRITE_SIZE.
@@ -185,12 +186,26 @@ def workload_size(P) -> int:
     return synth.WORKLOADS[P["workload"]]["n"]
 
 
+def code_only(text: str) -> str:
+    """Source text without // comments and blank lines: edits to comments
+    leave the compiled kernels, and so the counters, as they were."""
+    out = []
+    for line in text.splitlines():
+        i = line.find("//")
+        if i >= 0:
+            line = line[:i]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
     for name in PATHS[path]["sources"]:
         with open(os.path.join(ROOT, "top_selection_two_amd", "csrc", name),
-                  "rb") as f:
-            h.update(f.read())
+                  encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
