@@ -9,7 +9,11 @@ misaligned starts, n = 0, repeated calls and two streams (the device
 counters clean themselves).  Top-k by radix selection covers k from 129 to
 16384, ties at the k-th value, sorted and all-equal inputs, selection that
 stops after the first digit (the whole bucket is needed), k = n, and the
-1e8 workload.
+1e8 workload.  From 2^24 elements on, inputs built around the sampled
+positions drive each way through the sampled path: the one-workgroup
+finish with and without copies of the threshold, a copy too large for it,
+a copy too large for the candidate buffer, and a sample whose threshold is
+too high.
 """
 import numpy as np
 import pytest
@@ -221,3 +225,80 @@ def test_large_k_repeated_and_mixed_with_small_k(ltk, rng):
         assert np.array_equal(ltk.topk(d, k).cpu().numpy(), oracle.topk(x, k))
         h = ltk.histogram(d, I32_MIN, 22, 1024).cpu().numpy()
         assert np.array_equal(h, oracle.histogram(x, I32_MIN, 22, 1024))
+
+
+# ------------------------------------------- the sampled path (n >= 2^24)
+# From 2^24 elements on, a strided sample of 16384 16-byte vectors sets a
+# threshold t and a filter pass copies the values above t.  With an
+# aligned input of n = 2^24 the sample reads elements 1024 i .. 1024 i + 3
+# (i < 16384), so the cases below can steer what the sample sees and send
+# the call down each of its ways: the one-workgroup finish (with and
+# without copies of t), the selection passes over the copy, and the
+# passes over the input when the copy is too large or the sample claims
+# too much.
+N_SAMPLED = 2 ** 24
+
+
+def sampled_positions():
+    base = np.arange(16384, dtype=np.int64) * 1024
+    return (base[:, None] + np.arange(4)[None, :]).ravel()
+
+
+def unsampled_choice(rng, count):
+    """count distinct positions that the sample does not read."""
+    pos = rng.choice(N_SAMPLED // 1024 * 1020, size=count, replace=False)
+    # map 0..1020*16384 onto the 1020 unsampled slots of each 1024 block
+    return (pos // 1020) * 1024 + 4 + (pos % 1020)
+
+
+@pytest.mark.parametrize("k", [129, 1000, 16384])
+def test_sampled_all_equal(ltk, k):
+    # gt = 0 above t and every value equal to it: k copies of t
+    for v in (0, -7, I32_MIN, I32_MAX):
+        check_topk(ltk, np.full(N_SAMPLED, v, np.int32), k)
+
+
+@pytest.mark.parametrize("k", [129, 1000, 16384])
+def test_sampled_few_above_a_sea(ltk, rng, k):
+    # fewer than k values above t = 5: all of them, then copies of 5
+    x = np.full(N_SAMPLED, 5, np.int32)
+    pos = unsampled_choice(rng, 100)
+    x[pos] = 10 + np.arange(100, dtype=np.int32)
+    check_topk(ltk, x, k)
+
+
+@pytest.mark.parametrize("k", [1000, 16384])
+def test_sampled_copy_between_finish_and_buffer(ltk, rng, k):
+    # the sample sees only zeros, t = 0, and 2M values lie above it: too
+    # many for one workgroup, few enough for the candidate buffer
+    x = np.zeros(N_SAMPLED, np.int32)
+    pos = unsampled_choice(rng, 2_000_000)
+    x[pos] = rng.integers(1, 2 ** 31 - 1, size=pos.size, dtype=np.int64)
+    check_topk(ltk, x, k)
+
+
+def test_sampled_copy_beyond_buffer(ltk, rng):
+    # 5M values above t = 0: more than the candidate buffer holds, so the
+    # selection passes read the input
+    x = np.zeros(N_SAMPLED, np.int32)
+    pos = unsampled_choice(rng, 5_000_000)
+    x[pos] = rng.integers(1, 1_000_000, size=pos.size)
+    check_topk(ltk, x, 1000)
+    check_topk(ltk, x, 16384)
+
+
+@pytest.mark.parametrize("k", [1000, 16384])
+def test_sampled_threshold_too_high(ltk, rng, k):
+    # the sample sees only large values, the rest of the input is small:
+    # fewer than k values reach t, so the passes read the input
+    x = rng.integers(-1_000_000, 1_000_000, size=N_SAMPLED).astype(np.int32)
+    sp = sampled_positions()
+    x[sp] = 1_000_000_000 + rng.permutation(sp.size).astype(np.int32)
+    check_topk(ltk, x, k)
+
+
+def test_sampled_misaligned_and_ties(ltk, rng):
+    # a misaligned start moves the sample; ties at the k-th value
+    x = rng.integers(0, 1 << 16, size=N_SAMPLED + 12345).astype(np.int32)
+    check_topk(ltk, x, 5000, offset=1)
+    check_topk(ltk, x, 16384, offset=3)
