@@ -28,7 +28,7 @@
  *    1.6 MiB: per-block candidates (1.5 MiB, int32 and key-value), partial
  *    results, histogram counters and tickets; the first topk_i32 call with
  *    k > LIBTOPK_MAX_K on the pair adds a 16 MiB candidate buffer (and
- *    16 KiB for sample lists).  It is
+ *    64 KiB for sample lists).  It is
  *    allocated by the
  *    first call on that pair (so do that first call before capturing the
  *    stream into a HIP graph), kept for reuse, and freed by

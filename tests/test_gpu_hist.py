@@ -228,27 +228,30 @@ def test_large_k_repeated_and_mixed_with_small_k(ltk, rng):
 
 
 # ------------------------------------------- the sampled path (n >= 2^24)
-# From 2^24 elements on, a strided sample of 16384 16-byte vectors sets a
-# threshold t and a filter pass copies the values above t.  With an
-# aligned input of n = 2^24 the sample reads elements 1024 i .. 1024 i + 3
-# (i < 16384), so the cases below can steer what the sample sees and send
-# the call down each of its ways: the one-workgroup finish (with and
-# without copies of t), the selection passes over the copy, and the
-# passes over the input when the copy is too large or the sample claims
-# too much.
+# From 2^24 elements on, a strided sample of 16-byte vectors (16, 32 or
+# 64 thousand of them, by k) sets a threshold t and a filter pass copies
+# the values above t.  With an aligned input of n = 2^24 the sample reads
+# elements s i .. s i + 3 with a stride s of 1024, 512 or 256, all within
+# the positions 256 i .. 256 i + 3, so the cases below can steer what the
+# sample sees and send the call down each of its ways: the one-workgroup
+# finish (with and without copies of t), the selection passes over the
+# copy, and the passes over the input when the copy is too large or the
+# sample claims too much.
 N_SAMPLED = 2 ** 24
+SPACING = 256
 
 
 def sampled_positions():
-    base = np.arange(16384, dtype=np.int64) * 1024
+    """Every position a sample of an aligned 2^24 input may read."""
+    base = np.arange(N_SAMPLED // SPACING, dtype=np.int64) * SPACING
     return (base[:, None] + np.arange(4)[None, :]).ravel()
 
 
 def unsampled_choice(rng, count):
-    """count distinct positions that the sample does not read."""
-    pos = rng.choice(N_SAMPLED // 1024 * 1020, size=count, replace=False)
-    # map 0..1020*16384 onto the 1020 unsampled slots of each 1024 block
-    return (pos // 1020) * 1024 + 4 + (pos % 1020)
+    """count distinct positions that no sample reads."""
+    free = SPACING - 4
+    pos = rng.choice(N_SAMPLED // SPACING * free, size=count, replace=False)
+    return (pos // free) * SPACING + 4 + (pos % free)
 
 
 @pytest.mark.parametrize("k", [129, 1000, 16384])

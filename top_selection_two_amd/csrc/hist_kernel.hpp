@@ -446,10 +446,10 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   if (t == 0) st_agent(p.ticket, 0u);
 }
 
-// The filter threshold for top-k with large n.  kSampleGrid workgroups
-// read S = kSampleVecs 16-byte vectors spread evenly over the input (one
-// per thread); t is to be the value of rank `need` among the S * 4 sampled
-// values (`need` is k scaled to the sample, with a wide margin).  Each
+// The filter threshold for top-k with large n.  `grid` workgroups read
+// grid * 1024 16-byte vectors spread evenly over the input (one per
+// thread); t is to be the value of rank `need` among the S = grid * 4096
+// sampled values (`need` is k scaled to the sample, with a wide margin).  Each
 // workgroup finds the value of rank `need` among its own samples and
 // publishes its `need` largest; the last workgroup finds the value of rank
 // `need` in the union of those lists, which is that of the whole sample.
@@ -459,19 +459,19 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
 // values are >= t, the top-k lies among them, whatever t is, so a poor
 // sample costs time, never correctness.
 constexpr int kSampleThreads = 1024;
-constexpr int kSampleGrid = 16;
-constexpr int kSampleVecs = kSampleThreads * kSampleGrid;
-constexpr int kSampleVals = 4 * kSampleVecs;
-constexpr int kNeedMax = 256;     // largest `need`
+constexpr int kSampleGridMax = 64;  // workgroups (S = 4096 values each)
+constexpr int kNeedMax = 256;       // largest `need`
+constexpr int kUnionSlots = 4 * kSampleThreads;  // grid * need <= this
 constexpr int kThreshBins = 4096;
 
 struct SampleParams {
   const v4i* body;   // the 16-byte-aligned body of the input
   int64_t nvec;      // vectors in it
   int64_t stride;    // vectors between consecutive samples
-  int need;          // 1 <= need <= kNeedMax
+  int grid;          // workgroups, <= kSampleGridMax
+  int need;          // 1 <= need <= kNeedMax, grid * need <= kUnionSlots
   RadixState* st;
-  int* samp;         // [kSampleGrid * kNeedMax] the published lists
+  int* samp;         // [kSampleGridMax * kNeedMax] the published lists
   unsigned* ticket;
 };
 
@@ -586,17 +586,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     if (q && pos < kNeedMax) st_agent(mine + pos, (int)u[j]);
   }
   for (int i = a + t; i < p.need; i += kSampleThreads) st_agent(mine + i, (int)v);
-  if (!last_to_finish(p.ticket, kSampleGrid, &sh.is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
 
-  // The union of the lists: kSampleGrid * need <= 4 * kSampleThreads
-  // values.
+  // The union of the lists: grid * need <= kUnionSlots values.
   unsigned w[4], valid = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = j * kSampleThreads + t;
     const int g = i / p.need, r = i - g * p.need;
     w[j] = 0u;
-    if (g < kSampleGrid) {
+    if (g < p.grid) {
       w[j] = (unsigned)ld_agent(p.samp + g * kNeedMax + r);
       valid |= 1u << j;
     }
@@ -737,8 +736,8 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
 // registers, so a compare-exchange step of distance d costs: d < 64, a
 // lane exchange inside the wave (DPP and row swaps, in registers); d >=
 // 1024, a swap between two of the thread's registers; 64 <= d < 1024, a
-// round trip through LDS with two barriers (only these need the
-// workgroup).
+// round trip through LDS with two barriers, which takes two such steps
+// at once when it can (only these need the workgroup).
 constexpr int kSortThreads = 1024;
 
 template <int V>
@@ -780,6 +779,11 @@ __device__ __forceinline__ void sort_desc_block(const int* src, int* dst,
           }
         }
       } else {
+        // Through LDS, two distances (d and d / 2) per round trip when
+        // both need it: element i reads the other three of its group of
+        // four and does both steps itself.
+        const int h = d >> 1;
+        const bool two = h >= kWave;
 #pragma unroll
         for (int j = 0; j < V; ++j) lds[j * kSortThreads + t] = v[j];
         __syncthreads();
@@ -787,9 +791,17 @@ __device__ __forceinline__ void sort_desc_block(const int* src, int* dst,
         for (int j = 0; j < V; ++j) {
           const int i = j * kSortThreads + t;
           const int o = lds[i ^ d];
-          v[j] = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
+          const int a = keep_max(i, d, size) ? max(v[j], o) : min(v[j], o);
+          if (two) {
+            const int c = lds[i ^ h], e = lds[i ^ h ^ d];
+            const int c1 = keep_max(i ^ h, d, size) ? max(c, e) : min(c, e);
+            v[j] = keep_max(i, h, size) ? max(a, c1) : min(a, c1);
+          } else {
+            v[j] = a;
+          }
         }
         __syncthreads();
+        if (two) d = h;  // both distances done
       }
     }
     // Distances 32 .. 1: the run's direction is the same for the wave.
@@ -991,6 +1003,42 @@ __device__ __forceinline__ void fin_visit_lds(const int* b, int nb, F&& f) {
   }
 }
 
+// The digit holding the kleft-th largest of a wide histogram (one copy of
+// kFinWideBins bins; thread t owns bins kFinWideBins - 1 - 4t - i, i < 4);
+// clears it.
+constexpr int kFinWideBits = 12;
+constexpr int kFinWideBins = 1 << kFinWideBits;
+static_assert(kFinWideBins == kFinWaves * kDigitBins, "shares the waves' copies");
+static_assert(kFinWideBins == 4 * kFinThreads, "four bins per thread");
+
+__device__ __forceinline__ void fin_pick_wide(FinishShared& sh, int kleft) {
+  const int t = threadIdx.x, w = t / kWave;
+  int c[4], local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = (int)sh.h[kFinWideBins - 1 - 4 * t - i];
+    local += c[i];
+  }
+  const int incl_w = wave_scan_incl(local);
+  if (lane() == kWave - 1) sh.scan[w] = incl_w;
+  __syncthreads();
+  int run = incl_w - local;
+#pragma unroll
+  for (int j = 0; j < kFinWaves; ++j) run += j < w ? sh.scan[j] : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = kFinWideBins - 1 - 4 * t - i;
+    if (run + c[i] >= kleft && run < kleft) {
+      sh.pick[0] = b;
+      sh.pick[1] = run;
+      sh.pick[2] = c[i];
+    }
+    run += c[i];
+    sh.h[b] = 0u;
+  }
+  __syncthreads();
+}
+
 // The digit holding the kleft-th largest of the histogram (waves' copies
 // summed; thread t < 256 looks at bin 255 - t); clears the histogram.
 __device__ __forceinline__ void fin_pick(FinishShared& sh, int kleft) {
@@ -1019,26 +1067,28 @@ __device__ __forceinline__ void fin_pick(FinishShared& sh, int kleft) {
 }
 
 // Append the elements of the LDS bucket b[0..nb) for which q holds to
-// dst[base..), kFinRound per thread and round (reads clamped into the
-// array, issued together), placed by fin_round's scan.
+// dst[base..), in one round (reads clamped into the array, issued
+// together), placed by fin_round's scan.
 template <class Q>
 __device__ __forceinline__ void fin_compact(const int* b, int nb, int* dst,
                                             int base, int cap, int* scan,
                                             Q&& q) {
+  // The whole bucket in one round: nb <= kFinBucketCap, N slots per
+  // thread.
+  constexpr int N = kFinBucketCap / kFinThreads;
+  static_assert(N * kFinThreads == kFinBucketCap, "one round covers the bucket");
+  if (nb <= 0) return;
   const int t = threadIdx.x;
   int na = base, nn = 0;
-  for (int r = 0; r < nb; r += kFinRound * kFinThreads) {
-    int x[kFinRound];
-    bool ok[kFinRound];
+  int x[N];
+  bool ok[N];
 #pragma unroll
-    for (int j = 0; j < kFinRound; ++j)
-      x[j] = b[min(r + j * kFinThreads + t, nb - 1)];
+  for (int j = 0; j < N; ++j) x[j] = b[min(j * kFinThreads + t, nb - 1)];
 #pragma unroll
-    for (int j = 0; j < kFinRound; ++j) ok[j] = r + j * kFinThreads + t < nb;
-    fin_round(
-        x, ok, [](int) {}, q, [](int) { return false; }, dst, cap,
-        static_cast<int*>(nullptr), 0, na, nn, scan);
-  }
+  for (int j = 0; j < N; ++j) ok[j] = j * kFinThreads + t < nb;
+  fin_round(
+      x, ok, [](int) {}, q, [](int) { return false; }, dst, cap,
+      static_cast<int*>(nullptr), 0, na, nn, scan);
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
@@ -1067,7 +1117,6 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     sh.nbucket = 0;
   }
   __syncthreads();
-  unsigned* hw = sh.h + w * kDigitBins;
   const unsigned ut = bias(s.thresh);
   // The leading one bits of bias(t) are shared by every candidate.
   const int lead = ~ut == 0u ? 32 : __builtin_clz(~ut);
@@ -1077,9 +1126,13 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   int kleft = k, count = m, nb = 0;
   bool done = false, in_lds = false;
   while (rem > 0 && !done) {
-    const int nbits = rem < 8 ? rem : 8;
+    // Digits of up to 12 bits (one shared histogram of 4096 bins) while
+    // more than 8 bits remain, then the rest (per-wave copies).
+    const bool wide = rem > 8;
+    const int nbits = wide ? min(rem, kFinWideBits) : rem;
     const unsigned dshift = (unsigned)(rem - nbits);
     const unsigned dmask = (1u << nbits) - 1u;
+    unsigned* hw = wide ? sh.h : sh.h + w * kDigitBins;
     if (in_lds) {
       fin_visit_lds(sh.bucket, nb, [&](int x, bool ok, int)
                                        __attribute__((always_inline)) {
@@ -1149,7 +1202,10 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
       });
     }
     __syncthreads();
-    fin_pick(sh, kleft);
+    if (wide)
+      fin_pick_wide(sh, kleft);
+    else
+      fin_pick(sh, kleft);
     const unsigned d = (unsigned)sh.pick[0];
     const int above = sh.pick[1];
     count = sh.pick[2];

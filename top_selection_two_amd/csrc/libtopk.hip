@@ -284,7 +284,7 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
 constexpr int64_t kSampleMinN = (int64_t)1 << 24;
 
 // The candidate buffer of radix selection (kCandCap int32) and, after it,
-// the published sample lists (kSampleGrid * kNeedMax int32), allocated
+// the published sample lists (kSampleGridMax * kNeedMax int32), allocated
 // once per (device, stream) on first use.
 int get_rcand(int dev, hipStream_t stream, int** out) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -293,7 +293,7 @@ int get_rcand(int dev, hipStream_t stream, int** out) {
     if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
     void* p = nullptr;
     const hipError_t e =
-        hipMalloc(&p, (size_t)(kCandCap + kSampleGrid * kNeedMax) *
+        hipMalloc(&p, (size_t)(kCandCap + kSampleGridMax * kNeedMax) *
                           sizeof(int));
     if (e != hipSuccess) {
       debug_hip("hipMalloc(candidates)", e);
@@ -334,20 +334,30 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   // top-k, from the input).
   bool filtered = false;
   const int64_t nvec = (n - pl.head) / 4;
-  if (n >= kSampleMinN && nvec >= kSampleVecs) {
+  if (n >= kSampleMinN && nvec >= (int64_t)kSampleGridMax * kSampleThreads) {
     SampleParams q;
     q.body = reinterpret_cast<const v4i*>(in + pl.head);
     q.nvec = nvec;
-    q.stride = nvec / kSampleVecs;
-    // The sample's share of k, plus four standard deviations and 4.
-    const double ks = (double)k * kSampleVals / (double)n;
-    q.need = (int)std::ceil(ks + 4.0 * std::sqrt(ks) + 4.0);
-    if (q.need > kNeedMax) q.need = kNeedMax;
+    // need = the sample's share of k, plus four standard deviations and 4.
+    // The largest sample whose workgroups' lists (need values each) fit
+    // the last workgroup's kUnionSlots.
+    int grid = kSampleGridMax;
+    int need = 0;
+    for (;;) {
+      const double ks = (double)k * (4.0 * kSampleThreads * grid) / (double)n;
+      need = (int)std::ceil(ks + 4.0 * std::sqrt(ks) + 4.0);
+      if (need > kNeedMax) need = kNeedMax;
+      if (grid * need <= kUnionSlots || grid == 1) break;
+      grid /= 2;
+    }
+    q.grid = grid;
+    q.need = need;
+    q.stride = nvec / ((int64_t)grid * kSampleThreads);
     q.st = sc.rstate;
     q.samp = rcand + kCandCap;
     q.ticket = sc.ticket;
-    rc = launch_threads((const void*)&sample_kernel, kSampleGrid,
-                        kSampleThreads, q, s);
+    rc = launch_threads((const void*)&sample_kernel, grid, kSampleThreads, q,
+                        s);
     if (rc != LIBTOPK_OK) return rc;
     rc = launch((const void*)&filter_kernel<kTileVec>, pl.grid, sp, s);
     if (rc != LIBTOPK_OK) return rc;
