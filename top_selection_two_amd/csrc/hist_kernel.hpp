@@ -449,15 +449,16 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
 // The filter threshold for top-k with large n.  `grid` workgroups read
 // grid * 1024 16-byte vectors spread evenly over the input (one per
 // thread); t is to be the value of rank `need` among the S = grid * 4096
-// sampled values (`need` is k scaled to the sample, with a wide margin).  Each
-// workgroup finds the value of rank `need` among its own samples and
-// publishes its `need` largest; the last workgroup finds the value of rank
-// `need` in the union of those lists, which is that of the whole sample.
-// Both use block_rank: three histogram levels in LDS (the top 12 bits of
-// the biased value, the next 12, the last 8).  The filter pass then copies
-// every value above t aside and counts those equal to it: when at least k
-// values are >= t, the top-k lies among them, whatever t is, so a poor
-// sample costs time, never correctness.
+// sampled values (`need` is k scaled to the sample, with a wide margin).
+// Each workgroup publishes a list that holds its `need` largest samples
+// (usually every sample in the 12-bit bins from its rank-`need` one up);
+// the last workgroup finds the value of rank `need` in the union of those
+// lists, which is that of the whole sample, exactly, with block_rank:
+// three histogram levels in LDS (the top 12 bits of the biased value, the
+// next 12, the last 8).  The filter pass then copies every value above t
+// aside and counts those equal to it: when at least k values are >= t,
+// the top-k lies among them, whatever t is, so a poor sample costs time,
+// never correctness.
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleGridMax = 64;  // workgroups (S = 4096 values each)
 constexpr int kNeedMax = 256;       // largest `need`
@@ -472,13 +473,14 @@ struct SampleParams {
   int need;          // 1 <= need <= kNeedMax, grid * need <= kUnionSlots
   RadixState* st;
   int* samp;         // [kSampleGridMax * kNeedMax] the published lists
+  int* samp_cnt;     // [kSampleGridMax] their lengths
   unsigned* ticket;
 };
 
 struct RankShared {
   unsigned h[kThreshBins];
   int scan[kSampleThreads / kWave];
-  int pick[2];
+  int pick[3];  // bin, count above it, count in it
   int cnt;
   int is_last;
 };
@@ -511,6 +513,7 @@ __device__ __forceinline__ void sample_pick(RankShared& sh, int need) {
     if ((run >= need && before < need) || (b == 0 && run < need)) {
       sh.pick[0] = b;
       sh.pick[1] = before;
+      sh.pick[2] = c[i];
     }
     sh.h[b] = 0u;
   }
@@ -569,33 +572,54 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     u[3] = bias(d.w);
   }
   __syncthreads();
-  int a;
-  const unsigned v = block_rank<4>(u, 0xfu, p.need, sh, &a);
-  // Publish this workgroup's `need` largest: the a values above v (one
-  // LDS atomic per wave and slot), then need - a copies of v.
+  // This workgroup's list, at most cap = min(kUnionSlots / grid, kNeedMax)
+  // (>= need) values that include its `need` largest: every sample in the 12-bit
+  // bins from the one holding its rank-`need` value up (one histogram
+  // level), or, when more than cap share those bins, exactly the `need`
+  // largest (all three levels).
+  const int cap = min(kUnionSlots / p.grid, kNeedMax);
   int* mine = p.samp + blockIdx.x * kNeedMax;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool q = u[j] > v;
+  for (int j = 0; j < 4; ++j) atomicAdd(&sh.h[u[j] >> 20], 1u);
+  __syncthreads();
+  sample_pick(sh, p.need);
+  const unsigned b1 = (unsigned)sh.pick[0];
+  const int inb = sh.pick[1] + sh.pick[2];
+  int len;
+  // One LDS atomic per wave and slot places the appended values.
+  auto publish = [&](bool q, unsigned x) __attribute__((always_inline)) {
     const uint64_t b = ballot(q);
-    if (b == 0) continue;
+    if (b == 0) return;
     int base = 0;
     if (lane() == 0) base = atomicAdd(&sh.cnt, popc(b));
     base = uni(base);
     const int pos = base + lanes_below(b);
-    if (q && pos < kNeedMax) st_agent(mine + pos, (int)u[j]);
+    if (q && pos < cap) st_agent(mine + pos, (int)x);
+  };
+  if (inb <= cap) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) publish((u[j] >> 20) >= b1, u[j]);
+    len = inb;
+  } else {
+    int a;
+    const unsigned v = block_rank<4>(u, 0xfu, p.need, sh, &a);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) publish(u[j] > v, u[j]);
+    for (int i = a + t; i < p.need; i += kSampleThreads)
+      st_agent(mine + i, (int)v);
+    len = p.need;
   }
-  for (int i = a + t; i < p.need; i += kSampleThreads) st_agent(mine + i, (int)v);
+  if (t == 0) st_agent(p.samp_cnt + blockIdx.x, len);
   if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
 
-  // The union of the lists: grid * need <= kUnionSlots values.
+  // The union of the lists: slot i is entry i % cap of list i / cap.
   unsigned w[4], valid = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = j * kSampleThreads + t;
-    const int g = i / p.need, r = i - g * p.need;
+    const int g = i / cap, r = i - g * cap;
     w[j] = 0u;
-    if (g < p.grid) {
+    if (g < p.grid && r < ld_agent(p.samp_cnt + g)) {
       w[j] = (unsigned)ld_agent(p.samp + g * kNeedMax + r);
       valid |= 1u << j;
     }

@@ -284,7 +284,8 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
 constexpr int64_t kSampleMinN = (int64_t)1 << 24;
 
 // The candidate buffer of radix selection (kCandCap int32) and, after it,
-// the published sample lists (kSampleGridMax * kNeedMax int32), allocated
+// the published sample lists and their lengths (kSampleGridMax *
+// (kNeedMax + 1) int32), allocated
 // once per (device, stream) on first use.
 int get_rcand(int dev, hipStream_t stream, int** out) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -293,7 +294,7 @@ int get_rcand(int dev, hipStream_t stream, int** out) {
     if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
     void* p = nullptr;
     const hipError_t e =
-        hipMalloc(&p, (size_t)(kCandCap + kSampleGridMax * kNeedMax) *
+        hipMalloc(&p, (size_t)(kCandCap + kSampleGridMax * (kNeedMax + 1)) *
                           sizeof(int));
     if (e != hipSuccess) {
       debug_hip("hipMalloc(candidates)", e);
@@ -355,6 +356,7 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     q.stride = nvec / ((int64_t)grid * kSampleThreads);
     q.st = sc.rstate;
     q.samp = rcand + kCandCap;
+    q.samp_cnt = q.samp + kSampleGridMax * kNeedMax;
     q.ticket = sc.ticket;
     rc = launch_threads((const void*)&sample_kernel, grid, kSampleThreads, q,
                         s);
