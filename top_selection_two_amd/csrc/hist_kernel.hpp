@@ -451,11 +451,10 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
 // thread); t is to be the value of rank `need` among the S = grid * 4096
 // sampled values (`need` is k scaled to the sample, with a wide margin).
 // Each workgroup publishes a list that holds its `need` largest samples
-// (usually every sample in the 12-bit bins from its rank-`need` one up);
+// (usually every sample in the top-digit bins from its rank-`need` one up);
 // the last workgroup finds the value of rank `need` in the union of those
-// lists, which is that of the whole sample, exactly, with block_rank:
-// three histogram levels in LDS (the top 12 bits of the biased value, the
-// next 12, the last 8).  The filter pass then copies every value above t
+// lists, which is that of the whole sample, exactly, with block_rank: four
+// 8-bit digit levels of LDS histograms ([Radix] §3.2's digits).  The filter pass then copies every value above t
 // aside and counts those equal to it: when at least k values are >= t,
 // the top-k lies among them, whatever t is, so a poor sample costs time,
 // never correctness.
@@ -463,8 +462,6 @@ constexpr int kSampleThreads = 1024;
 constexpr int kSampleGridMax = 64;  // workgroups (S = 4096 values each)
 constexpr int kNeedMax = 256;       // largest `need`
 constexpr int kUnionSlots = 4 * kSampleThreads;  // grid * need <= this
-constexpr int kThreshBins = 4096;
-
 struct SampleParams {
   const v4i* body;   // the 16-byte-aligned body of the input
   int64_t nvec;      // vectors in it
@@ -478,42 +475,35 @@ struct SampleParams {
 };
 
 struct RankShared {
-  unsigned h[kThreshBins];
+  unsigned h[kDigitBins];
   int scan[kSampleThreads / kWave];
   int pick[3];  // bin, count above it, count in it
   int cnt;
   int is_last;
 };
 
-// Thread t owns bins kThreshBins - 1 - 4t - i, i < 4 (top bin first); find
-// the highest bin whose suffix count reaches `need` (bin 0 if none does)
-// and the count above it.  h is cleared on the way.
-__device__ __forceinline__ void sample_pick(RankShared& sh, int need) {
-  constexpr int kPer = kThreshBins / kSampleThreads;
+// The highest of 256 bins (one LDS copy, h[0..256)) whose suffix count
+// reaches `need` (bin 0 if none does), the count above it and the count in
+// it, into sh.pick; threads t < 256 look at bin 255 - t.  Clears h.
+__device__ __forceinline__ void pick256(RankShared& sh, int need) {
   const int t = threadIdx.x, w = t / kWave;
-  int c[kPer], local = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    c[i] = (int)sh.h[kThreshBins - 1 - kPer * t - i];
-    local += c[i];
+  const int b = kDigitBins - 1 - t;
+  int c = 0, incl_w = 0;
+  if (t < kDigitBins) {
+    c = (int)sh.h[b];
+    incl_w = wave_scan_incl(c);
+    if (lane() == kWave - 1) sh.scan[w] = incl_w;
   }
-  const int incl_w = wave_scan_incl(local);
-  if (lane() == kWave - 1) sh.scan[w] = incl_w;
   __syncthreads();
-  int run = incl_w - local;
-  // All totals read at once (a fixed count the compiler issues together).
+  if (t < kDigitBins) {
+    int incl = incl_w;
 #pragma unroll
-  for (int j = 0; j < kSampleThreads / kWave; ++j)
-    run += j < w ? sh.scan[j] : 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = kThreshBins - 1 - kPer * t - i;
-    const int before = run;
-    run += c[i];
-    if ((run >= need && before < need) || (b == 0 && run < need)) {
+    for (int j = 0; j < kDigitBins / kWave; ++j) incl += j < w ? sh.scan[j] : 0;
+    const int above = incl - c;
+    if ((incl >= need && above < need) || (b == 0 && incl < need)) {
       sh.pick[0] = b;
-      sh.pick[1] = before;
-      sh.pick[2] = c[i];
+      sh.pick[1] = above;
+      sh.pick[2] = c;
     }
     sh.h[b] = 0u;
   }
@@ -522,42 +512,38 @@ __device__ __forceinline__ void sample_pick(RankShared& sh, int need) {
 
 // The biased value v of rank `need` (1 = the largest) among the PER values
 // each thread of the workgroup holds (slot j only where bit j of `valid`
-// is set), and in *above the number of values greater than v.  There are
-// at least `need` valid values.  sh.h is zero on entry and on return.
+// is set), and in *above the number of values greater than v: four 8-bit
+// digit levels, each an LDS histogram of the values whose higher digits
+// equal those chosen so far.  There are at least `need` valid values.
+// sh.h[0..256) is zero on entry and on return.
 template <int PER>
 __device__ __forceinline__ unsigned block_rank(const unsigned (&u)[PER],
                                                unsigned valid, int need,
                                                RankShared& sh, int* above) {
+  unsigned prefix = 0u;
+  int a = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (valid & (1u << j)) atomicAdd(&sh.h[u[j] >> 20], 1u);
-  __syncthreads();
-  sample_pick(sh, need);
-  const unsigned b1 = (unsigned)sh.pick[0];
-  int a = sh.pick[1];
+  for (int level = 0; level < 4; ++level) {
+    const unsigned shift = 24u - 8u * level;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((valid & (1u << j)) && (u[j] >> 20) == b1)
-      atomicAdd(&sh.h[(u[j] >> 8) & 0xfffu], 1u);
-  __syncthreads();
-  sample_pick(sh, need - a);
-  const unsigned b12 = (b1 << 12) | (unsigned)sh.pick[0];
-  a += sh.pick[1];
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((valid & (1u << j)) && (u[j] >> 8) == b12)
-      atomicAdd(&sh.h[u[j] & 0xffu], 1u);
-  __syncthreads();
-  sample_pick(sh, need - a);
-  const unsigned v = (b12 << 8) | (unsigned)sh.pick[0];
-  *above = a + sh.pick[1];
-  return v;
+    for (int j = 0; j < PER; ++j) {
+      const bool in = (valid & (1u << j)) &&
+                      (level == 0 || (u[j] >> (shift + 8u)) == (prefix >> (shift + 8u)));
+      if (in) atomicAdd(&sh.h[(u[j] >> shift) & 0xffu], 1u);
+    }
+    __syncthreads();
+    pick256(sh, need - a);
+    prefix |= (unsigned)sh.pick[0] << shift;
+    a += sh.pick[1];
+  }
+  *above = a;
+  return prefix;
 }
 
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) {
   __shared__ RankShared sh;
   const int t = threadIdx.x;
-  for (int i = t; i < kThreshBins; i += kSampleThreads) sh.h[i] = 0u;
+  for (int i = t; i < kDigitBins; i += kSampleThreads) sh.h[i] = 0u;
   if (t == 0) sh.cnt = 0;
   unsigned u[4];
   {
@@ -573,16 +559,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   }
   __syncthreads();
   // This workgroup's list, at most cap = min(kUnionSlots / grid, kNeedMax)
-  // (>= need) values that include its `need` largest: every sample in the 12-bit
-  // bins from the one holding its rank-`need` value up (one histogram
-  // level), or, when more than cap share those bins, exactly the `need`
-  // largest (all three levels).
+  // (>= need) values that include its `need` largest: every sample in the
+  // 8-bit bins (top digit) from the one holding its rank-`need` value up
+  // (one histogram level), or, when more than cap share those bins,
+  // exactly the `need` largest (all four levels).
   const int cap = min(kUnionSlots / p.grid, kNeedMax);
   int* mine = p.samp + blockIdx.x * kNeedMax;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) atomicAdd(&sh.h[u[j] >> 20], 1u);
+  for (int j = 0; j < 4; ++j) atomicAdd(&sh.h[u[j] >> 24], 1u);
   __syncthreads();
-  sample_pick(sh, p.need);
+  pick256(sh, p.need);
   const unsigned b1 = (unsigned)sh.pick[0];
   const int inb = sh.pick[1] + sh.pick[2];
   int len;
@@ -598,7 +584,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   };
   if (inb <= cap) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) publish((u[j] >> 20) >= b1, u[j]);
+    for (int j = 0; j < 4; ++j) publish((u[j] >> 24) >= b1, u[j]);
     len = inb;
   } else {
     int a;
@@ -613,16 +599,21 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
 
   // The union of the lists: slot i is entry i % cap of list i / cap.
+  // Every slot's value and its list's length are loaded together (slots
+  // past a list's length hold stale values and are masked out).
   unsigned w[4], valid = 0;
+  int len_of[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = j * kSampleThreads + t;
-    const int g = i / cap, r = i - g * cap;
-    w[j] = 0u;
-    if (g < p.grid && r < ld_agent(p.samp_cnt + g)) {
-      w[j] = (unsigned)ld_agent(p.samp + g * kNeedMax + r);
-      valid |= 1u << j;
-    }
+    const int g = min(i / cap, p.grid - 1), r = i - (i / cap) * cap;
+    w[j] = (unsigned)ld_agent(p.samp + g * kNeedMax + r);
+    len_of[j] = ld_agent(p.samp_cnt + g);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = j * kSampleThreads + t;
+    if (i / cap < p.grid && i - (i / cap) * cap < len_of[j]) valid |= 1u << j;
   }
   int a2;
   const unsigned tv = block_rank<4>(w, valid, p.need, sh, &a2);
