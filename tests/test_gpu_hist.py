@@ -13,7 +13,8 @@ stops after the first digit (the whole bucket is needed), k = n, and the
 positions drive each way through the sampled path: the one-workgroup
 finish with and without copies of the threshold, a copy too large for it,
 a copy too large for the candidate buffer, and a sample whose threshold is
-too high.
+too high; and the finish's placement by the first digit against its sort,
+with distinct values and with ties, around k = 4096.
 """
 import numpy as np
 import pytest
@@ -305,3 +306,27 @@ def test_sampled_misaligned_and_ties(ltk, rng):
     x = rng.integers(0, 1 << 16, size=N_SAMPLED + 12345).astype(np.int32)
     check_topk(ltk, x, 5000, offset=1)
     check_topk(ltk, x, 16384, offset=3)
+
+
+@pytest.mark.parametrize("hi", [None, 2 ** 24, 2 ** 20])
+@pytest.mark.parametrize("k", [129, 1000, 4096, 4097])
+def test_sampled_placement_and_ties(ltk, rng, hi, k):
+    # The one-workgroup finish places the result by its first digit's
+    # counts when k <= 4096 and no bin is crowded, and sorts otherwise:
+    # distinct values, occasional ties and heavy ties, around k = 4096.
+    if hi is None:
+        x = rng.integers(I32_MIN, I32_MAX, size=N_SAMPLED, dtype=np.int64,
+                         endpoint=True).astype(np.int32)
+    else:
+        x = rng.integers(0, hi, size=N_SAMPLED).astype(np.int32)
+    check_topk(ltk, x, k)
+
+
+@pytest.mark.parametrize("span", [2 ** 20, 2 ** 18])
+@pytest.mark.parametrize("k", [200, 4096])
+def test_sampled_placement_with_equal_values(ltk, rng, span, k):
+    # Values just below INT32_MAX, each about n / span times: the copy's
+    # bins each hold one value many times over (about 16 times: placed by
+    # the first digit; about 64: sorted instead).
+    x = (I32_MAX - rng.integers(0, span, size=N_SAMPLED)).astype(np.int32)
+    check_topk(ltk, x, k)

@@ -871,6 +871,7 @@ struct FinishShared {
   int scan[kFinWaves];
   int ntop, nbucket;
   int pick[3];  // digit, count above it, count in it
+  int maxc;     // the largest count of the first digit's bins
 };
 
 // Visit cand[0..m) as f(x, ok, i), kFinRound 16-byte vectors per thread
@@ -1023,16 +1024,28 @@ __device__ __forceinline__ void fin_visit_lds(const int* b, int nb, F&& f) {
 // clears it.
 constexpr int kFinWideBits = 12;
 constexpr int kFinWideBins = 1 << kFinWideBits;
+// Placement by the first digit: up to this k (its staging area is the last
+// quarter of `top`) and this many values in any bin.
+constexpr int kPlaceMaxK = kMaxKSelect - 3 * kFinWideBins;
+constexpr int kPlaceBinMax = 32;
 static_assert(kFinWideBins == kFinWaves * kDigitBins, "shares the waves' copies");
 static_assert(kFinWideBins == 4 * kFinThreads, "four bins per thread");
 
-__device__ __forceinline__ void fin_pick_wide(FinishShared& sh, int kleft) {
+// With `rec`, it also records each bin's count (rec[kFinWideBins + b]) and
+// the count of the bins above it (rec[b]), and the largest count in
+// sh.maxc.
+__device__ __forceinline__ void fin_pick_wide(FinishShared& sh, int kleft,
+                                              int* rec) {
   const int t = threadIdx.x, w = t / kWave;
   int c[4], local = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     c[i] = (int)sh.h[kFinWideBins - 1 - 4 * t - i];
     local += c[i];
+  }
+  if (rec) {
+    const int mc = wave_max(max(max(c[0], c[1]), max(c[2], c[3])));
+    if (lane() == 0) atomicMax(&sh.maxc, mc);
   }
   const int incl_w = wave_scan_incl(local);
   if (lane() == kWave - 1) sh.scan[w] = incl_w;
@@ -1047,6 +1060,10 @@ __device__ __forceinline__ void fin_pick_wide(FinishShared& sh, int kleft) {
       sh.pick[0] = b;
       sh.pick[1] = run;
       sh.pick[2] = c[i];
+    }
+    if (rec) {
+      rec[b] = run;
+      rec[kFinWideBins + b] = c[i];
     }
     run += c[i];
     sh.h[b] = 0u;
@@ -1106,6 +1123,56 @@ __device__ __forceinline__ void fin_compact(const int* b, int nb, int* dst,
       static_cast<int*>(nullptr), 0, na, nn, scan);
 }
 
+// Placement by the first digit, instead of gathering and sorting.  The
+// first (wide) digit pass counted every bin of the copy, and a bin above
+// b0 (the one holding the k-th largest) holds only top-k members, so the
+// output position of a member of bin b > b0 is the count of the bins
+// above b plus its rank inside b; b0's members (those `wanted`) start at
+// above0.  Members are grouped by bin in LDS (a cursor per bin), then each
+// finds its rank among its bin's members by counting (larger values, or
+// equal ones at a lower slot).  `fill` copies of g end the result.  Taken
+// when k <= kPlaceMaxK and no bin holds more than kPlaceBinMax values.
+template <class W>
+__device__ __forceinline__ void fin_place(FinishShared& sh, int* out, int k,
+                                          int nb, unsigned shift0,
+                                          unsigned mask0, int b0, int above0,
+                                          W&& wanted, int fill, int g) {
+  const int t = threadIdx.x;
+  const int* off = sh.top;                        // bins above, per bin
+  const int* cnt = sh.top + kFinWideBins;         // count, per bin
+  int* cur = sh.top + 2 * kFinWideBins;           // cursor, per bin
+  int* stage = sh.top + 3 * kFinWideBins;         // members, by bin
+  for (int i = t; i < kFinWideBins; i += kFinThreads) cur[i] = 0;
+  __syncthreads();
+  auto bin = [&](int x) __attribute__((always_inline)) {
+    return (int)((bias(x) >> shift0) & mask0);
+  };
+  for (int i = t; i < nb; i += kFinThreads) {
+    const int x = sh.bucket[i];
+    const int b = bin(x);
+    if (b > b0 || (b == b0 && wanted(x))) {
+      const int pos = (b > b0 ? off[b] : above0) + atomicAdd(&cur[b], 1);
+      if (pos < kPlaceMaxK) stage[pos] = x;
+    }
+  }
+  __syncthreads();
+  const int n0 = cur[b0];
+  const int members = min(above0 + n0, k);
+  for (int q = t; q < members; q += kFinThreads) {
+    const int x = stage[q];
+    const int b = bin(x);
+    const int lo = b > b0 ? off[b] : above0;
+    const int n = b > b0 ? cnt[b] : n0;
+    int r = 0;
+    for (int j = lo; j < lo + n; ++j) {
+      const int y = stage[j];
+      r += (y > x || (y == x && j < q)) ? 1 : 0;
+    }
+    out[lo + r] = x;
+  }
+  for (int j = k - fill + t; j < k; j += kFinThreads) out[j] = g;
+}
+
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     SelectParams p) {
   __shared__ FinishShared sh;
@@ -1130,6 +1197,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   if (t == 0) {
     sh.ntop = 0;
     sh.nbucket = 0;
+    sh.maxc = 0;
   }
   __syncthreads();
   const unsigned ut = bias(s.thresh);
@@ -1140,6 +1208,12 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   int rem = 32 - lead;  // bits below the prefix
   int kleft = k, count = m, nb = 0;
   bool done = false, in_lds = false;
+  // Placement by the first digit (see below): that digit's window, the
+  // bin holding the k-th largest and the count above it.
+  bool place = false;
+  unsigned shift0 = 0u, mask0 = 0u;
+  int b0 = 0, above0 = 0;
+  bool first = true;
   while (rem > 0 && !done) {
     // Digits of up to 12 bits (one shared histogram of 4096 bins) while
     // more than 8 bits remain, then the rest (per-wave copies).
@@ -1188,6 +1262,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
       }
       in_lds = true;
       nb = m;
+      place = first && wide && k <= kPlaceMaxK;
     } else if (count <= kFinBucketCap) {
       // The bucket fits now: keep it in LDS, and the values above it (all
       // in the top-k) in top.
@@ -1218,12 +1293,20 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
     __syncthreads();
     if (wide)
-      fin_pick_wide(sh, kleft);
+      fin_pick_wide(sh, kleft, place && first ? sh.top : nullptr);
     else
       fin_pick(sh, kleft);
     const unsigned d = (unsigned)sh.pick[0];
     const int above = sh.pick[1];
     count = sh.pick[2];
+    if (place && first) {
+      place = sh.maxc <= kPlaceBinMax;
+      shift0 = dshift;
+      mask0 = dmask;
+      b0 = (int)d;
+      above0 = above;
+    }
+    first = false;
     prefix |= d << dshift;
     mask |= dmask << dshift;
     kleft -= above;
@@ -1237,6 +1320,12 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     const unsigned key = bias(x) & mask;
     return key > prefix || (done && key == prefix);
   };
+  if (place) {
+    fin_place(sh, p.out, k, nb, shift0, mask0, b0, above0, wanted,
+              done ? 0 : kleft, unbias(prefix));
+    if (t == 0) p.st->fast = 0;
+    return;
+  }
   if (in_lds) {
     fin_compact(sh.bucket, nb, sh.top, sh.ntop, k, sh.scan, wanted);
   } else {
