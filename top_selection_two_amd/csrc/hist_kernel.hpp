@@ -850,14 +850,17 @@ __device__ __forceinline__ void sort_desc(const int* src, int* dst, int k,
 // Otherwise select from the m candidates (m <= kFinishMax) here, with
 // barriers instead of device counters between digits.  Every candidate is
 // above t, so all of them share the leading one bits of bias(t): those
-// bits start the prefix, and 8-bit digits below them follow ([Radix]
-// §3.2's digits, one LDS histogram per wave).  When the copy fits in LDS
-// (kFinBucketCap) the first digit pass copies it there and later passes
-// read LDS; otherwise passes read the copy until a chosen bucket fits,
-// and that pass keeps the bucket in LDS and the values above it as known
-// members of the top-k.  The values above the final bucket (or the whole
-// bucket, when it is needed entire), copies of g for what is left, and a
-// bitonic sort in LDS finish the top-k.
+// bits start the prefix, and the digits below them follow ([Radix]
+// §3.2's digits): up to 12 bits in one shared 4096-bin histogram while
+// more than 8 bits remain, then 8-bit digits with one LDS histogram per
+// wave.  When the copy fits in LDS (kFinBucketCap) the first digit pass
+// copies it there and later passes read LDS; otherwise passes read the
+// copy until a chosen bucket fits, and that pass keeps the bucket in LDS
+// and the values above it as known members of the top-k.  The result is
+// then placed by the first digit's counts (fin_place) when k and the bins
+// are small enough, or else gathered (the values above the final bucket,
+// or the whole bucket when it is needed entire, and copies of g) and
+// sorted by a bitonic network in LDS.
 constexpr int kFinThreads = kSortThreads;
 constexpr int kFinWaves = kFinThreads / kWave;
 // LDS: top (64 KiB) + bucket (76 KiB) + histograms (16 KiB) fill the
