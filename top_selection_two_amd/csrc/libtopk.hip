@@ -280,8 +280,12 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
-// Inputs from this size on are sampled for a filter threshold.
-constexpr int64_t kSampleMinN = (int64_t)1 << 24;
+// Inputs from this size on are sampled for a filter threshold (measured
+// on top-1000 and top-16384 of 1e6 .. 1.6e7 uniform int32: below 2^21 the
+// digit passes are as fast; for k above kPlaceMaxK, whose finish sorts
+// instead of placing, below 2^22).
+constexpr int64_t kSampleMinN = (int64_t)1 << 21;
+constexpr int64_t kSampleMinNSorted = (int64_t)1 << 22;
 
 // The candidate buffer of radix selection (kCandCap int32) and, after it,
 // the published sample lists and their lengths (kSampleGridMax *
@@ -335,7 +339,10 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   // top-k, from the input).
   bool filtered = false;
   const int64_t nvec = (n - pl.head) / 4;
-  if (n >= kSampleMinN && nvec >= (int64_t)kSampleGridMax * kSampleThreads) {
+  const bool sampled =
+      n >= (k <= kPlaceMaxK ? kSampleMinN : kSampleMinNSorted) &&
+      nvec >= (int64_t)kSampleGridMax * kSampleThreads;
+  if (sampled) {
     SampleParams q;
     q.body = reinterpret_cast<const v4i*>(in + pl.head);
     q.nvec = nvec;
