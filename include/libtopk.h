@@ -91,11 +91,11 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
  * k-th largest value, a gather pass collects the values above it, and one
  * workgroup sorts the k results.  Once a digit leaves fewer than 2^22
  * candidates they are copied aside and the remaining passes read only
- * them.  From n = 2^21 on (2^22 for k > 4096), a sample first fixes a
- * threshold and a filter pass copies the values above it aside; when that
- * copy is small (the usual case) one workgroup selects the top-k from it,
- * the digit passes return at once, and the input is read once.  Six
- * stream-ordered launches, eight on sampled inputs.
+ * them.  From n = 2^18 on (when n is large enough for k), a sample first
+ * fixes a threshold and a filter pass copies the values above it aside;
+ * when that copy is small (the usual case) one workgroup selects the
+ * top-k from it, the digit passes return at once, and the input is read
+ * once.  Six stream-ordered launches, eight on sampled inputs.
  *
  *   in   device, int32[n], read once (k <= LIBTOPK_MAX_K)
  *   n    number of elements, 1 <= n <= 2^32

@@ -9,7 +9,7 @@ misaligned starts, n = 0, repeated calls and two streams (the device
 counters clean themselves).  Top-k by radix selection covers k from 129 to
 16384, ties at the k-th value, sorted and all-equal inputs, selection that
 stops after the first digit (the whole bucket is needed), k = n, and the
-1e8 workload.  At 2^24 elements (the sampled path starts at 2^21), inputs
+1e8 workload.  At 2^24 elements (the sampled path starts at 2^18), inputs
 built around the sampled positions drive each way through it: the one-workgroup
 finish with and without copies of the threshold, a copy too large for it,
 a copy too large for the candidate buffer, and a sample whose threshold is
@@ -229,7 +229,7 @@ def test_large_k_repeated_and_mixed_with_small_k(ltk, rng):
 
 
 # ------------------------------------------- the sampled path (n = 2^24)
-# From 2^21 elements on, a strided sample of 16-byte vectors (16, 32 or
+# From 2^18 elements on, a strided sample of 16-byte vectors (16, 32 or
 # 64 thousand of them, by k) sets a threshold t and a filter pass copies
 # the values above t.  With an aligned input of n = 2^24 the sample reads
 # elements s i .. s i + 3 with a stride s of 1024, 512 or 256, all within
@@ -332,13 +332,15 @@ def test_sampled_placement_with_equal_values(ltk, rng, span, k):
     check_topk(ltk, x, k)
 
 
-@pytest.mark.parametrize("n,k", [(2 ** 21 - 1, 1000), (2 ** 21, 1000),
-                                 (2 ** 21 + 5, 129), (3_000_000, 4096),
-                                 (3_000_000, 5000), (2 ** 22, 5000),
+@pytest.mark.parametrize("n,k", [(2 ** 18 - 1, 1000), (2 ** 18, 1000),
+                                 (2 ** 18 + 5, 129), (300_000, 16384),
+                                 (600_000, 5000), (1_000_000, 16384),
+                                 (3_000_000, 4096), (3_000_000, 5000),
                                  (6_000_000, 16384)])
 def test_sampling_thresholds(ltk, rng, n, k):
     # Around the sizes where the sampled path takes over from the digit
-    # passes (2^21, and 2^22 for k > 4096): both ways agree with the oracle.
+    # passes (2^18, and about 334 k for large k): both ways agree with the
+    # oracle, with distinct values and with ties, aligned or not.
     x = rng.integers(I32_MIN, I32_MAX, size=n, dtype=np.int64,
                      endpoint=True).astype(np.int32)
     check_topk(ltk, x, k)

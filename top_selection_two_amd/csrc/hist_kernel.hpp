@@ -1027,9 +1027,9 @@ __device__ __forceinline__ void fin_visit_lds(const int* b, int nb, F&& f) {
 // clears it.
 constexpr int kFinWideBits = 12;
 constexpr int kFinWideBins = 1 << kFinWideBits;
-// Placement by the first digit: up to this k (its staging area is the last
-// quarter of `top`) and this many values in any bin.
-constexpr int kPlaceMaxK = kMaxKSelect - 3 * kFinWideBins;
+// Placement by the first digit: staged in LDS up to this k (the last
+// quarter of `top`), and taken while no bin holds more than kPlaceBinMax.
+constexpr int kPlaceMaxK = kMaxKSelect - 3 * kFinWideBins;  // LDS staging
 constexpr int kPlaceBinMax = 32;
 static_assert(kFinWideBins == kFinWaves * kDigitBins, "shares the waves' copies");
 static_assert(kFinWideBins == 4 * kFinThreads, "four bins per thread");
@@ -1131,48 +1131,82 @@ __device__ __forceinline__ void fin_compact(const int* b, int nb, int* dst,
 // b0 (the one holding the k-th largest) holds only top-k members, so the
 // output position of a member of bin b > b0 is the count of the bins
 // above b plus its rank inside b; b0's members (those `wanted`) start at
-// above0.  Members are grouped by bin in LDS (a cursor per bin), then each
-// finds its rank among its bin's members by counting (larger values, or
-// equal ones at a lower slot).  `fill` copies of g end the result.  Taken
-// when k <= kPlaceMaxK and no bin holds more than kPlaceBinMax values.
-template <class W>
-__device__ __forceinline__ void fin_place(FinishShared& sh, int* out, int k,
-                                          int nb, unsigned shift0,
-                                          unsigned mask0, int b0, int above0,
-                                          W&& wanted, int fill, int g) {
+// above0.  Members are grouped by bin in a staging area (a cursor per bin
+// in LDS), then each finds its rank among its bin's members by counting
+// (larger values, or equal ones at a lower slot), and after a barrier all
+// are written to their places.  The staging area is LDS for k <=
+// kPlaceMaxK; for larger k it is `out` itself (__syncthreads orders global
+// memory within the workgroup too), copied to the free bucket area in LDS
+// for the ranking, and the places are written after a barrier.  The members are read from the LDS
+// copy (SRC_LDS) or from the copy in memory.  `fill` copies of g end the
+// result.  Taken when no first-digit bin holds more than kPlaceBinMax
+// values.
+constexpr int kPlaceSlots = kMaxKSelect / kFinThreads;  // per thread
+
+template <bool GSTAGE, bool SRC_LDS, class W>
+__device__ __forceinline__ void fin_place(FinishShared& sh, const int* cand,
+                                          int m, int nb, int* out, int k,
+                                          unsigned shift0, unsigned mask0,
+                                          int b0, int above0, W&& wanted,
+                                          int fill, int g) {
   const int t = threadIdx.x;
   const int* off = sh.top;                        // bins above, per bin
   const int* cnt = sh.top + kFinWideBins;         // count, per bin
   int* cur = sh.top + 2 * kFinWideBins;           // cursor, per bin
-  int* stage = sh.top + 3 * kFinWideBins;         // members, by bin
+  int* stage = GSTAGE ? out : sh.top + 3 * kFinWideBins;
+  const int cap = GSTAGE ? k : kPlaceMaxK;
   for (int i = t; i < kFinWideBins; i += kFinThreads) cur[i] = 0;
   __syncthreads();
   auto bin = [&](int x) __attribute__((always_inline)) {
     return (int)((bias(x) >> shift0) & mask0);
   };
-  for (int i = t; i < nb; i += kFinThreads) {
-    const int x = sh.bucket[i];
+  auto group = [&](int x, bool ok, int) __attribute__((always_inline)) {
     const int b = bin(x);
-    if (b > b0 || (b == b0 && wanted(x))) {
+    if (ok && (b > b0 || (b == b0 && wanted(x)))) {
       const int pos = (b > b0 ? off[b] : above0) + atomicAdd(&cur[b], 1);
-      if (pos < kPlaceMaxK) stage[pos] = x;
+      if (pos < cap) stage[pos] = x;
     }
-  }
+  };
+  if (SRC_LDS)
+    fin_visit_lds(sh.bucket, nb, group);
+  else
+    fin_visit_copy(cand, m, group);
   __syncthreads();
   const int n0 = cur[b0];
   const int members = min(above0 + n0, k);
-  for (int q = t; q < members; q += kFinThreads) {
-    const int x = stage[q];
-    const int b = bin(x);
-    const int lo = b > b0 ? off[b] : above0;
-    const int n = b > b0 ? cnt[b] : n0;
-    int r = 0;
-    for (int j = lo; j < lo + n; ++j) {
-      const int y = stage[j];
-      r += (y > x || (y == x && j < q)) ? 1 : 0;
-    }
-    out[lo + r] = x;
+  if (GSTAGE) {
+    // The ranking reads each bin's members many times over: from LDS, not
+    // memory.  The bucket area is free by now (members <= k <=
+    // kFinBucketCap).
+    static_assert(kMaxKSelect <= kFinBucketCap, "bucket area holds k values");
+    for (int i = t; i < members; i += kFinThreads) sh.bucket[i] = stage[i];
+    __syncthreads();
+    stage = sh.bucket;
   }
+  int fx[kPlaceSlots], fp[kPlaceSlots];
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j) {
+    const int q = j * kFinThreads + t;
+    fp[j] = -1;
+    fx[j] = 0;
+    if (q < members) {
+      const int x = stage[q];
+      const int b = bin(x);
+      const int lo = b > b0 ? off[b] : above0;
+      const int n = b > b0 ? cnt[b] : n0;
+      int r = 0;
+      for (int i = lo; i < lo + n; ++i) {
+        const int y = stage[i];
+        r += (y > x || (y == x && i < q)) ? 1 : 0;
+      }
+      fx[j] = x;
+      fp[j] = lo + r;
+    }
+  }
+  __syncthreads();  // every read of the staging area comes first
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j)
+    if (fp[j] >= 0) out[fp[j]] = fx[j];
   for (int j = k - fill + t; j < k; j += kFinThreads) out[j] = g;
 }
 
@@ -1213,7 +1247,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   bool done = false, in_lds = false;
   // Placement by the first digit (see below): that digit's window, the
   // bin holding the k-th largest and the count above it.
-  bool place = false;
+  bool place = false, place_lds = false;  // place_lds: the copy is in LDS
   unsigned shift0 = 0u, mask0 = 0u;
   int b0 = 0, above0 = 0;
   bool first = true;
@@ -1265,7 +1299,8 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
       }
       in_lds = true;
       nb = m;
-      place = first && wide && k <= kPlaceMaxK;
+      place = first && wide;
+      place_lds = place;
     } else if (count <= kFinBucketCap) {
       // The bucket fits now: keep it in LDS, and the values above it (all
       // in the top-k) in top.
@@ -1282,7 +1317,9 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
           [&](int x) __attribute__((always_inline)) {
             return (bias(x) & mask) > prefix;
           },
-          sh.bucket, kFinBucketCap, sh.top, k, &na, &nt, sh.scan);
+          // (top holds the placement's bin counts when placing: the
+          // values above are then left for the placement to find)
+          sh.bucket, kFinBucketCap, sh.top, place ? 0 : k, &na, &nt, sh.scan);
       in_lds = true;
       nb = min(na, kFinBucketCap);
       if (t == 0) sh.ntop = nt;
@@ -1293,6 +1330,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
         if (ok && (u & mask) == prefix)
           atomicAdd(&hw[(u >> dshift) & dmask], 1u);
       });
+      if (first) place = wide;
     }
     __syncthreads();
     if (wide)
@@ -1324,8 +1362,22 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     return key > prefix || (done && key == prefix);
   };
   if (place) {
-    fin_place(sh, p.out, k, nb, shift0, mask0, b0, above0, wanted,
-              done ? 0 : kleft, unbias(prefix));
+    const int fill = done ? 0 : kleft, g = unbias(prefix);
+    if (k <= kPlaceMaxK) {
+      if (place_lds)
+        fin_place<false, true>(sh, p.cand, m, nb, p.out, k, shift0, mask0, b0,
+                               above0, wanted, fill, g);
+      else
+        fin_place<false, false>(sh, p.cand, m, nb, p.out, k, shift0, mask0,
+                                b0, above0, wanted, fill, g);
+    } else {
+      if (place_lds)
+        fin_place<true, true>(sh, p.cand, m, nb, p.out, k, shift0, mask0, b0,
+                              above0, wanted, fill, g);
+      else
+        fin_place<true, false>(sh, p.cand, m, nb, p.out, k, shift0, mask0,
+                               b0, above0, wanted, fill, g);
+    }
     if (t == 0) p.st->fast = 0;
     return;
   }

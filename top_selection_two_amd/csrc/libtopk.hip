@@ -280,12 +280,11 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
                 p, s);
 }
 
-// Inputs from this size on are sampled for a filter threshold (measured
-// on top-1000 and top-16384 of 1e6 .. 1.6e7 uniform int32: below 2^21 the
-// digit passes are as fast; for k above kPlaceMaxK, whose finish sorts
-// instead of placing, below 2^22).
-constexpr int64_t kSampleMinN = (int64_t)1 << 21;
-constexpr int64_t kSampleMinNSorted = (int64_t)1 << 22;
+// Inputs from this size on are sampled for a filter threshold (the
+// smallest the full sample can read; measured on top-1000 .. top-16384 of
+// 3e5 .. 1e7 uniform int32, sampled calls are as fast as the digit passes
+// or up to 4x faster).
+constexpr int64_t kSampleMinN = (int64_t)kSampleGridMax * kSampleThreads * 4;
 
 // The candidate buffer of radix selection (kCandCap int32) and, after it,
 // the published sample lists and their lengths (kSampleGridMax *
@@ -339,25 +338,25 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   // top-k, from the input).
   bool filtered = false;
   const int64_t nvec = (n - pl.head) / 4;
-  const bool sampled =
-      n >= (k <= kPlaceMaxK ? kSampleMinN : kSampleMinNSorted) &&
-      nvec >= (int64_t)kSampleGridMax * kSampleThreads;
+  bool sampled = n >= kSampleMinN &&
+                 nvec >= (int64_t)kSampleGridMax * kSampleThreads;
+  // need = the sample's share of k, plus four standard deviations and 4.
+  // The largest sample (grid workgroups of 4096 values) for which each
+  // workgroup's list (need values) fits kNeedMax and all of them the last
+  // workgroup's kUnionSlots; none at all if even one workgroup's sample
+  // asks too much (k too large for n).
+  int grid = kSampleGridMax, need = 0;
+  while (sampled) {
+    const double ks = (double)k * (4.0 * kSampleThreads * grid) / (double)n;
+    need = (int)std::ceil(ks + 4.0 * std::sqrt(ks) + 4.0);
+    if (need <= kNeedMax && grid * need <= kUnionSlots) break;
+    if (grid == 1) sampled = false;
+    grid /= 2;
+  }
   if (sampled) {
     SampleParams q;
     q.body = reinterpret_cast<const v4i*>(in + pl.head);
     q.nvec = nvec;
-    // need = the sample's share of k, plus four standard deviations and 4.
-    // The largest sample whose workgroups' lists (need values each) fit
-    // the last workgroup's kUnionSlots.
-    int grid = kSampleGridMax;
-    int need = 0;
-    for (;;) {
-      const double ks = (double)k * (4.0 * kSampleThreads * grid) / (double)n;
-      need = (int)std::ceil(ks + 4.0 * std::sqrt(ks) + 4.0);
-      if (need > kNeedMax) need = kNeedMax;
-      if (grid * need <= kUnionSlots || grid == 1) break;
-      grid /= 2;
-    }
     q.grid = grid;
     q.need = need;
     q.stride = nvec / ((int64_t)grid * kSampleThreads);
