@@ -336,7 +336,8 @@ def test_sampled_placement_with_equal_values(ltk, rng, span, k):
                                  (2 ** 18 + 5, 129), (300_000, 16384),
                                  (600_000, 5000), (1_000_000, 16384),
                                  (3_000_000, 4096), (3_000_000, 5000),
-                                 (6_000_000, 16384)])
+                                 (6_000_000, 16384), (100_000, 5000),
+                                 (200_000, 16384), (2 ** 18 - 1, 2000)])
 def test_sampling_thresholds(ltk, rng, n, k):
     # Around the sizes where the sampled path takes over from the digit
     # passes (2^18, and about 334 k for large k): both ways agree with the

@@ -843,7 +843,7 @@ __device__ __forceinline__ void sort_desc(const int* src, int* dst, int k,
 // The last step of radix selection, one workgroup of 1024 threads.
 //
 // After the selection passes and the gather (state.fast == 0), out holds
-// the top-k unordered: sort it.
+// the top-k unordered: place it by a digit (fin_place_all) or sort it.
 //
 // After a small filter copy (state.fast == 1) of m values above the
 // threshold t: when m < k, they and k - m copies of t are the top-k.
@@ -1210,13 +1210,97 @@ __device__ __forceinline__ void fin_place(FinishShared& sh, const int* cand,
   for (int j = k - fill + t; j < k; j += kFinThreads) out[j] = g;
 }
 
+// Sort the k values of out[0..k) descending by placement instead of a
+// sorting network: their leading bits in common fix a window of up to 12
+// bits below them, a histogram of that digit and its suffix counts give
+// each bin's first place, the values are grouped by bin in LDS (in place
+// in the bucket area, after all of them are read), and each is ranked
+// among its bin's values by counting.  Returns false, having changed
+// nothing, when a bin holds more than kPlaceBinMax values (the caller then
+// sorts).  Barriers inside: call uniformly.
+__device__ __forceinline__ bool fin_place_all(FinishShared& sh, int* out,
+                                              int k) {
+  const int t = threadIdx.x;
+  int x[kPlaceSlots];
+  int lo = kI32Max, hi = kI32Min;
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j) {
+    const int q = j * kFinThreads + t;
+    x[j] = q < k ? out[q] : 0;
+    if (q < k) {
+      lo = min(lo, x[j]);
+      hi = max(hi, x[j]);
+    }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (t == 0) {
+    sh.pick[0] = kI32Max;
+    sh.pick[1] = kI32Min;
+  }
+  for (int i = t; i < kFinWideBins; i += kFinThreads) sh.h[i] = 0u;
+  __syncthreads();
+  if (lane() == 0) {
+    atomicMin(&sh.pick[0], lo);
+    atomicMax(&sh.pick[1], hi);
+  }
+  __syncthreads();
+  const unsigned blo = bias(sh.pick[0]), bhi = bias(sh.pick[1]);
+  if (blo == bhi) return true;  // all equal: any order is sorted
+  const int top = 31 - __builtin_clz(blo ^ bhi);  // highest differing bit
+  const unsigned shift = top >= kFinWideBits - 1 ? (unsigned)(top - kFinWideBits + 1) : 0u;
+  const unsigned dmask = (2u << (top - (int)shift)) - 1u;
+  auto bin = [&](int v) __attribute__((always_inline)) {
+    return (int)((bias(v) >> shift) & dmask);
+  };
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j)
+    if (j * kFinThreads + t < k) atomicAdd(&sh.h[bin(x[j])], 1u);
+  if (t == 0) sh.maxc = 0;
+  __syncthreads();
+  fin_pick_wide(sh, k, sh.top);  // suffix counts and counts into top
+  if (sh.maxc > kPlaceBinMax) return false;
+  const int* off = sh.top;
+  const int* cnt = sh.top + kFinWideBins;
+  int* cur = sh.top + 2 * kFinWideBins;
+  int* stage = sh.bucket;
+  for (int i = t; i < kFinWideBins; i += kFinThreads) cur[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j) {
+    if (j * kFinThreads + t < k) {
+      const int b = bin(x[j]);
+      stage[off[b] + atomicAdd(&cur[b], 1)] = x[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPlaceSlots; ++j) {
+    const int q = j * kFinThreads + t;
+    if (q < k) {
+      const int v = stage[q];
+      const int b = bin(v);
+      const int l0 = off[b], n = cnt[b];
+      int r = 0;
+      for (int i = l0; i < l0 + n; ++i) {
+        const int y = stage[i];
+        r += (y > v || (y == v && i < q)) ? 1 : 0;
+      }
+      out[l0 + r] = v;  // stage and out are distinct
+    }
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     SelectParams p) {
   __shared__ FinishShared sh;
   const int t = threadIdx.x, w = t / kWave, k = p.k;
   const RadixState s = *p.st;
   if (!s.fast) {
-    sort_desc(p.out, p.out, k, sh.top);
+    // One value per thread sorts faster than it is placed.
+    if (k <= kFinThreads || !fin_place_all(sh, p.out, k))
+      sort_desc(p.out, p.out, k, sh.top);
     return;
   }
   const int m = s.bucket;
