@@ -144,7 +144,8 @@ PATHS = {
                      "range (SplitMix64 seed 3), resident in HBM"),
         "short": "top-1000 of 1e8 int32, uniform full range, seed 3",
         "kernel": "filter_kernel",
-        "sources": ["wave.hpp", "hist_kernel.hpp", "libtopk.hip"],
+        "sources": ["wave.hpp", "hist_kernel.hpp", "select_kernel.hpp",
+                    "libtopk.hip"],
         "counters": "topk_large_counters_full_1e8_k1000.json",
         "summary": "topk_large_full_1e8_k1000.md",
         "out_bytes": 4 * 1000,

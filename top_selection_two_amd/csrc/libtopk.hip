@@ -22,6 +22,7 @@
 
 #include "libtopk.h"
 #include "hist_kernel.hpp"
+#include "select_kernel.hpp"
 #include "reduce_kernel.hpp"
 #include "stats_kernel.hpp"
 #include "topk_kernel.hpp"
