@@ -692,7 +692,18 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     mx = wave_max(mx);
     const RegCount<kWaves> cnt{u};
     // tsh is certified on these heads (they only grew since), so the
-    // search may start there.
+    // searches may start there.  First a short search (8 bits): a value
+    // that at least k heads reach, hence every one of the block's top-k
+    // keys too.  When few heads reach it, the smallest key of that value
+    // is the bound; otherwise (many heads near the top, ties) the exact
+    // k-th largest head key keeps the candidates few.  For k above 32 the
+    // short search rarely leaves few heads, so it is not tried.
+    const unsigned tq =
+        k <= kWave / 2 ? radix_lower_bound(bias(tsh), bias(mx), k, 8, cnt)
+                       : 0u;
+    if (k <= kWave / 2 && cnt(tq) <= kWave) {
+      T = (uint64_t)tq << 32;
+    } else {
     const unsigned tv = radix_select(bias(tsh), bias(mx), k, cnt);
     const int above = tv == 0xffffffffu ? 0 : cnt(tv + 1u);
     const int need = k - above;  // >= 1 heads of value tv are needed
@@ -717,6 +728,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       tl = radix_select(0u, 0xffffffffu, need, count_lo);
     }
     T = ((uint64_t)tv << 32) | tl;
+    }
   }
   uint64_t* dst = p.cand + (int64_t)blk * k;
   {
