@@ -488,7 +488,7 @@ def main():
                        args.path)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
+        print("bench.py measures one GPU only: the library has no multi-GPU "
               "path (requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
