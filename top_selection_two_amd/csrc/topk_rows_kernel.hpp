@@ -147,8 +147,11 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
   };
   int T;
   if (k <= kWave) {
+    // 6 steps: a looser bound admits a few more candidates, but the
+    // search costs less (A/B on 97,656 x 1,024 rows, top-20: 6 steps
+    // 74.9 us, 8 steps 75.6, 10 steps 76.5).
     const unsigned bm[1] = {bias(mx)};
-    T = unbias(radix_lower_bound(bias(wave_min(mx)), bias(hi), k, 8,
+    T = unbias(radix_lower_bound(bias(wave_min(mx)), bias(hi), k, 6,
                                  RegCount<1>{bm}));
   } else {
     T = unbias(radix_lower_bound(bias(row_min()), bias(hi), k, 8,
