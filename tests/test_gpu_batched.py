@@ -244,6 +244,23 @@ def test_merge_sizes(ltk, rng, m, length):
             check_merge(ltk, lists, k)
 
 
+@pytest.mark.parametrize("m", [3, 1024, 3000])
+def test_merge_top_in_few_lists(ltk, rng, m):
+    # All of the top-k in one list, or spread over a few: those lists have
+    # more survivors than stage 2 reads first from each (eight).
+    for length in (9, 64, 200):
+        lists = desc_lists(rng, m, length, hi=10**6)
+        for owners in (1, 2, 3):
+            big = lists.copy()
+            for j in range(owners):
+                row = (j * 977) % m
+                big[row] = np.sort(10**6 + 10 + rng.integers(
+                    0, 10**5, length).astype(np.int32))[::-1]
+            for k in (20, 100, 128):
+                if k <= m * length:
+                    check_merge(ltk, big, k)
+
+
 @pytest.mark.parametrize("m", [5, 1024, 2500])
 def test_merge_ties(ltk, rng, m):
     for k in (20, 128):

@@ -162,6 +162,25 @@ def test_ties_below_a_unique_maximum(ltk, copies, k):
     check_topk(ltk, x, 100)
 
 
+@pytest.mark.parametrize("run", [1, 9, 300])
+@pytest.mark.parametrize("k", [25, 64, 100, 128])
+def test_top_values_in_runs(ltk, run, k):
+    # The largest values sit in runs of `run` consecutive elements, so the
+    # few workgroups whose tiles hold a run have many survivors each: more
+    # than stage 2 reads first from a candidate list (eight), which sends
+    # it back for the rest of those lists.  Runs of 1 are the plain case.
+    n = 4_000_037
+    x = synth.fill(800 + run, n, -10**6, 10**6)
+    nruns = (300 + run - 1) // run
+    starts = np.sort(synth.fill(900 + run, nruns, 0, n - run)).astype(np.int64)
+    top = 10**6 + 1 + synth.fill(950 + run, nruns * run, 0, 10**5)
+    for i, s0 in enumerate(starts):
+        x[s0:s0 + run] = top[i * run:(i + 1) * run]
+    check_topk(ltk, x, k)
+    x[starts[0]:starts[0] + run] = 10**6 + 2 * 10**5    # ties at the top
+    check_topk(ltk, x, k)
+
+
 def test_sum_exceeds_int32(ltk):
     x = np.full(3_000_000, I32_MAX, np.int32)
     check_reduce(ltk, x)

@@ -373,17 +373,18 @@ __device__ __forceinline__ void wave_append(bool p, int v, int* counter,
   if (p && pos < cap) dst[pos] = v;
 }
 
-// Visit the candidates of the flagged blocks (blocks[0..nb), k each): 16
-// independent agent-coherent loads per thread are in flight before any is
-// used.  f(valid, value) is called uniformly across the block.
+// Visit the candidates of the flagged blocks (blocks[0..nb), cv.per each;
+// total = nb * cv.per): 16 independent agent-coherent loads per thread are
+// in flight before any is used.  f(valid, value, list, entry) is called
+// uniformly across the block; `list` is the entry's list in cv.
 template <class F>
-__device__ __forceinline__ void scan_flagged(const CandView& cv,
-                                             const int* blocks, int total,
-                                             F&& f) {
+__device__ __forceinline__ void scan_flagged_at(const CandView& cv,
+                                                const int* blocks, int total,
+                                                F&& f) {
   const int per = cv.per;
   constexpr int B = 16;
   for (int base = 0; base < total; base += kBlock * B) {
-    int v[B];
+    int v[B], lb[B], le[B];
     bool ok[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -391,13 +392,28 @@ __device__ __forceinline__ void scan_flagged(const CandView& cv,
       ok[j] = idx < total;
       idx = ok[j] ? idx : total - 1;
       const int fb = idx / per;
-      const int e = idx - fb * per;
-      v[j] = ld_agent(cv.cand + (int64_t)blocks[fb] * cv.stride + e);
+      le[j] = idx - fb * per;
+      lb[j] = blocks[fb];
+      v[j] = ld_agent(cv.cand + (int64_t)lb[j] * cv.stride + le[j]);
     }
 #pragma unroll
-    for (int j = 0; j < B; ++j) f(ok[j], v[j]);
+    for (int j = 0; j < B; ++j) f(ok[j], v[j], lb[j], le[j]);
   }
 }
+
+// The same with f(valid, value).
+template <class F>
+__device__ __forceinline__ void scan_flagged(const CandView& cv,
+                                             const int* blocks, int total,
+                                             F&& f) {
+  scan_flagged_at(cv, blocks, total,
+                  [&](bool ok, int v, int, int) __attribute__((always_inline)) {
+                    f(ok, v);
+                  });
+}
+
+// Entries read first from each flagged list that is not in LDS.
+constexpr int kPrefix = 8;
 
 // ---- stage 2, run by the last workgroup ---------------------------------
 // Merge grid*k candidates into out[0..k):
@@ -588,6 +604,7 @@ __device__ __forceinline__ void stage2_init(SH& sh, Stage2Lds& s2) {
     sh.bcast[2] = 0;        // survivors
     sh.bcast[5] = 0;        // flagged blocks
     sh.bcast[6] = kI32Min;  // T2b
+    sh.bcast[7] = 0;        // flagged lists read past their prefix
   }
 }
 
@@ -693,9 +710,32 @@ __device__ __forceinline__ Stage2Bound stage2_bound(const CandView& cv, int G,
       wave_append(v >= tf, v, &sh.bcast[2], s2.surv, kSurvCap);
     }
   } else {
-    scan_flagged(cv, s2.blocks, r.total, [&](bool ok, int c) {
-      wave_append(ok && c >= tf, c, &sh.bcast[2], s2.surv, kSurvCap);
-    });
+    // Every list is descending, so its survivors are a prefix of it.  The
+    // first kPrefix entries of all flagged lists take one pass (one round
+    // trip to memory for up to kMaxGrid lists); the rest of a list is read
+    // only when its last entry read still reaches T2, which is rare (about
+    // one survivor per flagged list is usual).  Reading whole lists took
+    // (G' * k) / (16 * kBlock) dependent round trips for G' flagged lists.
+    // Those lists go to s2.cand, unused on this path.
+    const int pf = min(kPrefix, per);
+    const int nflag = sh.bcast[5];
+    scan_flagged_at(CandView{cv.cand, cv.stride, pf}, s2.blocks, nflag * pf,
+                    [&](bool ok, int c, int b, int e)
+                        __attribute__((always_inline)) {
+                          const bool s = ok && c >= tf;
+                          wave_append(s, c, &sh.bcast[2], s2.surv, kSurvCap);
+                          wave_append(s && e == pf - 1 && per > pf, b,
+                                      &sh.bcast[7], s2.cand, kDirectCand);
+                        });
+    __syncthreads();
+    const int nlong = sh.bcast[7];
+    if (nlong > 0) {
+      scan_flagged(CandView{cv.cand + pf, cv.stride, per - pf}, s2.cand,
+                   nlong * (per - pf), [&](bool ok, int c) {
+                     wave_append(ok && c >= tf, c, &sh.bcast[2], s2.surv,
+                                 kSurvCap);
+                   });
+    }
   }
   __syncthreads();
   r.m = sh.bcast[2];
