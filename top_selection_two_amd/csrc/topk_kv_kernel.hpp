@@ -392,33 +392,48 @@ struct KvStage2Lds {
   alignas(16) uint64_t gmax[kBlock + 8];  // group maxima of the block maxima
   uint64_t heads[kMaxGrid];
   int blocks[kMaxGrid];                   // blocks whose maximum reaches T2
+  int longb[kMaxGrid];                    // ... and read past their prefix
   int gmax_rank[kWave];
   int surv_rank[kWave];
 };
 
-// Visit the candidate keys of the flagged blocks, 8 agent-coherent 8-byte
-// loads per thread in flight at a time; f(valid, key) is called uniformly.
+// Visit entries e0 .. e0 + per - 1 of the candidate key lists of the
+// flagged blocks (blocks[0..nb), total = nb * per), 8 agent-coherent 8-byte
+// loads per thread in flight at a time; f(valid, key, block, entry) is
+// called uniformly, `entry` counted from e0.
 template <class F>
-__device__ __forceinline__ void kv_scan_flagged(const TopkKvParams& p,
-                                                const int* blocks, int total,
-                                                F&& f) {
+__device__ __forceinline__ void kv_scan_lists(const TopkKvParams& p,
+                                              const int* blocks, int e0,
+                                              int per, int total, F&& f) {
   const int k = p.k;
   constexpr int B = 8;
   for (int base = 0; base < total; base += kBlock * B) {
     uint64_t v[B];
+    int lb[B], le[B];
     bool ok[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       int idx = base + j * kBlock + (int)threadIdx.x;
       ok[j] = idx < total;
       idx = ok[j] ? idx : total - 1;
-      const int fb = idx / k;
-      const int e = idx - fb * k;
-      v[j] = ld_agent(p.cand + (int64_t)blocks[fb] * k + e);
+      const int fb = idx / per;
+      le[j] = idx - fb * per;
+      lb[j] = blocks[fb];
+      v[j] = ld_agent(p.cand + (int64_t)lb[j] * k + e0 + le[j]);
     }
 #pragma unroll
-    for (int j = 0; j < B; ++j) f(ok[j], v[j]);
+    for (int j = 0; j < B; ++j) f(ok[j], v[j], lb[j], le[j]);
   }
+}
+
+// Every key of the flagged blocks' lists (total = nb * k); f(valid, key).
+template <class F>
+__device__ __forceinline__ void kv_scan_flagged(const TopkKvParams& p,
+                                                const int* blocks, int total,
+                                                F&& f) {
+  kv_scan_lists(p, blocks, 0, p.k, total,
+                [&](bool ok, uint64_t c, int, int)
+                    __attribute__((always_inline)) { f(ok, c); });
 }
 
 // Write the i-th result (rank r < k) from its key.
@@ -437,7 +452,9 @@ __device__ __forceinline__ void kv_write_out(const TopkKvParams& p, int r,
 //     (64 groups for k <= 32, else 256, ranked by key); T2 = max(T2a, T2b):
 //     at least k candidate keys are >= T2;
 //  3. survivors = candidate keys >= T2 of the blocks whose maximum reaches
-//     it (read from memory), into LDS;
+//     it (read from memory: the first kPrefix keys of each such list, and
+//     the rest only of a list whose kPrefix-th key still reaches T2, as
+//     the lists are descending), into LDS;
 //  4. up to 256 survivors are ranked; more are cut to exactly k by
 //     selecting the k-th largest key by counting, then ranked.
 template <bool F32, int KCAP>
@@ -453,6 +470,7 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
   if (tid == 0) {
     sh.bcast[2] = 0;  // survivors
     sh.bcast[5] = 0;  // flagged blocks
+    sh.bcast[7] = 0;  // flagged blocks read past their prefix
     sh.bkey[0] = 0;   // T2b
     sh.bkey[1] = 0;   // T2a (stays 0 when equal empty-group keys tie)
   }
@@ -527,10 +545,30 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
   }
   __syncthreads();
-  const int total = sh.bcast[5] * k;
-  kv_scan_flagged(p, s2.blocks, total, [&](bool ok, uint64_t c) {
-    kv_wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv, kKvSurvCap);
-  });
+  const int nflag = sh.bcast[5];
+  const int total = nflag * k;
+  // Survivors are a prefix of each (descending) list: about one per list
+  // is usual.  Reading whole lists took nflag * k / (8 * kBlock) dependent
+  // round trips.
+  const int pf = min(kPrefix, k);
+  kv_scan_lists(p, s2.blocks, 0, pf, nflag * pf,
+                [&](bool ok, uint64_t c, int b, int e)
+                    __attribute__((always_inline)) {
+                      const bool s = ok && c >= T2;
+                      kv_wave_append(s, c, &sh.bcast[2], s2.surv, kKvSurvCap);
+                      wave_append(s && e == pf - 1 && k > pf, b, &sh.bcast[7],
+                                  s2.longb, kMaxGrid);
+                    });
+  __syncthreads();
+  const int nlong = sh.bcast[7];
+  if (nlong > 0) {
+    kv_scan_lists(p, s2.longb, pf, k - pf, nlong * (k - pf),
+                  [&](bool ok, uint64_t c, int, int)
+                      __attribute__((always_inline)) {
+                        kv_wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv,
+                                       kKvSurvCap);
+                      });
+  }
   __syncthreads();
   int m = sh.bcast[2];
 
