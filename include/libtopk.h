@@ -290,6 +290,8 @@ int libtopk_set_grid(int32_t blocks);
 /*
  * Workgroups that a call of size n would launch under the current setting
  * (reporting and traffic accounting; no device work).  Returns 0 for n < 1.
+ * Key-value calls whose kernel fits only one workgroup per compute unit
+ * (k > 64) launch half as many unless a grid is set.
  */
 int32_t libtopk_grid_for(int64_t n);
 
