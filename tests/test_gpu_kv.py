@@ -158,6 +158,18 @@ def test_grid_sweep(ltk, grid):
         ltk.set_grid(0)
 
 
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_monotone_input_over_many_tiles(ltk, order):
+    # Several tiles per workgroup, the last examined first; with ties, so
+    # that positions decide among equal values.
+    n = 6_000_011
+    x = np.sort(synth.fill(42, n, 0, 50_000))
+    if order == "descending":
+        x = x[::-1].copy()
+    for k in (1, 20, 64, 100, 128):
+        check(ltk, x, k)
+
+
 @pytest.mark.parametrize("copies", [300, 20_000])
 def test_ties_below_a_unique_maximum(ltk, copies):
     n = 4_000_037

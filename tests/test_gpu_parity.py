@@ -181,6 +181,19 @@ def test_top_values_in_runs(ltk, run, k):
     check_topk(ltk, x, k)
 
 
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_monotone_input_over_many_tiles(ltk, order):
+    # Each workgroup streams several tiles, its last one first: on monotone
+    # input the first tile it examines holds its largest (ascending) or its
+    # smallest (descending) values.
+    n = 6_000_011
+    x = np.sort(synth.fill(41, n))
+    if order == "descending":
+        x = x[::-1].copy()
+    for k in (1, 20, 64, 100, 128):
+        check_topk(ltk, x, k)
+
+
 def test_sum_exceeds_int32(ltk):
     x = np.full(3_000_000, I32_MAX, np.int32)
     check_reduce(ltk, x)

@@ -655,7 +655,11 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     const char* first = reinterpret_cast<const char*>(body) +
                         (int64_t)blk * kTileBytes<U>;
     const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
-    // First position of tile i of this block, advanced per tile.
+    // First position of tile i of this block, advanced per tile.  Tiles
+    // go in position order (unlike topk_kernel's tile_order): the
+    // value-only admission test skips a value equal to the bound, which is
+    // right only if every element behind the bound has an earlier
+    // position, that is a larger key.
     uint32_t tpos = (uint32_t)(p.head + (int64_t)blk * (4 * kBlock * U));
     const uint32_t tstep = (uint32_t)p.grid * (uint32_t)(4 * kBlock * U);
 #pragma unroll
