@@ -655,19 +655,18 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     const char* first = reinterpret_cast<const char*>(body) +
                         (int64_t)blk * kTileBytes<U>;
     const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
-    // Peek at the block's last tile first (64- and 128-key lists, where
-    // an insertion is dearest).  At least k of its lanes hold a value >=
-    // the k-th largest of the lane maxima found there, so every value
-    // strictly below that is out of the block's top-k, whatever its
+    // Peek at the block's last tile first.  At least k of its lanes hold a
+    // value >= the k-th largest of the lane maxima found there, so every
+    // value strictly below that is out of the block's top-k, whatever its
     // position; equal values still go through.  Tiles stay in position
     // order.  On ascending input the lanes would otherwise insert nearly
-    // every element (key-value top-100 of 1e8 sorted took 2.5 ms).  The
-    // bound is certified on the final lane heads too: a lane whose maximum
-    // there reaches it either admits that maximum or passes a higher
-    // certified bound.  Cost on uniform input: 0.8 / 2.1 / 3.3 us at
-    // top-64 / 100 / 128 of 1e8.  (Issuing the ring's first tiles before
-    // the peek measured 1 us slower still.)
-    if (KCAP >= 64 && count >= 2) {
+    // every element (key-value top-20 / top-100 of 1e8 sorted took 507 us
+    // / 2.5 ms).  The bound is certified on the final lane heads too: a
+    // lane whose maximum there reaches it either admits that maximum or
+    // passes a higher certified bound.  Cost on uniform input: 0.2 / 0.4 /
+    // 0.8 / 2.1 / 3.3 us at top-20 / 32 / 64 / 100 / 128 of 1e8.  (Issuing
+    // the ring's first tiles before the peek measured 1 us slower still.)
+    if (count >= 2) {
       const v4i* last = reinterpret_cast<const v4i*>(first + (count - 1) * stride);
       v4i e[U];
 #pragma unroll
