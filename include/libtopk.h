@@ -109,6 +109,36 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
 int topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out,
              libtopk_stream_t stream);
 
+/* Bytes of the fixed device array behind topk_i32_noalloc (524 KiB). */
+#define LIBTOPK_NOALLOC_SCRATCH_BYTES 536576
+
+/*
+ * topk_i32_noalloc — topk_i32 for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.  Same operation, arguments, output and errors as
+ * topk_i32 for k <= LIBTOPK_MAX_K (one launch), but the call never
+ * allocates: no hipMalloc, hipFree or allocating library routine.  Its
+ * scratch (stage-1 candidates, block maxima and completion tickets) is a
+ * fixed array of LIBTOPK_NOALLOC_SCRATCH_BYTES in the library's device
+ * memory, one per device, held until the process ends; it is sized for
+ * every k <= LIBTOPK_MAX_K and every n <= 2^32.  The first call on a device
+ * looks up the array's address and clears its tickets with a small kernel
+ * on `stream` (no allocation).
+ *
+ * Every call on one device shares that device's array, which keeps the
+ * last call's contents: calls that overlap on one device (different
+ * streams, or different host threads) race and give wrong results; order
+ * them on one stream or otherwise.
+ *
+ *   in, n, out, stream   as for topk_i32
+ *   k    1 <= k <= min(n, LIBTOPK_MAX_K)
+ *
+ * Errors: as topk_i32; k > LIBTOPK_MAX_K returns LIBTOPK_ERR_UNSUPPORTED
+ * (radix selection needs megabytes of candidate space, not in the array).
+ */
+int topk_i32_noalloc(const int32_t *in, int64_t n, int32_t k, int32_t *out,
+                     libtopk_stream_t stream);
+
 /*
  * reduce_i32 — fold in[0..n) with one operator into a single int64.
  *

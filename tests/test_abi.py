@@ -87,6 +87,21 @@ def test_topk_rejects_invalid_arguments(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
+    ((0, 100, 5, FAKE), ltk.ERR_INVALID),                  # NULL input
+    ((FAKE, 100, 5, 0), ltk.ERR_INVALID),                  # NULL output
+    ((FAKE + 2, 100, 5, FAKE * 4), ltk.ERR_INVALID),       # misaligned input
+    ((FAKE, 0, 1, FAKE * 4), ltk.ERR_INVALID),             # n = 0
+    ((FAKE, (1 << 32) + 1, 5, 1 << 40), ltk.ERR_INVALID),  # n > 2^32
+    ((FAKE, 100, 0, FAKE * 4), ltk.ERR_INVALID),           # k = 0
+    ((FAKE, 10, 11, FAKE * 4), ltk.ERR_INVALID),           # k > n
+    ((FAKE, 1000, 129, FAKE * 64), ltk.ERR_UNSUPPORTED),   # beyond the array
+    ((FAKE, 1000, 20, FAKE + 400), ltk.ERR_INVALID),       # out inside in
+])
+def test_topk_noalloc_rejects_invalid_arguments(args, status):
+    assert ltk.topk_noalloc_raw(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
     ((FAKE, 10, 0, 0), ltk.ERR_INVALID),                   # NULL output
     ((FAKE, 10, 0, FAKE * 4 + 4), ltk.ERR_INVALID),        # misaligned output
     ((FAKE + 1, 10, 0, FAKE * 4), ltk.ERR_INVALID),        # misaligned input
@@ -204,6 +219,7 @@ def test_histogram_rejects_invalid_arguments(args, status):
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
+    assert ltk.topk_noalloc_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
     assert ltk.reduce_raw(FAKE, 1000, 0, FAKE * 4) == ltk.ERR_HIP
     assert ltk.reduce_raw(0, 0, 1, FAKE * 4) == ltk.ERR_HIP
     assert ltk.stats_raw(FAKE, 1000, FAKE * 4) == ltk.ERR_HIP

@@ -43,6 +43,8 @@ _VP = ctypes.c_void_p
 SIGNATURES = {
     "topk_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
                  ctypes.c_int),
+    "topk_i32_noalloc": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
+                         ctypes.c_int),
     "reduce_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, _VP, _VP],
                    ctypes.c_int),
     "reduce_stats_i32": ([_VP, ctypes.c_int64, _VP, _VP], ctypes.c_int),
@@ -121,6 +123,13 @@ def release() -> None:
 def topk_raw(in_ptr: int, n: int, k: int, out_ptr: int, stream: int = 0) -> int:
     """Call topk_i32 on raw device pointers; returns the status code."""
     return lib.topk_i32(in_ptr or None, n, k, out_ptr or None, stream or None)
+
+
+def topk_noalloc_raw(in_ptr: int, n: int, k: int, out_ptr: int,
+                     stream: int = 0) -> int:
+    """Call topk_i32_noalloc on raw device pointers; returns the status."""
+    return lib.topk_i32_noalloc(in_ptr or None, n, k, out_ptr or None,
+                                stream or None)
 
 
 def reduce_raw(in_ptr: int, n: int, op: int, out_ptr: int,

@@ -474,9 +474,107 @@ int row_grid(int64_t rows, int64_t cols, int cus) {
   return g < 1 ? 1 : (int)g;
 }
 
+// ---- scratch of the allocation-free top-k -----------------------------------
+// topk_i32_noalloc keeps the stage-1 candidates, block maxima, k-th values
+// and tickets of the register-list top-k in one file-scope device array
+// instead of the per-stream scratch, so that a call never allocates.  The
+// array is sized for the largest grid and list (kMaxGrid x kMaxK), so every
+// k <= kMaxK and every n fits.  Each device holds its own copy at its own
+// address until the process ends.
+struct NoAllocScratch {
+  int cand[kMaxGrid * kMaxK];
+  int heads[kMaxGrid];
+  int kths[kMaxGrid];
+  unsigned ticket[kMaxGrid];
+};
+constexpr size_t kNoAllocBytes = sizeof(NoAllocScratch);
+static_assert(kNoAllocBytes == LIBTOPK_NOALLOC_SCRATCH_BYTES,
+              "the header states the array's size");
+
+}  // namespace
+
+// The array itself.  In host code its name is only a stand-in for the
+// device symbol: the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+std::mutex g_noalloc_mu;
+std::map<int, NoAllocScratch*> g_noalloc;  // device -> address of `scratch`
+
+// The device address of `scratch` on device `dev` (current), looked up once
+// per device.  The first lookup also clears the tickets with a fill kernel
+// on the caller's stream (they must be 0 when a call starts; every call's
+// last workgroup leaves them so).  Nothing is allocated.
+int noalloc_scratch(int dev, hipStream_t stream, NoAllocScratch** out) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  auto it = g_noalloc.find(dev);
+  if (it != g_noalloc.end()) {
+    *out = it->second;
+    return LIBTOPK_OK;
+  }
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr) {
+    debug_hip("hipGetSymbolAddress(scratch)", e);
+    (void)hipGetLastError();
+    return LIBTOPK_ERR_HIP;
+  }
+  NoAllocScratch* s = (NoAllocScratch*)ptr;
+  hipLaunchKernelGGL(zero_words, dim3((kMaxGrid + 255) / 256), dim3(256), 0,
+                     stream, s->ticket, kMaxGrid);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    debug_hip("zero_words launch", e);
+    return LIBTOPK_ERR_HIP;
+  }
+  g_noalloc[dev] = s;
+  *out = s;
+  return LIBTOPK_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int topk_i32_noalloc(const int32_t* in, int64_t n, int32_t k, int32_t* out,
+                     libtopk_stream_t stream) {
+  if (!in || !out) return LIBTOPK_ERR_INVALID;
+  if (((uintptr_t)in & 3u) || ((uintptr_t)out & 3u)) return LIBTOPK_ERR_INVALID;
+  if (n < 1 || n > kMaxN) return LIBTOPK_ERR_INVALID;
+  if (k < 1 || (int64_t)k > n) return LIBTOPK_ERR_INVALID;
+  // Radix selection (k > LIBTOPK_MAX_K) needs megabytes of candidates: not
+  // in the fixed array.
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (overlaps(in, (size_t)n * 4, out, (size_t)k * 4))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  NoAllocScratch* sc = nullptr;
+  rc = noalloc_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  const Plan pl = plan(in, n, cus);
+  TopkParams p;
+  p.in = in;
+  p.n = n;
+  p.ld = n;  // one row
+  p.k = k;
+  p.grid = pl.grid;
+  p.refresh = refresh_period(k);
+  p.cand = sc->cand;
+  p.heads = sc->heads;
+  p.kths = sc->kths;
+  p.ticket = sc->ticket;
+  p.out = out;
+  return launch(topk_fn(k), pl.grid, p, s);
+}
 
 int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
              libtopk_stream_t stream) {
