@@ -32,8 +32,11 @@
  *    allocated by the
  *    first call on that pair (so do that first call before capturing the
  *    stream into a HIP graph), kept for reuse, and freed by
- *    libtopk_release() or at process exit.  Every call leaves it ready for
- *    the next one, so no per-call clearing is enqueued.
+ *    libtopk_release() or at process exit.  No per-call clearing is
+ *    enqueued: the words that the workgroups of one launch count into
+ *    (completion tickets, histogram counters) carry that launch's epoch,
+ *    so no result depends on what an earlier call, finished or not, left
+ *    in the scratch.
  *  - Calls on different streams may run concurrently.  Thread-safe.
  *  - No C++ exception crosses this interface.  The library prints nothing
  *    unless LIBTOPK_DEBUG is set in the environment (then HIP failures are
@@ -109,8 +112,8 @@ enum { LIBTOPK_SUM = 0, LIBTOPK_MAX = 1, LIBTOPK_MIN = 2 };
 int topk_i32(const int32_t *in, int64_t n, int32_t k, int32_t *out,
              libtopk_stream_t stream);
 
-/* Bytes of the fixed device array behind topk_i32_noalloc (524 KiB). */
-#define LIBTOPK_NOALLOC_SCRATCH_BYTES 536576
+/* Bytes of the fixed device array behind topk_i32_noalloc (528 KiB). */
+#define LIBTOPK_NOALLOC_SCRATCH_BYTES 540672
 
 /*
  * topk_i32_noalloc — topk_i32 for callers that cannot allocate device
@@ -324,6 +327,19 @@ int libtopk_set_grid(int32_t blocks);
  * (k > 64) launch half as many unless a grid is set.
  */
 int32_t libtopk_grid_for(int64_t n);
+
+/*
+ * Test hook: overwrite, on `stream`, the completion tickets and histogram
+ * counters that later calls will use with pseudo-random nonzero words
+ * derived from `seed` -- which == 0: those of the scratch of calls on
+ * `stream` (allocated first if need be); which == 1: the tickets of the
+ * fixed array of topk_i32_noalloc on the current device.  These words are
+ * tagged with each launch's epoch, so no later result may depend on what
+ * they held; tests use this to check that.  They index no memory, so any
+ * value is safe.  Returns LIBTOPK_ERR_INVALID for another `which`.
+ */
+int libtopk_debug_scramble(libtopk_stream_t stream, int32_t which,
+                           uint64_t seed);
 
 /*
  * Free every cached scratch area after synchronising the devices that own

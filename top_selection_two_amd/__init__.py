@@ -63,6 +63,8 @@ SIGNATURES = {
     "libtopk_max_k": ([], ctypes.c_int),
     "libtopk_set_grid": ([ctypes.c_int32], ctypes.c_int),
     "libtopk_grid_for": ([ctypes.c_int64], ctypes.c_int32),
+    "libtopk_debug_scramble": ([_VP, ctypes.c_int32, ctypes.c_uint64],
+                               ctypes.c_int),
     "libtopk_release": ([], None),
 }
 
@@ -117,6 +119,19 @@ def grid_for(n: int) -> int:
 
 def release() -> None:
     lib.libtopk_release()
+
+
+def debug_scramble(which: int = 0, seed: int = 1, stream: int | None = None):
+    """Overwrite the tickets and histogram counters that later calls on the
+    current stream (which=0) or topk_i32_noalloc (which=1) use with
+    pseudo-random words: no result may depend on them (a test hook)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    rc = lib.libtopk_debug_scramble(stream or None, which,
+                                    seed & (2 ** 64 - 1))
+    if rc != OK:
+        raise LibtopkError(rc, "libtopk_debug_scramble")
 
 
 # ---------------------------------------------------------------- raw calls

@@ -16,8 +16,9 @@
 // larger histograms use one copy per workgroup).  At the end each
 // workgroup adds its nonzero bins into 64-bit device counters (global
 // atomics, one per bin and workgroup rather than one per element), and the
-// last workgroup to finish (ticket) hands the counters on and clears them,
-// so no memset is ever enqueued.
+// last workgroup to finish (ticket) hands the counters on and arms them for
+// the next launch; the counters are tagged with the launch's epoch, so no
+// memset is ever enqueued and no stale count is ever added in.
 #pragma once
 
 #include "wave.hpp"
@@ -35,8 +36,9 @@ struct HistParams {
   int grid;
   int lo, shift, nbins;
   int64_t* out;             // [nbins]
-  unsigned long long* acc;  // [kMaxBins] device counters, zero between calls
-  unsigned* ticket;
+  uint64_t* acc;            // [kMaxBins] epoch-tagged device counters
+  uint64_t* ticket;
+  uint32_t epoch;           // this launch's (see Tagged)
 };
 
 // Inclusive prefix sum over the wave (row shifts within 16-lane rows, then
@@ -127,33 +129,40 @@ __device__ __forceinline__ int acc_copies(int nbins) {
   return nbins * kAccCopies <= kMaxBins ? kAccCopies : 1;
 }
 
+// Device counters carry the launch's epoch tag (see Tagged): a counter left
+// at any value by an earlier launch, finished or not, counts as zero, and
+// the last workgroup arms every counter it reads for the next epoch instead
+// of clearing it.  A count is at most n <= 2^32, so 33 bits hold it.
+typedef Tagged<33> BinCount;
+
 // Add this workgroup's nonzero count for bin b.
-__device__ __forceinline__ void acc_add(unsigned long long* acc, int nbins,
-                                        int b, unsigned c) {
+__device__ __forceinline__ void acc_add(uint64_t* acc, int nbins, int b,
+                                        unsigned c, uint32_t epoch) {
   if (!c) return;
   const int copies = acc_copies(nbins);
   const int copy = copies > 1 ? (int)(blockIdx.x % kAccCopies) : 0;
-  atomicAdd(acc + copy * nbins + b, (unsigned long long)c);
+  BinCount::add(acc + copy * nbins + b, c, epoch);
 }
 
-// Read bin b summed over the copies and clear it (last workgroup only).
-// All copies are loaded before any is used, so the device-coherent loads
-// overlap.
-__device__ __forceinline__ unsigned long long acc_take(unsigned long long* acc,
-                                                       int nbins, int b) {
+// Read bin b summed over the copies and arm it for the next epoch (last
+// workgroup only).  All copies are loaded before any is used, so the
+// device-coherent loads overlap.
+__device__ __forceinline__ uint64_t acc_take(uint64_t* acc, int nbins, int b,
+                                             uint32_t epoch) {
+  const uint64_t next = BinCount::armed(epoch + 1u);
   if (acc_copies(nbins) == 1) {
-    const unsigned long long t = ld_agent(acc + b);
-    st_agent(acc + b, 0ull);
+    const uint64_t t = BinCount::count(ld_agent(acc + b), epoch);
+    st_agent(acc + b, next);
     return t;
   }
-  unsigned long long v[kAccCopies];
+  uint64_t v[kAccCopies];
 #pragma unroll
   for (int j = 0; j < kAccCopies; ++j) v[j] = ld_agent(acc + j * nbins + b);
-  unsigned long long t = 0;
+  uint64_t t = 0;
 #pragma unroll
   for (int j = 0; j < kAccCopies; ++j) {
-    t += v[j];
-    st_agent(acc + j * nbins + b, 0ull);
+    t += BinCount::count(v[j], epoch);
+    st_agent(acc + j * nbins + b, next);
   }
   return t;
 }
@@ -189,13 +198,12 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
 #pragma unroll
       for (int j = 1; j < kWaves; ++j) c += h[j * kWaveHistBins + b];
     }
-    acc_add(p.acc, nb, b, c);
+    acc_add(p.acc, nb, b, c, p.epoch);
   }
 
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &is_last)) return;
   for (int b = threadIdx.x; b < nb; b += kBlock)
-    p.out[b] = (int64_t)acc_take(p.acc, nb, b);
-  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
+    p.out[b] = (int64_t)acc_take(p.acc, nb, b, p.epoch);
 }
 
 }  // namespace ltk

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 
@@ -51,14 +52,25 @@ struct Scratch {
   uint64_t* kvcand = nullptr;  // kMaxGrid * kMaxK (key-value candidates)
   uint64_t* kvheads = nullptr; // kMaxGrid
   uint64_t* kvkths = nullptr;  // kMaxGrid
-  unsigned long long* acc = nullptr;  // kMaxBins histogram counters, 0
-                                      // between calls
+  uint64_t* acc = nullptr;     // kMaxBins histogram counters (epoch-tagged)
   RadixState* rstate = nullptr;       // radix-selection state
   int* rcand = nullptr;               // kCandCap candidates + sample
                                       // lists, allocated by the first
                                       // top-k call with k > 128
-  unsigned* ticket = nullptr;  // kMaxGrid words (one per row), 0 between calls
+  uint64_t* ticket = nullptr;  // kMaxGrid epoch-tagged tickets (one per row)
+  // Launches on this scratch so far: each launch takes the next value as
+  // its epoch, which tags the tickets and counters it uses (see Tagged in
+  // wave.hpp).
+  std::shared_ptr<std::atomic<uint32_t>> epochs;
 };
+
+// The epoch of a new launch on a scratch (never 0, which freshly cleared
+// words carry).
+uint32_t next_epoch(std::atomic<uint32_t>& c) {
+  uint32_t e = c.fetch_add(1u) + 1u;
+  while (e == 0u) e = c.fetch_add(1u) + 1u;
+  return e;
+}
 
 constexpr size_t kCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(int);
 constexpr size_t kHeadBytes = (size_t)kMaxGrid * sizeof(int);
@@ -66,9 +78,9 @@ constexpr size_t kPartBytes = (size_t)kMaxGrid * sizeof(int64_t);
 constexpr size_t kStatBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
 constexpr size_t kKvCandBytes = (size_t)kMaxGrid * kMaxK * sizeof(uint64_t);
 constexpr size_t kKvHeadBytes = (size_t)kMaxGrid * sizeof(uint64_t);
-constexpr size_t kAccBytes = (size_t)kMaxBins * sizeof(unsigned long long);
+constexpr size_t kAccBytes = (size_t)kMaxBins * sizeof(uint64_t);
 constexpr size_t kStateBytes = 256;
-constexpr size_t kTicketBytes = (size_t)kMaxGrid * sizeof(unsigned);
+constexpr size_t kTicketBytes = (size_t)kMaxGrid * sizeof(uint64_t);
 constexpr size_t kScratchBytes = kCandBytes + 2 * kHeadBytes + kPartBytes +
                                  kStatBytes + kKvCandBytes +
                                  2 * kKvHeadBytes + kAccBytes + kStateBytes +
@@ -89,6 +101,17 @@ void debug_hip(const char* what, hipError_t e) {
 __global__ void zero_words(unsigned* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
+}
+
+// Test hook: overwrite n 64-bit words with pseudo-random nonzero values
+// (a SplitMix64-style mix of seed and index).
+__global__ void scramble_words(uint64_t* p, int n, uint64_t seed) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint64_t z = seed + 0x9e3779b97f4a7c15ull * (uint64_t)(i + 1);
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  p[i] = (z ^ (z >> 31)) | 1ull;
 }
 
 int current_device(int* dev) {
@@ -160,14 +183,16 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   b += kKvHeadBytes;
   s.kvkths = (uint64_t*)b;
   b += kKvHeadBytes;
-  s.acc = (unsigned long long*)b;
+  s.acc = (uint64_t*)b;
   b += kAccBytes;
   s.rstate = (RadixState*)b;
   b += kStateBytes;
-  s.ticket = (unsigned*)b;
+  s.ticket = (uint64_t*)b;
+  s.epochs = std::make_shared<std::atomic<uint32_t>>(0u);
   // A kernel (not a memset) clears the histogram counters, the selection
   // state and the tickets (contiguous), ordered on the caller's stream
-  // before the first real launch.
+  // before the first real launch.  (Any value would do for the counters and
+  // tickets, which carry epoch tags; zero is the tidy start.)
   const int zwords = (int)((kAccBytes + kStateBytes + kTicketBytes) / 4);
   hipLaunchKernelGGL(zero_words, dim3((zwords + 255) / 256), dim3(256), 0,
                      stream, (unsigned*)s.acc, zwords);
@@ -298,6 +323,7 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
   p.heads = sc.kvheads;
   p.kths = sc.kvkths;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   p.out_v = out_v;
   p.out_i = out_i;
   return launch(fn, pl.grid, p, s);
@@ -387,9 +413,11 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     q.samp = rcand + kCandCap;
     q.samp_cnt = q.samp + kSampleGridMax * kNeedMax;
     q.ticket = sc.ticket;
+    q.epoch = next_epoch(*sc.epochs);
     rc = launch_threads((const void*)&sample_kernel, grid, kSampleThreads, q,
                         s);
     if (rc != LIBTOPK_OK) return rc;
+    sp.epoch = next_epoch(*sc.epochs);
     rc = launch((const void*)&filter_kernel<kTileVec>, pl.grid, sp, s);
     if (rc != LIBTOPK_OK) return rc;
     filtered = true;
@@ -397,9 +425,11 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   for (int pass = 0; pass < 4; ++pass) {
     sp.dshift = 24 - 8 * pass;
     sp.first = pass == 0 && !filtered;  // the filter wrote the first state
+    sp.epoch = next_epoch(*sc.epochs);
     rc = launch((const void*)&select_pass_kernel<kTileVec>, pl.grid, sp, s);
     if (rc != LIBTOPK_OK) return rc;
   }
+  sp.epoch = next_epoch(*sc.epochs);
   rc = launch((const void*)&gather_kernel<kTileVec>, pl.grid, sp, s);
   if (rc != LIBTOPK_OK) return rc;
   return launch_threads((const void*)&select_finish_kernel, 1, kFinThreads,
@@ -485,7 +515,7 @@ struct NoAllocScratch {
   int cand[kMaxGrid * kMaxK];
   int heads[kMaxGrid];
   int kths[kMaxGrid];
-  unsigned ticket[kMaxGrid];
+  uint64_t ticket[kMaxGrid];  // epoch-tagged (see Tagged in wave.hpp)
 };
 constexpr size_t kNoAllocBytes = sizeof(NoAllocScratch);
 static_assert(kNoAllocBytes == LIBTOPK_NOALLOC_SCRATCH_BYTES,
@@ -499,18 +529,26 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
 namespace {
 
+// Per device: the address of `scratch` and the epochs of its launches.
+struct NoAllocState {
+  NoAllocScratch* s = nullptr;
+  std::atomic<uint32_t> epochs{0u};
+};
 std::mutex g_noalloc_mu;
-std::map<int, NoAllocScratch*> g_noalloc;  // device -> address of `scratch`
+std::map<int, std::unique_ptr<NoAllocState>> g_noalloc;
 
 // The device address of `scratch` on device `dev` (current), looked up once
-// per device.  The first lookup also clears the tickets with a fill kernel
-// on the caller's stream (they must be 0 when a call starts; every call's
-// last workgroup leaves them so).  Nothing is allocated.
-int noalloc_scratch(int dev, hipStream_t stream, NoAllocScratch** out) {
+// per device, and its epoch counter.  The first lookup also clears the
+// tickets with a fill kernel on the caller's stream (they carry epoch tags,
+// so any value would do; zero is the tidy start).  Nothing is allocated on
+// the device (the host keeps one small record per device).
+int noalloc_scratch(int dev, hipStream_t stream, NoAllocScratch** out,
+                    std::atomic<uint32_t>** epochs) {
   std::lock_guard<std::mutex> lock(g_noalloc_mu);
   auto it = g_noalloc.find(dev);
   if (it != g_noalloc.end()) {
-    *out = it->second;
+    *out = it->second->s;
+    *epochs = &it->second->epochs;
     return LIBTOPK_OK;
   }
   void* ptr = nullptr;
@@ -521,15 +559,19 @@ int noalloc_scratch(int dev, hipStream_t stream, NoAllocScratch** out) {
     return LIBTOPK_ERR_HIP;
   }
   NoAllocScratch* s = (NoAllocScratch*)ptr;
-  hipLaunchKernelGGL(zero_words, dim3((kMaxGrid + 255) / 256), dim3(256), 0,
-                     stream, s->ticket, kMaxGrid);
+  const int zwords = (int)(sizeof(s->ticket) / 4);
+  hipLaunchKernelGGL(zero_words, dim3((zwords + 255) / 256), dim3(256), 0,
+                     stream, (unsigned*)s->ticket, zwords);
   e = hipGetLastError();
   if (e != hipSuccess) {
     debug_hip("zero_words launch", e);
     return LIBTOPK_ERR_HIP;
   }
-  g_noalloc[dev] = s;
+  std::unique_ptr<NoAllocState> st(new NoAllocState);
+  st->s = s;
   *out = s;
+  *epochs = &st->epochs;
+  g_noalloc[dev] = std::move(st);
   return LIBTOPK_OK;
 }
 
@@ -553,7 +595,8 @@ int topk_i32_noalloc(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   if (rc != LIBTOPK_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   NoAllocScratch* sc = nullptr;
-  rc = noalloc_scratch(dev, s, &sc);
+  std::atomic<uint32_t>* epochs = nullptr;
+  rc = noalloc_scratch(dev, s, &sc, &epochs);
   if (rc != LIBTOPK_OK) return rc;
   int cus;
   {
@@ -572,6 +615,7 @@ int topk_i32_noalloc(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   p.heads = sc->heads;
   p.kths = sc->kths;
   p.ticket = sc->ticket;
+  p.epoch = next_epoch(*epochs);
   p.out = out;
   return launch(topk_fn(k), pl.grid, p, s);
 }
@@ -610,6 +654,7 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
   p.heads = sc.heads;
   p.kths = sc.kths;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   p.out = out;
   return launch(topk_fn(k), pl.grid, p, s);
 }
@@ -646,6 +691,7 @@ int reduce_i32(const int32_t* in, int64_t n, int32_t op, int64_t* out_i64,
   p.grid = pl.grid;
   p.partials = sc.partials;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   p.out = out_i64;
   return launch(reduce_fn(op), pl.grid, p, s);
 }
@@ -693,6 +739,7 @@ int reduce_stats_i32(const int32_t* in, int64_t n, int64_t* out,
   p.grid = pl.grid;
   p.partials = sc.spart;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   p.out = out;
   return launch((const void*)&stats_kernel<kTileVec>, pl.grid, p, s);
 }
@@ -760,6 +807,7 @@ int topk_batched_i32(const int32_t* in, int64_t rows, int64_t cols,
     const int64_t nr = rows - r0 < per_launch ? rows - r0 : per_launch;
     p.in = in + r0 * ld;
     p.out = out + r0 * k;
+    p.epoch = next_epoch(*sc.epochs);
     rc = launch(topk_fn(k), (int)(nr * gr), p, s);
     if (rc != LIBTOPK_OK) return rc;
   }
@@ -792,6 +840,7 @@ int topk_merge_i32(const int32_t* lists, int64_t m, int32_t len, int32_t k,
   p.groups = (int)((m + kMaxGrid - 1) / kMaxGrid);
   p.cand = sc.cand;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   p.out = out;
   return launch((const void*)&topk_merge_kernel, p.groups, p, s);
 }
@@ -833,7 +882,49 @@ int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
   p.out = out;
   p.acc = sc.acc;
   p.ticket = sc.ticket;
+  p.epoch = next_epoch(*sc.epochs);
   return launch((const void*)&hist_kernel<kTileVec>, pl.grid, p, s);
+}
+
+int libtopk_debug_scramble(libtopk_stream_t stream, int32_t which,
+                           uint64_t seed) {
+  if (which != 0 && which != 1) return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* words[2];
+  int counts[2];
+  int parts = 0;
+  if (which == 0) {
+    Scratch sc;
+    rc = get_scratch(dev, s, &sc);
+    if (rc != LIBTOPK_OK) return rc;
+    words[0] = sc.ticket;
+    counts[0] = kMaxGrid;
+    words[1] = sc.acc;
+    counts[1] = kMaxBins;
+    parts = 2;
+  } else {
+    NoAllocScratch* sc = nullptr;
+    std::atomic<uint32_t>* epochs = nullptr;
+    rc = noalloc_scratch(dev, s, &sc, &epochs);
+    if (rc != LIBTOPK_OK) return rc;
+    words[0] = sc->ticket;
+    counts[0] = kMaxGrid;
+    parts = 1;
+  }
+  for (int i = 0; i < parts; ++i) {
+    hipLaunchKernelGGL(scramble_words, dim3((counts[i] + 255) / 256),
+                       dim3(256), 0, s, words[i], counts[i],
+                       seed + 0x632be59bd9b4e019ull * (uint64_t)i);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      debug_hip("scramble_words launch", e);
+      return LIBTOPK_ERR_HIP;
+    }
+  }
+  return LIBTOPK_OK;
 }
 
 const char* libtopk_strerror(int status) {

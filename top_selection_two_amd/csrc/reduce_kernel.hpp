@@ -33,7 +33,8 @@ struct ReduceParams {
   int64_t covered;
   int grid;
   int64_t* partials;  // [grid]
-  unsigned* ticket;   // completion counter; 0 between calls
+  uint64_t* ticket;   // completion counter (epoch-tagged, see Tagged)
+  uint32_t epoch;     // this launch's
   int64_t* out;       // [1]
 };
 
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
     st_agent(p.partials + blk, b);
   }
 
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &is_last)) return;
 
   int64_t v = F::widen(F::identity());
   for (int i = threadIdx.x; i < p.grid; i += kBlock)
@@ -169,7 +170,6 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceParams p) {
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) r = F::combine(r, red[i]);
     *p.out = r;
-    st_agent(p.ticket, 0u);
   }
 }
 

@@ -76,8 +76,9 @@ struct SelectParams {
   RadixState* st;
   int* cand;    // [kCandCap] candidate buffer
   int* out;     // [k]
-  unsigned long long* acc;  // [256] device counters, zero between calls
-  unsigned* ticket;
+  uint64_t* acc;            // [256] epoch-tagged device counters
+  uint64_t* ticket;
+  uint32_t epoch;           // this launch's (see Tagged)
 };
 
 // Append the lanes where q holds to dst at a device counter (one atomic per
@@ -211,10 +212,10 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
     unsigned c = h[b];
 #pragma unroll
     for (int j = 1; j < kWaves; ++j) c += h[j * kDigitBins + b];
-    acc_add(p.acc, kDigitBins, b, c);
+    acc_add(p.acc, kDigitBins, b, c, p.epoch);
   }
 
-  if (!last_to_finish(p.ticket, grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, grid, p.epoch, &is_last)) return;
 
   // Pick the digit holding the k-th largest: thread t looks at bin 255 - t,
   // so an inclusive prefix sum over threads is the count of the bucket's
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
   // reached by exact counts.
   const int t = threadIdx.x;
   const int b = kDigitBins - 1 - t;
-  const unsigned long long raw = acc_take(p.acc, kDigitBins, b);
-  const int c = raw > (unsigned long long)kCandCap ? kCandCap : (int)raw;
+  const uint64_t raw = acc_take(p.acc, kDigitBins, b, p.epoch);
+  const int c = raw > (uint64_t)kCandCap ? kCandCap : (int)raw;
   const int incl_w = wave_scan_incl(c);
   if (lane() == kWave - 1) scan[w] = incl_w;
   __syncthreads();
@@ -258,7 +259,6 @@ __global__ __launch_bounds__(kBlock) void select_pass_kernel(SelectParams p) {
       p.st->fast = 0;
     }
   }
-  if (t == 0) st_agent(p.ticket, 0u);
 }
 
 // The filter threshold for top-k with large n.  `grid` workgroups read
@@ -286,7 +286,8 @@ struct SampleParams {
   RadixState* st;
   int* samp;         // [kSampleGridMax * kNeedMax] the published lists
   int* samp_cnt;     // [kSampleGridMax] their lengths
-  unsigned* ticket;
+  uint64_t* ticket;
+  uint32_t epoch;    // this launch's (see Tagged)
 };
 
 struct RankShared {
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     len = p.need;
   }
   if (t == 0) st_agent(p.samp_cnt + blockIdx.x, len);
-  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &sh.is_last)) return;
 
   // The union of the lists: slot i is entry i % cap of list i / cap.
   // Every slot's value and its list's length are loaded together (slots
@@ -436,7 +437,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
     p.st->thresh = unbias(tv);
     p.st->ccount = 0u;
     p.st->eqcount = 0u;
-    st_agent(p.ticket, 0u);
   }
 }
 
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(SelectParams p) {
     for (int j = 0; j < kWaves; ++j) e += weq[j];
     if (e) atomicAdd(&p.st->eqcount, e);
   }
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &is_last)) return;
   if (threadIdx.x == 0) {
     const unsigned gt = ld_agent(&p.st->ccount);
     const unsigned eqs = ld_agent(&p.st->eqcount);
@@ -525,7 +525,6 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(SelectParams p) {
     s.ccount = 0u;
     s.eqcount = 0u;
     s.fast = fast;
-    st_agent(p.ticket, 0u);
   }
 }
 
@@ -550,13 +549,12 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(SelectParams p) {
     stg.put(ok && (key > s.prefix || (s.done && key == s.prefix)), x);
   });
   stg.flush();
-  if (!last_to_finish(p.ticket, grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, grid, p.epoch, &is_last)) return;
   if (!s.done) {
     const int g = unbias(s.prefix);
     for (int j = p.k - s.kleft + (int)threadIdx.x; j < p.k; j += kBlock)
       p.out[j] = g;
   }
-  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
 // Sort src[0..k) (k <= kMaxKSelect) descending into dst[0..k) in one

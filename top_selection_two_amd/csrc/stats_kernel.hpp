@@ -40,7 +40,8 @@ struct StatsParams {
   int64_t covered;
   int grid;
   uint64_t* partials;  // [grid * 4]: sum, max:min, squares low, high
-  unsigned* ticket;    // completion counter; 0 between calls
+  uint64_t* ticket;    // completion counter (epoch-tagged, see Tagged)
+  uint32_t epoch;      // this launch's
   int64_t* out;        // [6]: count, sum, max, min, squares low, high
 };
 
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(StatsParams p) {
     for (int j = 0; j < 4; ++j) st_agent(p.partials + 4 * (int64_t)blk + j, wds[j]);
   }
 
-  if (!last_to_finish(p.ticket, p.grid, &is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &is_last)) return;
 
   // Fold the per-block partials.
   StatsAcc g = stats_identity();
@@ -225,7 +226,6 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(StatsParams p) {
     p.out[3] = (int64_t)r.mn;
     p.out[4] = (int64_t)r.qlo;
     p.out[5] = (int64_t)r.qhi;
-    st_agent(p.ticket, 0u);
   }
 }
 

@@ -60,7 +60,8 @@ struct TopkParams {
   int* cand;         // [rows * grid * k]  per-block candidates
   int* heads;        // [rows * grid]      max of each block's candidates
   int* kths;         // [rows * grid]      k-th largest of each block's
-  unsigned* ticket;  // [rows]             completion counters; 0 between calls
+  uint64_t* ticket;  // [rows]             completion counters (see Tagged)
+  uint32_t epoch;    // this launch's
   int* out;          // [rows * k]         results, descending
 };
 
@@ -851,7 +852,7 @@ __device__ __forceinline__ void stage2_finish(const CandView& cv, int k,
 }
 
 // Stage 2 of the top-k kernel for one row: merge the row's grid * k block
-// candidates into out[0..k), then re-arm the row's ticket.
+// candidates into out[0..k).
 template <class SH>
 __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
                                             Stage2Lds& s2) {
@@ -862,7 +863,6 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
   stage2_fill_blocks(p.heads, p.kths, p.cand, G, G * k, all_in_lds, sh, s2);
   const Stage2Bound r = stage2_bound(cv, G, k, all_in_lds, sh, s2);
   stage2_finish(cv, k, r, p.out, sh, s2);
-  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
 template <int KCAP, bool FIT, int U>
@@ -1087,7 +1087,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
   if (direct) return;
-  if (!last_to_finish(p.ticket + row, p.grid, &sh.is_last)) return;
+  if (!last_to_finish(p.ticket + row, p.grid, p.epoch, &sh.is_last)) return;
   TopkParams q = p;  // the row's slice of the scratch and of the output
   q.cand = p.cand + slot0 * k;
   q.heads = p.heads + slot0;
@@ -1114,7 +1114,8 @@ struct MergeParams {
   int k;
   int groups;        // workgroups, each merging up to kMaxGrid lists
   int* cand;         // [groups * k] group results (groups > 1)
-  unsigned* ticket;  // completion counter (groups > 1); 0 between calls
+  uint64_t* ticket;  // completion counter (groups > 1; see Tagged)
+  uint32_t epoch;    // this launch's
   int* out;          // [k]
 };
 
@@ -1139,13 +1140,12 @@ __global__ __launch_bounds__(kBlock) void topk_merge_kernel(MergeParams p) {
   stage2_finish(cv, k, r, dst, sh, s2);
   if (p.groups == 1) return;
 
-  if (!last_to_finish(p.ticket, p.groups, &sh.is_last)) return;
+  if (!last_to_finish(p.ticket, p.groups, p.epoch, &sh.is_last)) return;
   const CandView cg{p.cand, k, k};
   stage2_init(sh, s2);
   stage2_fill_lists(cg, p.groups, k, sh, s2);
   const Stage2Bound r2 = stage2_bound(cg, p.groups, k, false, sh, s2);
   stage2_finish(cg, k, r2, p.out, sh, s2);
-  if (threadIdx.x == 0) st_agent(p.ticket, 0u);
 }
 
 }  // namespace ltk

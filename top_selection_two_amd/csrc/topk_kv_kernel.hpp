@@ -54,7 +54,8 @@ struct TopkKvParams {
   uint64_t* cand;     // [grid * k]  per-block candidate keys, descending
   uint64_t* heads;    // [grid]      largest candidate key of each block
   uint64_t* kths;     // [grid]      k-th largest candidate key of each block
-  unsigned* ticket;   // completion counter; 0 between calls
+  uint64_t* ticket;   // completion counter (epoch-tagged, see Tagged)
+  uint32_t epoch;     // this launch's
   int* out_v;         // [k]         values (input bits), descending
   int64_t* out_i;     // [k]         their positions
 };
@@ -617,7 +618,6 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     const int r = kv_rank_all(s2.surv, m, v);
     if (tid < m && r < k) kv_write_out<F32>(p, r, v);
   }
-  if (tid == 0) st_agent(p.ticket, 0u);
 }
 
 template <int KCAP, bool FIT, int U, bool F32>
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   }
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
-  if (!last_to_finish(p.ticket, p.grid, &sh.is_last)) return;
+  if (!last_to_finish(p.ticket, p.grid, p.epoch, &sh.is_last)) return;
   topk_kv_stage2<F32, KCAP>(
       p, sh, *reinterpret_cast<KvStage2Lds*>(&ring_lds[0][0][0][0]));
 }

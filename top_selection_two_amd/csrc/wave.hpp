@@ -176,15 +176,69 @@ __device__ __forceinline__ void drain_memory_ops() {
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---- counters tagged with the launch's epoch ------------------------------
+// Every launch gets an epoch from the host (a per-scratch counter, new for
+// each launch).  A device counter shared by the workgroups of a launch
+// (completion ticket, histogram bin) is one 64-bit word: the epoch's tag in
+// the high bits, the launch's count in the low CB bits.  Whoever reads or
+// takes the last count of a word leaves it "armed" for the next epoch (tag
+// epoch + 1, count 0), so in the ordinary sequence of launches every add
+// meets its own tag and costs one atomic.  A word with any other tag (left
+// by a launch that never finished, or overwritten) is foreign: an add that
+// returns a foreign word installs the launch's tag with its own amount by
+// compare-and-swap, and if another workgroup installed it first, adds again
+// (its first add went to the foreign value, which the installation
+// replaced).  So a word's count never depends on what it held before the
+// launch, unless its stale tag happens to equal the launch's own (one
+// chance in 2^31 or more for an arbitrary value).
+template <int CB>
+struct Tagged {
+  static constexpr uint64_t kCountMask = (1ull << CB) - 1ull;
+  static constexpr uint32_t kTagMask = (uint32_t)((1ull << (64 - CB)) - 1ull);
+  __device__ static uint64_t armed(uint32_t epoch) {
+    return (uint64_t)(epoch & kTagMask) << CB;
+  }
+  __device__ static bool mine(uint64_t w, uint32_t epoch) {
+    return (uint32_t)(w >> CB) == (epoch & kTagMask);
+  }
+  // Add c (> 0) to the launch's count in *w; returns the count before the
+  // add.  The loop ends: each pass either succeeds or sees the word changed
+  // by another of the launch's at most `grid` adds.
+  __device__ static uint64_t add(uint64_t* w, uint64_t c, uint32_t epoch) {
+    unsigned long long* a = reinterpret_cast<unsigned long long*>(w);
+    const uint64_t o = atomicAdd(a, (unsigned long long)c);
+    if (mine(o, epoch)) return o & kCountMask;
+    uint64_t cur = o + c;
+    for (;;) {
+      const uint64_t prev = atomicCAS(a, (unsigned long long)cur,
+                                      (unsigned long long)(armed(epoch) | c));
+      if (prev == cur) return 0;
+      if (mine(prev, epoch))
+        return atomicAdd(a, (unsigned long long)c) & kCountMask;
+      cur = prev;
+    }
+  }
+  // The launch's count held in a word read after every add has completed
+  // (0 if no add of this launch reached it).
+  __device__ static uint64_t count(uint64_t w, uint32_t epoch) {
+    return mine(w, epoch) ? (w & kCountMask) : 0ull;
+  }
+};
+typedef Tagged<32> Ticket;    // completion tickets: 32-bit epoch, 32-bit count
+
 // Take the workgroup's completion ticket after its published stores have
-// completed; true in exactly one workgroup, the last one.  Barriers inside:
-// call uniformly.  `flag` is an LDS word.
-__device__ __forceinline__ bool last_to_finish(unsigned* ticket, int grid,
-                                               int* flag) {
+// completed; true in exactly one workgroup, the last one of the `grid` that
+// take this ticket in this launch, which also arms the ticket for the next
+// epoch.  Barriers inside: call uniformly.  `flag` is an LDS word.
+__device__ __forceinline__ bool last_to_finish(uint64_t* ticket, int grid,
+                                               uint32_t epoch, int* flag) {
   drain_memory_ops();
   __syncthreads();
-  if (threadIdx.x == 0)
-    *flag = atomicAdd(ticket, 1u) == (unsigned)(grid - 1);
+  if (threadIdx.x == 0) {
+    const bool last = Ticket::add(ticket, 1, epoch) == (uint64_t)(grid - 1);
+    if (last) st_agent(ticket, Ticket::armed(epoch + 1u));
+    *flag = last;
+  }
   __syncthreads();
   return *flag != 0;
 }
