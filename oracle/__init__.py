@@ -72,6 +72,10 @@ class Oracle:
         lib.oracle_histogram_i32.argtypes = [p, ctypes.c_int64, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, p]
         lib.oracle_histogram_i32.restype = ctypes.c_int
+        lib.oracle_topk_segmented_i32.argtypes = [p, ctypes.c_int64, p,
+                                                  ctypes.c_int64,
+                                                  ctypes.c_int32, p, p]
+        lib.oracle_topk_segmented_i32.restype = ctypes.c_int
         for name in ("oracle_topk_kv_i32", "oracle_topk_kv_f32"):
             fn = getattr(lib, name)
             fn.argtypes = [p, ctypes.c_int64, ctypes.c_int32, p, p]
@@ -165,6 +169,28 @@ class Oracle:
                              "(m=%d, len=%d, k=%d)" % (m, ln, k))
         return out
 
+    def topk_segmented(self, x, offsets, k: int):
+        """(out, counts): the top-k of every segment x[offsets[s] ..
+        offsets[s+1]), shape (nseg, k), a short segment's values followed by
+        INT32_MIN; counts[s] = min(k, segment length)."""
+        a = _as_i32(x)
+        off = np.ascontiguousarray(offsets, dtype=np.int64)
+        if off.ndim != 1 or off.size < 1:
+            raise ValueError("offsets: a 1-D array of nseg + 1 entries")
+        nseg = off.size - 1
+        out = np.empty((nseg, max(k, 0)), dtype=np.int32)
+        counts = np.empty(nseg, dtype=np.int32)
+        rc = self.lib.oracle_topk_segmented_i32(
+            a.ctypes.data if a.size else None, a.size, off.ctypes.data, nseg,
+            k, out.ctypes.data if nseg else None, counts.ctypes.data)
+        if rc == -2:
+            raise ValueError("oracle_topk_segmented_i32: offsets out of "
+                             "order or outside the array")
+        if rc != 0:
+            raise ValueError("oracle_topk_segmented_i32: invalid arguments "
+                             "(n=%d, nseg=%d, k=%d)" % (a.size, nseg, k))
+        return out, counts
+
     def histogram(self, x, lo: int, shift: int, nbins: int) -> np.ndarray:
         """int64 counts of x in nbins bins of width 2**shift from lo."""
         a = _as_i32(x)
@@ -235,3 +261,7 @@ def topk_batched(x, k: int, cols: int | None = None) -> np.ndarray:
 
 def topk_merge(lists, k: int) -> np.ndarray:
     return default().topk_merge(lists, k)
+
+
+def topk_segmented(x, offsets, k: int):
+    return default().topk_segmented(x, offsets, k)

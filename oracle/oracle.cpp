@@ -86,6 +86,22 @@
  *                     last k backwards.  A list that is not in descending
  *                     order is a caller error, reported as such.
  *
+ *   oracle_topk_segmented_i32
+ *                     the top-k of every segment of one array, segments of
+ *                     different lengths given by offsets ([TopK] §6: the
+ *                     two-stage pattern as a building block, for instance
+ *                     candidate selection per user, whose candidate lists
+ *                     differ in length; several TopK results merged
+ *                     again).  Segment s is in[offsets[s] .. offsets[s+1]),
+ *                     with 0 <= offsets[0] <= ... <= offsets[nseg] <= n.
+ *                     Definition: for each segment, sort a copy ascending
+ *                     and read its last min(k, len) values backwards into
+ *                     out[s * k ..]; a segment shorter than k has all its
+ *                     values there, the remaining slots hold INT32_MIN,
+ *                     and counts[s] = min(k, len) tells them apart from
+ *                     real INT32_MIN values.  Offsets out of order are a
+ *                     caller error, reported as such.
+ *
  *   oracle_histogram_i32
  *                     counts of the values falling into equal-width bins
  *                     ([TopK] §6: histogram computation as a use of the
@@ -329,6 +345,39 @@ int oracle_topk_merge_i32(const int32_t *lists, int64_t m, int32_t len,
     std::sort(v.begin(), v.end());
     for (int32_t i = 0; i < k; ++i)
         out[i] = v[(size_t)(total - 1 - i)];
+    return 0;
+}
+
+/* out[s * k + i], i < min(k, len_s): the i-th largest value of segment s,
+ * which is in[offsets[s] .. offsets[s + 1]); out[s * k + i] = INT32_MIN for
+ * len_s <= i < k; counts[s] = min(k, len_s) (counts may be NULL).  Returns
+ * 0; -1 on invalid arguments (null pointers, n < 0, nseg < 0, k < 1); -2 if
+ * the offsets are not non-decreasing within [0, n]. */
+int oracle_topk_segmented_i32(const int32_t *in, int64_t n,
+                              const int64_t *offsets, int64_t nseg,
+                              int32_t k, int32_t *out, int32_t *counts)
+{
+    if (!offsets || n < 0 || nseg < 0 || k < 1 || (nseg > 0 && !out) ||
+        (n > 0 && !in))
+        return -1;
+    if (offsets[0] < 0 || offsets[nseg] > n)
+        return -2;
+    for (int64_t s = 0; s < nseg; ++s)
+        if (offsets[s + 1] < offsets[s])
+            return -2;
+    for (int64_t s = 0; s < nseg; ++s) {
+        const int64_t a = offsets[s], b = offsets[s + 1];
+        std::vector<int32_t> v(in + a, in + b);
+        std::sort(v.begin(), v.end());
+        const int64_t len = b - a;
+        const int64_t have = len < (int64_t)k ? len : (int64_t)k;
+        for (int64_t i = 0; i < have; ++i)
+            out[s * k + i] = v[(size_t)(len - 1 - i)];
+        for (int64_t i = have; i < k; ++i)
+            out[s * k + i] = INT32_MIN;
+        if (counts)
+            counts[s] = (int32_t)have;
+    }
     return 0;
 }
 

@@ -394,10 +394,78 @@ def pin_histogram(o, rng):
             assert o.histogram(a, lo, shift, nbins).tolist() == want
 
 
+def pin_topk_segmented(o, rng):
+    """Segmented top-k: a hand example (empty and short segments, padding
+    and counts), repeated max extraction per segment over random
+    segmentations (brute force sharing nothing with a sort), numpy's sort
+    per segment on larger ones, equal segments against per-row top-k, one
+    segment against the whole array's top-k, and the two-stage lemma (the
+    top-k of the union of the segments' lists is the top-k of the whole);
+    offsets out of order are refused."""
+    x = np.array([5, 1, 9, 9, 3, 7, 2], np.int32)
+    out, cnt = o.topk_segmented(x, [0, 3, 3, 7], 2)
+    assert out.tolist() == [[9, 5], [I32_MIN, I32_MIN], [9, 7]]
+    assert cnt.tolist() == [2, 0, 2]
+    out, cnt = o.topk_segmented(x, [1, 2, 6], 3)     # [1] and [9, 9, 3, 7]
+    assert out.tolist() == [[1, I32_MIN, I32_MIN], [9, 9, 7]]
+    assert cnt.tolist() == [1, 3]
+    out, cnt = o.topk_segmented(np.array([I32_MIN, 4], np.int32), [0, 1, 2], 2)
+    assert out.tolist() == [[I32_MIN, I32_MIN], [4, I32_MIN]]
+    assert cnt.tolist() == [1, 1]
+    out, cnt = o.topk_segmented(x, [4], 5)            # no segments
+    assert out.shape == (0, 5) and cnt.size == 0
+    for bad in ([0, 5, 3], [-1, 2], [0, 8]):
+        refused = False
+        try:
+            o.topk_segmented(x, bad, 1)
+        except ValueError:
+            refused = True
+        assert refused, "offsets %s must be refused" % bad
+    for trial in range(60):
+        n = int(rng.integers(0, 40))
+        hi = int(rng.choice([2, 5, 2 ** 31]))
+        a = rng.integers(-hi, hi, size=n, dtype=np.int64).astype(np.int32)
+        nseg = int(rng.integers(0, 8))
+        cuts = np.sort(rng.integers(0, n + 1, size=nseg + 1))
+        k = int(rng.integers(1, 8))
+        out, cnt = o.topk_segmented(a, cuts, k)
+        for s in range(nseg):
+            seg = a[cuts[s]:cuts[s + 1]].tolist()
+            m = min(k, len(seg))
+            assert out[s].tolist() == brute_topk(seg, m) + [I32_MIN] * (k - m)
+            assert cnt[s] == m
+    for trial in range(20):
+        n = int(rng.integers(1, 20000))
+        a = rng.integers(-2 ** 31, 2 ** 31, size=n, dtype=np.int64)
+        a = a.astype(np.int32)
+        nseg = int(rng.integers(1, 60))
+        cuts = np.sort(rng.integers(0, n + 1, size=nseg + 1))
+        k = int(rng.integers(1, 129))
+        out, cnt = o.topk_segmented(a, cuts, k)
+        for s in range(nseg):
+            seg = np.sort(a[cuts[s]:cuts[s + 1]].astype(np.int64))[::-1][:k]
+            assert out[s, :seg.size].tolist() == seg.tolist()
+            assert (out[s, seg.size:] == I32_MIN).all()
+        live = out[out > I32_MIN]
+        whole = np.sort(a[cuts[0]:cuts[-1]].astype(np.int64))[::-1][:k]
+        assert np.sort(live.astype(np.int64))[::-1][:whole.size][
+            :np.count_nonzero(whole > I32_MIN)].tolist() == \
+            whole[whole > I32_MIN].tolist()
+    rows = rng.integers(-1000, 1000, size=(7, 90), dtype=np.int64)
+    rows = rows.astype(np.int32)
+    out, cnt = o.topk_segmented(rows.ravel(), np.arange(8) * 90, 13)
+    assert (out == np_topk_rows(rows, 13)).all() and (cnt == 13).all()
+    a = rng.integers(-2 ** 31, 2 ** 31, size=5000, dtype=np.int64)
+    a = a.astype(np.int32)
+    out, cnt = o.topk_segmented(a, [0, 5000], 40)
+    assert out[0].tolist() == np.sort(a.astype(np.int64))[::-1][:40].tolist()
+
+
 BATTERY = [pin_worked_example, pin_all_ones, pin_exhaustive_small,
            pin_empty_identities, pin_int64_sum, pin_closed_forms,
            pin_invariants, pin_checker_rejects, pin_stats, pin_topk_kv,
-           pin_topk_batched, pin_topk_merge, pin_histogram]
+           pin_topk_batched, pin_topk_merge, pin_histogram,
+           pin_topk_segmented]
 
 
 def run_battery(o, seed=7):
@@ -484,6 +552,20 @@ MUTANTS = {
     "merge_accepts_unsorted": (r"return -2;", "(void)0;"),
     "merge_ascending": (r"out\[i\] = v\[\(size_t\)\(total - 1 - i\)\];",
                         "out[i] = v[(size_t)(total - k + i)];"),
+    "segmented_end_past_segment": (
+        r"std::vector<int32_t> v\(in \+ a, in \+ b\);",
+        "std::vector<int32_t> v(in + a, in + (b < n ? b + 1 : b));"),
+    "segmented_skips_first": (
+        r"std::vector<int32_t> v\(in \+ a, in \+ b\);",
+        "std::vector<int32_t> v(in + (a < b ? a + 1 : a), in + b);"),
+    "segmented_pads_with_zero": (r"out\[s \* k \+ i\] = INT32_MIN;",
+                                 "out[s * k + i] = 0;"),
+    "segmented_counts_length": (r"counts\[s\] = \(int32_t\)have;",
+                                "counts[s] = (int32_t)len;"),
+    "segmented_ascending": (r"out\[s \* k \+ i\] = v\[\(size_t\)\(len - 1 - i\)\];",
+                            "out[s * k + i] = v[(size_t)(len - have + i)];"),
+    "segmented_drops_last_segment": (r"for \(int64_t s = 0; s < nseg; \+\+s\) \{\n        const int64_t a",
+                                     "for (int64_t s = 0; s < nseg; ++s) {\n        if (s == nseg - 1 && s > 0) { for (int32_t i = 0; i < k; ++i) out[s * k + i] = INT32_MIN; if (counts) counts[s] = 0; continue; }\n        const int64_t a"),
     "histogram_off_by_one_bin": (r"const int64_t b = d / width;",
                                  "const int64_t b = (d + 1) / width;"),
     "histogram_keeps_last_edge": (r"if \(b < nbins\)\n            \+\+out\[b\];",
