@@ -24,6 +24,8 @@ Paths (each prints ONE JSON line):
                  the 1e8 array
   topk_large     top-1000 of the 1e8 array (radix selection, several
                  launches per call)
+  segmented      per-segment top-20 of the 1e8 array cut into segments of
+                 log-uniform lengths in [16, 2^18] (numpy PCG64, seed 11)
 
 A step is one pass of the path's library calls over its input, which sits
 in HBM before anything is timed.  Results are first checked against the
@@ -240,6 +242,29 @@ PATHS = {
         "counters": "hist_counters_full_1e8_256.json",
         "summary": "hist_full_1e8_256.md",
     },
+    "segmented": {
+        "metric": ("Segmented Top-20 over 1e8 int32 (segment lengths "
+                   "log-uniform in [16, 2^18]): elements/s, HBM GB/s as % of "
+                   "8 TB/s peak"),
+        "inputs": [("full_1e8", None)],
+        "segments": (16, 1 << 18, 11),
+        "describe": ("top-20 of every segment of 1e8 int32 uniform over the "
+                     "full int32 range (SplitMix64 seed 3), cut into segments "
+                     "whose lengths are log-uniform in [16, 2^18] (numpy "
+                     "PCG64 seed 11; 3967 segments), resident in HBM"),
+        "short": "segmented top-20 of 1e8 int32, lengths log-uniform in "
+                 "[16, 2^18]",
+        "calls": [("seg20", "segmented", 20)],
+        # One call is two launches; summaries and traffic are per call.
+        "groups": [("ltk::seg_long_kernel<", ["seg20"])],
+        "call_kernels": ["ltk::seg_short_kernel(", "ltk::seg_long_kernel<"],
+        "once_per_call": "ltk::seg_short_kernel(",
+        "launches_per_call": 2,
+        "sources": ["wave.hpp", "topk_kernel.hpp", "topk_rows_kernel.hpp",
+                    "seg_kernel.hpp", "libtopk.hip"],
+        "counters": "seg_counters_full_1e8_k20.json",
+        "summary": "seg_full_1e8_k20.md",
+    },
     "topk_large": {
         "metric": ("Top-1000 over 1e8 int32 (radix selection): elements/s, "
                    "HBM GB/s as % of 8 TB/s peak"),
@@ -256,6 +281,7 @@ PATHS = {
                          "ltk::select_pass_kernel<", "ltk::gather_kernel<",
                          "ltk::select_finish_kernel("],
         "once_per_call": "ltk::select_finish_kernel(",
+        "launches_per_call": 8,
         "sources": ["wave.hpp", "hist_kernel.hpp", "select_kernel.hpp",
                     "libtopk.hip"],
         "counters": "topk_large_counters_full_1e8_k1000.json",
@@ -293,6 +319,9 @@ def call_algo_bytes(P, call) -> int:
         return 4 * n + 4 * call[2] * P["rows"]
     if kind == "hist":
         return 4 * n + 8 * call[2][2]
+    if kind == "segmented":
+        nseg = P["nseg"]
+        return 4 * n + 8 * (nseg + 1) + 4 * call[2] * nseg + 4 * nseg
     raise ValueError(kind)
 
 
@@ -576,11 +605,24 @@ def cpu_model() -> str:
 
 
 # ------------------------------------------------------------------ calls
+def segment_offsets(P):
+    import synth
+    lo, hi, seed = P["segments"]
+    return synth.segment_offsets(input_size(P), lo, hi, seed)
+
+
 def make_runner(ltk, P, call, xds, dev):
     """A closure that launches one library call on the current stream."""
     import torch
     kind = call[1]
     src = xds[call[3] if len(call) > 3 else 0]
+    if kind == "segmented":
+        offs = torch.from_numpy(segment_offsets(P)).to(dev)
+        nseg = offs.numel() - 1
+        out = torch.empty((nseg, call[2]), dtype=torch.int32, device=dev)
+        cnt = torch.empty(nseg, dtype=torch.int32, device=dev)
+        return lambda: ltk.topk_segmented(src, offs, call[2], out=out,
+                                          counts=cnt)
     if kind == "topk":
         out = torch.empty(call[2], dtype=torch.int32, device=dev)
         return lambda: ltk.topk(src, call[2], out=out)
@@ -622,6 +664,8 @@ def oracle_result(oracle, P, call, x):
                                    call[2])
     if kind == "hist":
         return oracle.histogram(x, *call[2])
+    if kind == "segmented":
+        return oracle.topk_segmented(x, segment_offsets(P), call[2])
     raise ValueError(kind)
 
 
@@ -634,7 +678,7 @@ def fetch_result(ltk, call, res):
         return int(res.cpu()[0])
     if kind == "stats":
         return ltk.unpack_stats(res)
-    if kind == "kv":
+    if kind in ("kv", "segmented"):
         return (res[0].cpu().numpy(), res[1].cpu().numpy())
     return np.asarray(res.cpu().numpy())
 
@@ -670,6 +714,8 @@ def main():
                          "(CPU only)")
     args = ap.parse_args()
     P = PATHS[args.path]
+    if "segments" in P:
+        P["nseg"] = int(segment_offsets(P).size - 1)
     if args.summarize:
         summarize(args.summarize, os.path.join(ROOT, "profiles"), args.path)
         return
@@ -911,8 +957,10 @@ def main():
                        "merge": merge})
     else:
         config["grid"] = ltk.grid_for(n)
-    if P.get("call_kernels"):
-        config["launches_per_call"] = 8
+    if P.get("launches_per_call"):
+        config["launches_per_call"] = P["launches_per_call"]
+    if "segments" in P:
+        config["segments"] = P["nseg"]
     config["hbm_gbps_per_step"] = round(
         sum(call_algo_bytes(P, c) for c in calls) / (ms_per_step * 1e-3)
         / 1e9, 1)

@@ -280,6 +280,50 @@ int topk_merge_i32(const int32_t *lists, int64_t m, int32_t len, int32_t k,
                    int32_t *out, libtopk_stream_t stream);
 
 /*
+ * topk_segmented_i32 — the top-k of every segment of one array, segments
+ * of any lengths given by offsets: segment s is
+ * in[offsets[s] .. offsets[s + 1]), and out[s * k + i], i < min(k, len_s),
+ * is its i-th largest value (descending, duplicates kept).  A segment
+ * shorter than k (empty included) fills the rest of its k slots with
+ * INT32_MIN; counts[s] = min(k, len_s) tells that padding from real
+ * INT32_MIN values.
+ *
+ * Operation: [TopK] §6 (the two-stage pattern as a building block, e.g.
+ * candidate selection per user, whose candidate lists differ in length;
+ * several TopK results merged again) with [TopK] §2's two stages per
+ * segment.  Two launches on `stream`: one wave per segment finishes
+ * segments of up to 4096 elements in registers and plans the rest on the
+ * device; persistent workgroups then stream the longer segments (a
+ * segment above 2^16 elements in up to 1024 parts, whose candidates the
+ * last part to finish merges).
+ *
+ *   in       device, int32[n] (may be NULL when n == 0)
+ *   n        elements of in, 0 <= n <= 2^32
+ *   offsets  device, int64[nseg + 1], 8-byte aligned; the caller promises
+ *            0 <= offsets[0] <= offsets[1] <= ... <= offsets[nseg] <= n.
+ *            The library does not check this (the offsets live on the
+ *            device); with offsets that break it the results are
+ *            unspecified, but nothing outside in[0..n), out and counts is
+ *            read or written.
+ *   nseg     0 <= nseg < 2^31 (0: nothing is enqueued, LIBTOPK_OK once k
+ *            is valid; the pointers may then be NULL)
+ *   k        1 <= k <= LIBTOPK_MAX_K
+ *   out      device, int32[nseg * k], written in full
+ *   counts   device, int32[nseg], or NULL when not wanted
+ *
+ * Scratch: besides the per-stream area, about 0.6 KiB per 1,000 elements
+ * of n (lists and the parts' candidates), allocated on the first call with
+ * a larger n on the stream (which then synchronises the stream once).
+ *
+ * Errors: LIBTOPK_ERR_INVALID for a NULL or misaligned pointer, n or nseg
+ * out of range, k < 1, or overlapping buffers; LIBTOPK_ERR_UNSUPPORTED for
+ * k > LIBTOPK_MAX_K.
+ */
+int topk_segmented_i32(const int32_t *in, int64_t n, const int64_t *offsets,
+                       int64_t nseg, int32_t k, int32_t *out, int32_t *counts,
+                       libtopk_stream_t stream);
+
+/*
  * histogram_i32 — counts of the values of in[0..n) in nbins equal bins:
  * out[b] = the number of elements v with
  *     lo + b * 2^shift <= v <= lo + (b + 1) * 2^shift - 1
@@ -332,7 +376,8 @@ int32_t libtopk_grid_for(int64_t n);
  * Test hook: overwrite, on `stream`, the completion tickets and histogram
  * counters that later calls will use with pseudo-random nonzero words
  * derived from `seed` -- which == 0: those of the scratch of calls on
- * `stream` (allocated first if need be); which == 1: the tickets of the
+ * `stream` (allocated first if need be), with the counters and tickets of
+ * the segmented top-k once it has run there; which == 1: the tickets of the
  * fixed array of topk_i32_noalloc on the current device.  These words are
  * tagged with each launch's epoch, so no later result may depend on what
  * they held; tests use this to check that.  They index no memory, so any

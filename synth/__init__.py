@@ -20,6 +20,10 @@ name                        n            values                      seed
 ``dup1000_1e7`` also comes in two variants: ``sorted`` (the same values in
 ascending order, the worst case for insertion-based selection) and ``equal``
 (n copies of the draw's element 0).
+
+``segment_offsets`` cuts an array into segments of varied lengths (the
+segmented top-k's input): lengths drawn log-uniformly from [lo, hi] with
+numpy's PCG64 generator under a fixed seed.
 """
 from __future__ import annotations
 
@@ -112,3 +116,24 @@ def workload(name: str, variant: str | None = None, n: int | None = None,
             x[:] = x[0]
         return x
     raise ValueError("unknown variant %r" % variant)
+
+
+def segment_offsets(n: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """int64 offsets (nseg + 1 entries, from 0 to n) cutting n elements into
+    consecutive segments whose lengths are drawn log-uniformly from
+    [lo, hi] (rounded down), the last one cut short at n."""
+    if not (1 <= lo <= hi) or n < 0:
+        raise ValueError("need 1 <= lo <= hi and n >= 0")
+    rng = np.random.default_rng(seed)
+    out = [0]
+    pos = 0
+    while pos < n:
+        chunk = rng.random(4096)
+        lens = np.floor(np.exp(np.log(lo) + chunk * (np.log(hi + 1) -
+                                                      np.log(lo))))
+        for ln in np.clip(lens, lo, hi).astype(np.int64):
+            pos = min(n, pos + int(ln))
+            out.append(pos)
+            if pos >= n:
+                break
+    return np.asarray(out, dtype=np.int64)

@@ -216,6 +216,35 @@ def test_histogram_rejects_invalid_arguments(args, status):
     assert ltk.histogram_raw(*args) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    # (in, n, offsets, nseg, k, out, counts)
+    ((FAKE, 100, FAKE * 8, -1, 5, FAKE * 64, 0), ltk.ERR_INVALID),   # nseg < 0
+    ((FAKE, -1, FAKE * 8, 2, 5, FAKE * 64, 0), ltk.ERR_INVALID),     # n < 0
+    ((FAKE, (1 << 32) + 1, FAKE * 8, 2, 5, 1 << 40, 0), ltk.ERR_INVALID),
+    ((FAKE, 100, FAKE * 8, 2, 0, FAKE * 64, 0), ltk.ERR_INVALID),    # k = 0
+    ((FAKE, 100, FAKE * 8, 2, 129, FAKE * 64, 0), ltk.ERR_UNSUPPORTED),
+    ((FAKE, 100, 0, 2, 5, FAKE * 64, 0), ltk.ERR_INVALID),           # NULL offsets
+    ((FAKE, 100, FAKE * 8 + 4, 2, 5, FAKE * 64, 0), ltk.ERR_INVALID),  # 4-aligned
+    ((FAKE, 100, FAKE * 8, 2, 5, 0, 0), ltk.ERR_INVALID),            # NULL out
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE * 64 + 2, 0), ltk.ERR_INVALID),
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE * 64, FAKE * 32 + 1), ltk.ERR_INVALID),
+    ((0, 100, FAKE * 8, 2, 5, FAKE * 64, 0), ltk.ERR_INVALID),       # NULL in
+    ((FAKE + 2, 100, FAKE * 8, 2, 5, FAKE * 64, 0), ltk.ERR_INVALID),
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE + 40, 0), ltk.ERR_INVALID),    # out in in
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE * 8 + 8, 0), ltk.ERR_INVALID),  # out on offsets
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE * 64, FAKE * 64 + 20), ltk.ERR_INVALID),
+    ((FAKE, 100, FAKE * 8, 2, 5, FAKE * 64, FAKE + 8), ltk.ERR_INVALID),
+])
+def test_topk_segmented_rejects_invalid_arguments(args, status):
+    assert ltk.topk_segmented_raw(*args) == status
+
+
+def test_topk_segmented_no_segments_is_a_no_op():
+    assert ltk.topk_segmented_raw(0, 0, 0, 0, 5, 0) == ltk.OK
+    assert ltk.topk_segmented_raw(FAKE, 100, 0, 0, 129, 0) == \
+        ltk.ERR_UNSUPPORTED
+
+
 @pytest.mark.skipif(not no_gpu(), reason="a GPU is visible")
 def test_valid_call_without_device_reports_hip_error():
     assert ltk.topk_raw(FAKE, 1000, 20, FAKE * 4) == ltk.ERR_HIP
@@ -233,6 +262,8 @@ def test_valid_call_without_device_reports_hip_error():
     assert ltk.histogram_raw(FAKE, 100, 0, 0, 16, FAKE * 64) == ltk.ERR_HIP
     assert ltk.histogram_raw(0, 0, 0, 0, 16, FAKE * 64) == ltk.ERR_HIP
     assert ltk.topk_raw(FAKE, 100000, 5000, FAKE * 64) == ltk.ERR_HIP
+    assert ltk.topk_segmented_raw(FAKE, 100, FAKE * 8, 2, 5, FAKE * 64) == \
+        ltk.ERR_HIP
 
 
 def test_grid_setting():

@@ -23,6 +23,9 @@ if the library is not built, importing this package raises.
     histogram(x, lo, shift, nbins)
                     -> int64 tensor [nbins]: counts of x in bins of width
                        2**shift starting at lo
+    topk_segmented(x, offsets, k)
+                    -> (int32 [nseg, k], int32 counts [nseg]): the top-k of
+                       every segment x[offsets[s] .. offsets[s+1])
 """
 from __future__ import annotations
 
@@ -57,6 +60,8 @@ SIGNATURES = {
                          ctypes.c_int),
     "topk_merge_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                         _VP, _VP], ctypes.c_int),
+    "topk_segmented_i32": ([_VP, ctypes.c_int64, _VP, ctypes.c_int64,
+                            ctypes.c_int32, _VP, _VP, _VP], ctypes.c_int),
     "histogram_i32": ([_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                        ctypes.c_int32, _VP, _VP], ctypes.c_int),
     "libtopk_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -180,6 +185,15 @@ def topk_merge_raw(lists_ptr: int, m: int, length: int, k: int, out_ptr: int,
     """Call topk_merge_i32 on raw device pointers; returns the status."""
     return lib.topk_merge_i32(lists_ptr or None, m, length, k,
                               out_ptr or None, stream or None)
+
+
+def topk_segmented_raw(in_ptr: int, n: int, offsets_ptr: int, nseg: int,
+                       k: int, out_ptr: int, counts_ptr: int = 0,
+                       stream: int = 0) -> int:
+    """Call topk_segmented_i32 on raw device pointers; returns the status."""
+    return lib.topk_segmented_i32(in_ptr or None, n, offsets_ptr or None,
+                                  nseg, k, out_ptr or None, counts_ptr or None,
+                                  stream or None)
 
 
 def histogram_raw(in_ptr: int, n: int, lo: int, shift: int, nbins: int,
@@ -365,6 +379,50 @@ def topk_merge(lists, k: int, out=None):
     if rc != OK:
         raise LibtopkError(rc, "topk_merge_i32")
     return out
+
+
+def topk_segmented(x, offsets, k: int, out=None, counts=None,
+                   with_counts: bool = True):
+    """Top-k of every segment x[offsets[s] .. offsets[s+1]) of the 1-D int32
+    device tensor x; offsets is an int64 device tensor of nseg + 1
+    non-decreasing entries within [0, x.numel()].  Returns (out, counts):
+    an int32 tensor [nseg, k], each row descending and padded with INT32_MIN
+    past a short segment's values, and the int32 counts [nseg] =
+    min(k, length) (None when with_counts is False)."""
+    import torch
+    _check_input(x)
+    if (not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.int64
+            or offsets.device != x.device or offsets.dim() != 1
+            or offsets.numel() < 1 or not offsets.is_contiguous()):
+        raise ValueError("offsets must be a contiguous 1-D int64 tensor of "
+                         "nseg + 1 entries on x's device")
+    nseg = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((nseg, max(int(k), 0)), dtype=torch.int32,
+                          device=x.device)
+    elif (out.dtype != torch.int32 or out.device != x.device
+          or out.numel() != nseg * k or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [nseg, k] tensor on "
+                         "x's device")
+    if with_counts and counts is None:
+        counts = torch.empty(nseg, dtype=torch.int32, device=x.device)
+    elif counts is not None and (counts.dtype != torch.int32
+                                 or counts.device != x.device
+                                 or counts.numel() != nseg
+                                 or not counts.is_contiguous()):
+        raise ValueError("counts must be a contiguous int32 [nseg] tensor on "
+                         "x's device")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.topk_segmented_i32(
+            x.data_ptr() if x.numel() else None, x.numel(),
+            offsets.data_ptr(), nseg, k,
+            out.data_ptr() if out.numel() else None,
+            counts.data_ptr() if counts is not None and nseg else None,
+            stream or None)
+    if rc != OK:
+        raise LibtopkError(rc, "topk_segmented_i32")
+    return out, counts
 
 
 def histogram(x, lo: int, shift: int, nbins: int, out=None):

@@ -29,6 +29,7 @@
 #include "topk_kernel.hpp"
 #include "topk_kv_kernel.hpp"
 #include "topk_rows_kernel.hpp"
+#include "seg_kernel.hpp"
 
 namespace {
 
@@ -58,10 +59,17 @@ struct Scratch {
                                       // lists, allocated by the first
                                       // top-k call with k > 128
   uint64_t* ticket = nullptr;  // kMaxGrid epoch-tagged tickets (one per row)
+  // Segmented top-k: work lists, per-unit candidates and tickets, sized by
+  // the largest n seen on the pair (grown on demand).
+  void* seg_base = nullptr;
+  int64_t seg_n = 0;
   // Launches on this scratch so far: each launch takes the next value as
   // its epoch, which tags the tickets and counters it uses (see Tagged in
   // wave.hpp).
   std::shared_ptr<std::atomic<uint32_t>> epochs;
+  // Segmented top-k calls so far: each call's tag for the counters its two
+  // launches share (the next call arms them).
+  std::shared_ptr<std::atomic<uint32_t>> seg_calls;
 };
 
 // The epoch of a new launch on a scratch (never 0, which freshly cleared
@@ -189,6 +197,7 @@ int get_scratch(int dev, hipStream_t stream, Scratch* out) {
   b += kStateBytes;
   s.ticket = (uint64_t*)b;
   s.epochs = std::make_shared<std::atomic<uint32_t>>(0u);
+  s.seg_calls = std::make_shared<std::atomic<uint32_t>>(0u);
   // A kernel (not a memset) clears the histogram counters, the selection
   // state and the tickets (contiguous), ordered on the caller's stream
   // before the first real launch.  (Any value would do for the counters and
@@ -357,6 +366,104 @@ int get_rcand(int dev, hipStream_t stream, int** out) {
   }
   *out = sc.rcand;
   return LIBTOPK_OK;
+}
+
+// The segmented top-k's scratch for inputs of up to n elements: lists of
+// the medium and huge segments, the units of the huge ones with their
+// candidates, maxima and k-th values, three counters, one ticket per huge
+// segment plus one, and the plan.  Sized from n (valid offsets list at
+// most n / (kSegShort + 1) medium and n / (kSegWhole + 1) huge segments,
+// and at most n / kSegUnit + huge units); grown on demand, the stream
+// synchronised before the old area is freed.
+struct SegScratch {
+  int* med;
+  SegHuge* huge;
+  SegUnit* units;
+  int* cand;
+  int* heads;
+  int* kths;
+  uint64_t* ctr;
+  uint64_t* ticket;
+  SegPlan* plan;
+  int med_cap, huge_cap, unit_cap;
+};
+
+void seg_layout(void* base, int64_t n, SegScratch* s, size_t* bytes) {
+  const int64_t nn = n < ((int64_t)1 << 20) ? ((int64_t)1 << 20) : n;
+  s->med_cap = (int)(nn / (kSegShort + 1) + 1);
+  s->huge_cap = (int)(nn / (kSegWhole + 1) + 1);
+  s->unit_cap = (int)(nn / kSegUnit + s->huge_cap + 1);
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += (b + 255) & ~(size_t)255;
+    return (char*)base + o;
+  };
+  // 1 KiB of slack after the per-unit arrays: stage 2 copies them to LDS in
+  // whole KiB chunks.
+  s->cand = (int*)take((size_t)s->unit_cap * kMaxK * 4 + 1024);
+  s->heads = (int*)take((size_t)s->unit_cap * 4 + 1024);
+  s->kths = (int*)take((size_t)s->unit_cap * 4 + 1024);
+  s->units = (SegUnit*)take((size_t)s->unit_cap * sizeof(SegUnit));
+  s->huge = (SegHuge*)take((size_t)s->huge_cap * sizeof(SegHuge));
+  s->med = (int*)take((size_t)s->med_cap * 4);
+  s->plan = (SegPlan*)take(sizeof(SegPlan));
+  s->ctr = (uint64_t*)take(4 * 8 + (size_t)(1 + s->huge_cap) * 8);
+  s->ticket = s->ctr + 4;
+  *bytes = off;
+}
+
+int get_seg(int dev, hipStream_t stream, int64_t n, SegScratch* out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& sc = g_cache[std::make_pair(dev, (void*)stream)];
+  size_t bytes = 0;
+  if (sc.seg_base && n <= sc.seg_n) {
+    seg_layout(sc.seg_base, sc.seg_n, out, &bytes);
+    return LIBTOPK_OK;
+  }
+  if (getenv("LIBTOPK_TEST_FAIL_ALLOC")) return LIBTOPK_ERR_NOMEM;
+  const int64_t want = n < ((int64_t)1 << 20) ? ((int64_t)1 << 20) : n;
+  seg_layout(nullptr, want, out, &bytes);
+  if (sc.seg_base) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(sc.seg_base);
+    sc.seg_base = nullptr;
+    sc.seg_n = 0;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    debug_hip("hipMalloc(segments)", e);
+    (void)hipGetLastError();
+    return LIBTOPK_ERR_NOMEM;
+  }
+  seg_layout(p, want, out, &bytes);
+  // Counters and tickets carry epoch tags; zero is the tidy start.
+  const int zwords = (int)((4 + 1 + out->huge_cap) * 2);
+  hipLaunchKernelGGL(zero_words, dim3((zwords + 255) / 256), dim3(256), 0,
+                     stream, (unsigned*)out->ctr, zwords);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    debug_hip("zero_words launch", e);
+    (void)hipFree(p);
+    return LIBTOPK_ERR_HIP;
+  }
+  sc.seg_base = p;
+  sc.seg_n = want;
+  return LIBTOPK_OK;
+}
+
+template <int KCAP, bool FIT>
+const void* seg_long_fn_of() {
+  return (const void*)&seg_long_kernel<KCAP, FIT, kTileVec>;
+}
+const void* seg_long_fn(int k) {
+  if (k <= 8) return seg_long_fn_of<8, true>();
+  if (k <= 16) return seg_long_fn_of<16, true>();
+  if (k <= 24) return seg_long_fn_of<24, true>();
+  if (k <= 32) return seg_long_fn_of<32, true>();
+  if (k <= 64) return seg_long_fn_of<64, false>();
+  return seg_long_fn_of<128, false>();
 }
 
 // Top-k for LIBTOPK_MAX_K < k <= LIBTOPK_MAX_K_SELECT: four digit passes of
@@ -845,6 +952,79 @@ int topk_merge_i32(const int32_t* lists, int64_t m, int32_t len, int32_t k,
   return launch((const void*)&topk_merge_kernel, p.groups, p, s);
 }
 
+int topk_segmented_i32(const int32_t* in, int64_t n, const int64_t* offsets,
+                       int64_t nseg, int32_t k, int32_t* out, int32_t* counts,
+                       libtopk_stream_t stream) {
+  if (n < 0 || n > kMaxN || nseg < 0 || nseg > (int64_t)INT32_MAX - 1)
+    return LIBTOPK_ERR_INVALID;
+  if (k < 1) return LIBTOPK_ERR_INVALID;
+  if (k > LIBTOPK_MAX_K) return LIBTOPK_ERR_UNSUPPORTED;
+  if (nseg == 0) return LIBTOPK_OK;
+  if (!offsets || ((uintptr_t)offsets & 7u)) return LIBTOPK_ERR_INVALID;
+  if (!out || ((uintptr_t)out & 3u)) return LIBTOPK_ERR_INVALID;
+  if (counts && ((uintptr_t)counts & 3u)) return LIBTOPK_ERR_INVALID;
+  if (n > 0 && (!in || ((uintptr_t)in & 3u))) return LIBTOPK_ERR_INVALID;
+  const size_t out_b = (size_t)(nseg * k) * 4, off_b = (size_t)(nseg + 1) * 8;
+  if (overlaps(out, out_b, offsets, off_b) ||
+      (n > 0 && overlaps(out, out_b, in, (size_t)n * 4)))
+    return LIBTOPK_ERR_INVALID;
+  if (counts && (overlaps(counts, (size_t)nseg * 4, out, out_b) ||
+                 overlaps(counts, (size_t)nseg * 4, offsets, off_b) ||
+                 (n > 0 && overlaps(counts, (size_t)nseg * 4, in,
+                                    (size_t)n * 4))))
+    return LIBTOPK_ERR_INVALID;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc != LIBTOPK_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Scratch sc;
+  rc = get_scratch(dev, s, &sc);
+  if (rc != LIBTOPK_OK) return rc;
+  SegScratch ss;
+  rc = get_seg(dev, s, n, &ss);
+  if (rc != LIBTOPK_OK) return rc;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    cus = compute_units(dev);
+  }
+  SegParams p;
+  p.in = in;
+  p.n = n;
+  p.in_mis = (int)(((uintptr_t)in & 15u) >> 2);
+  p.offsets = offsets;
+  p.nseg = nseg;
+  p.k = k;
+  p.refresh = refresh_period(k);
+  p.out = out;
+  p.counts = counts;
+  p.med = ss.med;
+  p.med_cap = ss.med_cap;
+  p.huge = ss.huge;
+  p.huge_cap = ss.huge_cap;
+  p.units = ss.units;
+  p.unit_cap = ss.unit_cap;
+  p.cand = ss.cand;
+  p.heads = ss.heads;
+  p.kths = ss.kths;
+  p.ctr = ss.ctr;
+  p.ticket = ss.ticket;
+  p.plan = ss.plan;
+  p.seg_tag = next_epoch(*sc.seg_calls);
+  // 1. One wave per segment: the short ones done, the others listed and
+  // planned.
+  const void* sfn = (const void*)&seg_short_kernel;
+  const int64_t want = (nseg + kWaves - 1) / kWaves;
+  const int64_t slots = (int64_t)resident_blocks(sfn) * cus;
+  p.epoch = next_epoch(*sc.epochs);
+  rc = launch(sfn, (int)(want < slots ? want : slots), p, s);
+  if (rc != LIBTOPK_OK) return rc;
+  // 2. Persistent workgroups over the plan's work items.
+  const void* lfn = seg_long_fn(k);
+  p.epoch = next_epoch(*sc.epochs);
+  return launch(lfn, resident_blocks(lfn) * cus, p, s);
+}
+
 int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
                   int32_t nbins, int64_t* out, libtopk_stream_t stream) {
   if (!out || ((uintptr_t)out & 7u)) return LIBTOPK_ERR_INVALID;
@@ -893,8 +1073,8 @@ int libtopk_debug_scramble(libtopk_stream_t stream, int32_t which,
   int rc = current_device(&dev);
   if (rc != LIBTOPK_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  uint64_t* words[2];
-  int counts[2];
+  uint64_t* words[3];
+  int counts[3];
   int parts = 0;
   if (which == 0) {
     Scratch sc;
@@ -905,6 +1085,19 @@ int libtopk_debug_scramble(libtopk_stream_t stream, int32_t which,
     words[1] = sc.acc;
     counts[1] = kMaxBins;
     parts = 2;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      const Scratch& cur = g_cache[std::make_pair(dev, (void*)s)];
+      if (cur.seg_base) {
+        // the segmented top-k's counters and tickets
+        SegScratch ss;
+        size_t bytes = 0;
+        seg_layout(cur.seg_base, cur.seg_n, &ss, &bytes);
+        words[2] = ss.ctr;
+        counts[2] = 4 + 1 + ss.huge_cap;
+        parts = 3;
+      }
+    }
   } else {
     NoAllocScratch* sc = nullptr;
     std::atomic<uint32_t>* epochs = nullptr;
@@ -968,6 +1161,7 @@ void libtopk_release(void) {
       (void)hipDeviceSynchronize();
       (void)hipFree(kv.second.base);
       if (kv.second.rcand) (void)hipFree(kv.second.rcand);
+      if (kv.second.seg_base) (void)hipFree(kv.second.seg_base);
     }
   }
   g_cache.clear();

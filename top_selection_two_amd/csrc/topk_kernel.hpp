@@ -865,21 +865,20 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
   stage2_finish(cv, k, r, p.out, sh, s2);
 }
 
+// The k largest of the elements that workgroup `blk` of `grid` owns in one
+// row (rin[0..n): its round-robin tiles, and the head and the tail when it
+// is the row's last workgroup), written in descending order to dst[0..k)
+// with agent-coherent stores; with head_out, also its largest and k-th
+// value (for a stage 2 to come).  Stage 1 and the block step of the
+// two-stage design ([TopK] §2.1).  Barriers inside: call uniformly.  The
+// caller's LDS (sh, ring_lds) must be free: on entry no thread may still
+// read what an earlier call left there.
 template <int KCAP, bool FIT, int U>
-__global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
-  __shared__ TopkShared<KCAP> sh;
-  // Each wave's ring of kRing tiles (its quarter of each tile).  A separate
-  // LDS object from `sh`, so that the compiler can tell LDS accesses to
-  // `sh` apart from the in-flight ring loads and does not wait for those.
-  __shared__ v4i ring_lds[kWaves][kRing][U][kWave];
-  static_assert(sizeof(ring_lds) >= sizeof(Stage2Lds), "ring too small");
-  // This workgroup's row, and its place among the row's workgroups.
-  const int row = (int)(blockIdx.x / (unsigned)p.grid);
-  const int blk = (int)blockIdx.x - row * p.grid;
-  const int* __restrict__ rin = p.in + (int64_t)row * p.ld;
-  const RowGeometry geo = row_geometry<U>(rin, p.n);
-  const int64_t slot0 = (int64_t)row * p.grid;  // the row's first block slot
-  const int k = p.k;
+__device__ __forceinline__ void workgroup_topk(
+    const int* __restrict__ rin, int64_t n, int blk, int grid, int k, int R,
+    int* dst, int* head_out, int* kth_out, TopkShared<KCAP>& sh,
+    v4i (&ring_lds)[kWaves][kRing][U][kWave]) {
+  const RowGeometry geo = row_geometry<U>(rin, n);
   const int w = threadIdx.x / kWave;
 
   int L[KCAP];
@@ -899,8 +898,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   // 16 B per lane, no VGPRs), kRing tiles ahead of the one it examines, so
   // the time spent inserting never leaves the memory pipe empty.
   const v4i* __restrict__ body = reinterpret_cast<const v4i*>(rin + geo.head);
-  const int64_t count = tiles_of(geo.ntiles, blk, p.grid);
-  const int R = p.refresh;
+  const int64_t count = tiles_of(geo.ntiles, blk, grid);
   if (count > 0) {
     v4i(*ring)[U][kWave] = ring_lds[w];
     // Byte offsets of this lane's loads within a tile, and the byte
@@ -911,7 +909,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       voff[u] = (uint32_t)((u * kBlock + threadIdx.x) * sizeof(v4i));
     const char* first = reinterpret_cast<const char*>(body) +
                         (int64_t)blk * kTileBytes<U>;
-    const int64_t stride = (int64_t)p.grid * kTileBytes<U>;
+    const int64_t stride = (int64_t)grid * kTileBytes<U>;
     // The workgroup's last tile is examined first, then the others in
     // order (see tile_order): on ascending input the lists then start from
     // the largest values and the bound rejects nearly everything after.
@@ -948,8 +946,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     }
   }
   // Elements outside the full tiles: the unaligned head and the tail.
-  if (blk == p.grid - 1) {
-    const int64_t left = p.n - geo.covered;
+  if (blk == grid - 1) {
+    const int64_t left = n - geo.covered;
     for (int64_t base = 0; base < left; base += kBlock) {
       const int64_t i = base + threadIdx.x;
       int x = kI32Min;
@@ -961,9 +959,6 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
   // barrier: the bound is certified whatever the other waves are doing).
   refresh_bound(L, k, tsh, thr, sh);
   const int T = tsh;  // certified for the workgroup; may differ per wave
-  // A row with one workgroup: its top-k is the row's result.
-  const bool direct = p.grid == 1;
-  int* dst = direct ? p.out + (int64_t)row * k : p.cand + (slot0 + blk) * k;
 
   // ---- block candidates: the workgroup's exact top-k ---------------------
   // The entries >= T among the first k of every list include the
@@ -1012,8 +1007,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     }
     if ((int)threadIdx.x < lb && rk < k) {
       st_agent(dst + rk, v);
-      if (!direct && rk == 0) st_agent(p.heads + slot0 + blk, v);
-      if (!direct && rk == k - 1) st_agent(p.kths + slot0 + blk, v);
+      if (head_out && rk == 0) st_agent(head_out, v);
+      if (head_out && rk == k - 1) st_agent(kth_out, v);
     }
   } else {
     // Wave merge: each wave's top-k of its entries >= T.
@@ -1070,9 +1065,9 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
       if (lane() == 0) {
         sh.bcast[0] = base;
         sh.bcast[1] = unbias(g);
-        if (!direct) {
-          st_agent(p.heads + slot0 + blk, mx);
-          st_agent(p.kths + slot0 + blk, unbias(g));
+        if (head_out) {
+          st_agent(head_out, mx);
+          st_agent(kth_out, unbias(g));
         }
       }
     }
@@ -1084,6 +1079,30 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
     for (int j = ngt + (int)threadIdx.x; j < k; j += kBlock)
       st_agent(dst + j, gv);
   }
+
+}
+
+template <int KCAP, bool FIT, int U>
+__global__ __launch_bounds__(kBlock) void topk_kernel(TopkParams p) {
+  __shared__ TopkShared<KCAP> sh;
+  // Each wave's ring of kRing tiles (its quarter of each tile).  A separate
+  // LDS object from `sh`, so that the compiler can tell LDS accesses to
+  // `sh` apart from the in-flight ring loads and does not wait for those.
+  __shared__ v4i ring_lds[kWaves][kRing][U][kWave];
+  static_assert(sizeof(ring_lds) >= sizeof(Stage2Lds), "ring too small");
+  // This workgroup's row, and its place among the row's workgroups.
+  const int row = (int)(blockIdx.x / (unsigned)p.grid);
+  const int blk = (int)blockIdx.x - row * p.grid;
+  const int* __restrict__ rin = p.in + (int64_t)row * p.ld;
+  const int64_t slot0 = (int64_t)row * p.grid;  // the row's first block slot
+  const int k = p.k;
+  // A row with one workgroup: its top-k is the row's result.
+  const bool direct = p.grid == 1;
+  int* dst = direct ? p.out + (int64_t)row * k : p.cand + (slot0 + blk) * k;
+  workgroup_topk<KCAP, FIT, U>(rin, p.n, blk, p.grid, k, p.refresh, dst,
+                               direct ? nullptr : p.heads + slot0 + blk,
+                               direct ? nullptr : p.kths + slot0 + blk, sh,
+                               ring_lds);
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
   if (direct) return;
