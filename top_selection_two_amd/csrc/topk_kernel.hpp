@@ -997,14 +997,19 @@ __device__ __forceinline__ void workgroup_topk(
   }
   __syncthreads();
   const int lb = sh.bcnt;
-  if (lb <= kBlock) {
-    int v, rk = kBlock;
-    if (lb <= kWave) {  // the usual case
-      v = block_rank64(sh.blist, lb, sh.ranks);
-      if ((int)threadIdx.x < lb) rk = sh.ranks[threadIdx.x];
-    } else {
-      rk = rank_all(sh.blist, lb, v);
+  if (lb <= kWave) {
+    // The usual case: at most 64 entries, sorted across wave 0's lanes (a
+    // register bitonic network), lanes 0..k-1 write them in order.
+    if (w == 0) {
+      const int v = wave_sort_desc<kWave>(lane() < lb ? sh.blist[lane()]
+                                                      : kI32Min);
+      if (lane() < k) st_agent(dst + lane(), v);
+      if (head_out && lane() == 0) st_agent(head_out, v);
+      if (head_out && lane() == k - 1) st_agent(kth_out, v);
     }
+  } else if (lb <= kBlock) {
+    int v;
+    const int rk = rank_all(sh.blist, lb, v);
     if ((int)threadIdx.x < lb && rk < k) {
       st_agent(dst + rk, v);
       if (head_out && rk == 0) st_agent(head_out, v);

@@ -276,6 +276,21 @@ __device__ __forceinline__ void kv_refresh_bound(const KvList<KCAP>& L,
     tsh = unbias(radix_lower_bound(lo, bias(mx), k, 6, cnt));
   }
   thr = max(thr, kv_tsk(tsh));
+  // Ties at the top: if this wave's own lists hold at least k entries of
+  // the value of its largest head, hv, a later element of value hv loses
+  // to all of them (this wave's later elements come at larger positions),
+  // so values <= hv can be skipped, not only values < T.  The snapshot's
+  // heads cannot certify that: another wave may already be a tile ahead.
+  // Only the first four levels are counted (a lower count, so the test
+  // stays sufficient): 256 slots cover k <= 128 when the ties spread over
+  // half the lanes, and a full KCAP-level walk costs more on distinct
+  // values than the rule saves (27 us of 136 on the top-100 of 1e8).
+  constexpr int D = KCAP < 4 ? KCAP : 4;
+  const int hv = wave_max(L.v[0]);
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < D; ++i) c += popc(ballot(L.v[i] == hv));
+  if (c >= k) thr = max(thr, hv);
 }
 
 // Ranks of distinct keys by counting (see block_rank64 and rank_all, which
@@ -330,6 +345,39 @@ __device__ __forceinline__ int kv_rank_all(uint64_t* keys, int n,
   return r;
 }
 
+// The same for n <= 2 * kBlock keys, two per thread: keys[t] and
+// keys[t + kBlock] (0 past n, ranked meaninglessly); keys[] with room for
+// 2 * kBlock + 8.  A barrier inside: call uniformly.  Under heavy ties this
+// replaces selection by counting (64 block-wide counting steps, each a
+// round of barriers: tens of microseconds) with one pass of comparisons.
+__device__ __forceinline__ void kv_rank_all2(uint64_t* keys, int n,
+                                             uint64_t& v0, int& r0,
+                                             uint64_t& v1, int& r1) {
+  const int t = threadIdx.x;
+  const int n8 = (n + 7) & ~7;
+  for (int j = n + t; j < n8; j += kBlock) keys[j] = 0ull;
+  __syncthreads();
+  v0 = t < n ? keys[t] : 0ull;
+  v1 = t + kBlock < n ? keys[t + kBlock] : 0ull;
+  const v4i* q = reinterpret_cast<const v4i*>(keys);
+  r0 = 0;
+  r1 = 0;
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    v4i o4[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) o4[qq] = q[j0 / 2 + qq];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint64_t a = ((uint64_t)(uint32_t)o4[qq].y << 32) |
+                         (uint32_t)o4[qq].x;
+      const uint64_t b = ((uint64_t)(uint32_t)o4[qq].w << 32) |
+                         (uint32_t)o4[qq].z;
+      r0 += (a > v0) + (b > v0);
+      r1 += (a > v1) + (b > v1);
+    }
+  }
+}
+
 // Append the lanes where p holds to an LDS key list (one LDS atomic per
 // wave); returns the wave's base position (wave-uniform).
 __device__ __forceinline__ int kv_wave_append(bool p, uint64_t v,
@@ -378,7 +426,7 @@ template <int KCAP>
 struct TopkKvShared {
   unsigned heads[kBlock];                 // lane-head snapshot (biased)
   alignas(16) uint64_t hkeys[kBlock + 8]; // lane-head keys, then ranks' use
-  alignas(16) uint64_t blist[kBlock + 8]; // keys >= the final bound
+  alignas(16) uint64_t blist[2 * kBlock + 8]; // keys >= the final bound
   int ranks[kWave];
   int bcnt;
   int red[2][kWaves];
@@ -573,7 +621,16 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
   __syncthreads();
   int m = sh.bcast[2];
 
-  // (4) cut to exactly k when there are too many to rank
+  // (4) up to 2 * kBlock survivors are ranked two per thread; more (heavy
+  // ties) are first cut to exactly k by selecting the k-th key by counting
+  if (m > kBlock && m <= 2 * kBlock) {
+    uint64_t v0, v1;
+    int r0, r1;
+    kv_rank_all2(s2.surv, m, v0, r0, v1, r1);
+    if (tid < m && r0 < k) kv_write_out<F32>(p, r0, v0);
+    if (tid + kBlock < m && r1 < k) kv_write_out<F32>(p, r1, v1);
+    return;
+  }
   if (m > kBlock) {
     uint64_t g;
     if (m <= kKvSurvCap) {
@@ -679,17 +736,23 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       sh.heads[threadIdx.x] = bias(m);
       __syncthreads();
       unsigned hu[kWaves];
-      int mx = kI32Min;
+      int mx = kI32Min, mn = kI32Max;
 #pragma unroll
       for (int j = 0; j < kWaves; ++j) {
         hu[j] = sh.heads[lane() + kWave * j];
         mx = max(mx, unbias(hu[j]));
+        mn = min(mn, unbias(hu[j]));
       }
       mx = wave_max(mx);
-      // Six bits over the whole range.  (Searching from the least lane
-      // maximum instead was tighter, 366 against 387 us on the sorted
-      // top-100, but 1 us slower on uniform input.)
-      tsh = unbias(radix_lower_bound(0u, bias(mx), k, 6, RegCount<kWaves>{hu}));
+      mn = wave_min(mn);
+      // Eight bits between the least and the largest lane maximum (every
+      // lane maximum reaches the least, so the search may start there).
+      // Searching from 0 over the whole range left the bound at 0 on small
+      // values (all of [0, 1000) shares the top 22 bits): on sorted input
+      // every lane then inserted every element through whole-list
+      // bubbles.
+      tsh = unbias(radix_lower_bound(bias(mn), bias(mx), k, 8,
+                                     RegCount<kWaves>{hu}));
       thr = kv_tsk(tsh);
       __syncthreads();  // every wave has read the peeked maxima
       sh.heads[threadIdx.x] = 0u;
@@ -828,26 +891,40 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
           if (lane() == 0) base = atomicAdd(&sh.bcnt, popc(b));
           base = uni(base);
           const int pos = base + lanes_below(b);
-          if (q && pos < kBlock) sh.blist[pos] = L.key(i);
+          if (q && pos < 2 * kBlock) sh.blist[pos] = L.key(i);
           // Stop once the list has overflowed (the count then exceeds
-          // kBlock, which sends the workgroup to the fallback).  A list
-          // filled exactly to kBlock must go on: a deeper level may hold
+          // 2 * kBlock, which sends the workgroup to the fallback).  A list
+          // filled exactly to capacity must go on: a deeper level may hold
           // more entries, and stopping would leave the count looking
           // complete.
-          more = base + popc(b) <= kBlock;
+          more = base + popc(b) <= 2 * kBlock;
         }
       }
     }
   }
   __syncthreads();
   int lb = sh.bcnt;
-  if (lb > kBlock) {
+  if (lb > 2 * kBlock) {
     // Too many keys reach T: select the k-th largest g among the list
     // entries >= T by counting, then keep exactly the k keys >= g.
+    // The entries >= T of a lane are a prefix of its list; each wave visits
+    // only as deep as its longest such prefix (a few levels under ties),
+    // not all KCAP slots, in each of the 64 counting steps.
+    int depth = 0;
+    {
+      bool more = true;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < KCAP; ++i) {
+        if (more) {
+          more = ballot(i < k && L.key(i) >= T && L.key(i) != 0ull) != 0;
+          depth += more;
+        }
+      }
+    }
     const uint64_t g = kv_select(k, sh, [&](auto&& f) {
 #pragma unroll
       for (int i = 0; i < KCAP; ++i)
-        if (i < k && L.key(i) >= T && L.key(i) != 0ull) f(L.key(i));
+        if (i < depth && L.key(i) >= T && L.key(i) != 0ull) f(L.key(i));
     });
     if (threadIdx.x == 0) sh.bcnt = 0;
     __syncthreads();
@@ -859,7 +936,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     __syncthreads();
     lb = sh.bcnt;  // == k
   }
-  {
+  if (lb <= kBlock) {
     uint64_t v;
     int rk = kBlock;
     if (lb <= kWave) {
@@ -872,6 +949,22 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       st_agent(dst + rk, v);
       if (rk == 0) st_agent(p.heads + blk, v);
       if (rk == k - 1) st_agent(p.kths + blk, v);
+    }
+  } else {
+    // Ties: up to 2 * kBlock keys reach T, ranked two per thread.
+    uint64_t v0, v1;
+    int r0, r1;
+    kv_rank_all2(sh.blist, lb, v0, r0, v1, r1);
+    const int t = threadIdx.x;
+    if (t < lb && r0 < k) {
+      st_agent(dst + r0, v0);
+      if (r0 == 0) st_agent(p.heads + blk, v0);
+      if (r0 == k - 1) st_agent(p.kths + blk, v0);
+    }
+    if (t + kBlock < lb && r1 < k) {
+      st_agent(dst + r1, v1);
+      if (r1 == 0) st_agent(p.heads + blk, v1);
+      if (r1 == k - 1) st_agent(p.kths + blk, v1);
     }
   }
 
