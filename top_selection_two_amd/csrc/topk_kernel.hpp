@@ -943,6 +943,17 @@ __device__ __forceinline__ void workgroup_topk(
         lds_barrier();
       }
       if (refresh_due(i, R)) refresh_bound(L, k, tsh, thr, sh);
+      // Workgroups blk and blk + grid/2 usually share a CU (the grid fills
+      // every CU once before the second round), and the hardware favours
+      // the older one: on top-20 of 1e8 the first half finished streaming
+      // 10 us before the second (46 against 56 us, median).  Raising each
+      // half's priority in turn, in slots of 5.12 us, evened them (53 and
+      // 56 us) and took 0.5-1 us off the call.
+      if ((((unsigned)(__builtin_amdgcn_s_memrealtime() >> 9)) +
+           (blk >= (grid >> 1) ? 1u : 0u)) & 1u)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
     }
   }
   // Elements outside the full tiles: the unaligned head and the tail.

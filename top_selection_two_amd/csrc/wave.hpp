@@ -149,18 +149,28 @@ __device__ __forceinline__ int64_t tiles_of(int64_t ntiles, int blk,
   return blk < ntiles ? (ntiles - blk + grid - 1) / grid : 0;
 }
 
-// Load local tile i (clamped to the last one, count - 1, so that a prefetch
-// past the end re-reads a tile just read, an L2 hit, instead of branching).
-// Non-temporal: every byte is read exactly once.
+// Load local tile i with buffer loads (non-temporal: every byte is read
+// exactly once).  A prefetch past the end (i >= count) goes through a
+// buffer of no bytes: its loads return zeros and read no memory, with the
+// same instructions, so the wait before each tile stays the same on every
+// path.  (Clamping to the last tile re-read it from HBM: 1.2-1.5 % extra
+// traffic for the statistics and the histogram.)  The buffer's fourth
+// word is the gfx9 default (32-bit data, no swizzle, no stride).
 template <int U>
 __device__ __forceinline__ void load_tile(const v4i* __restrict__ body,
                                           int blk, int grid, int64_t count,
                                           int64_t i, v4i (&d)[U]) {
-  if (i > count - 1) i = count - 1;
-  const int64_t base = (blk + i * grid) * (int64_t)(kBlock * U) + threadIdx.x;
+  const bool in = i < count;
+  const v4i* tile = body + (blk + (in ? i : 0) * grid) * (int64_t)(kBlock * U);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<v4i*>(tile), (short)0, in ? kBlock * U * 16 : 0,
+      0x00020000);
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    d[u] = __builtin_nontemporal_load(body + base + u * kBlock);
+  for (int u = 0; u < U; ++u) {
+    const auto q = __builtin_amdgcn_raw_buffer_load_b128(
+        r, (int)((threadIdx.x + u * kBlock) * 16), 0, 2 /* nt */);
+    d[u] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+  }
 }
 
 // Cross-workgroup hand-off without an agent-scope fence.
