@@ -75,6 +75,21 @@ def test_dup1000_1e7_k100(ltk, variant):
     check(ltk, x, 20)
 
 
+@pytest.mark.parametrize("k", [32, 40, 64, 128])
+@pytest.mark.parametrize("grid", [0, 512, 1024])
+def test_dup1000_stage2_tie_bound(ltk, k, grid):
+    # About 19 copies of the largest value per workgroup at 512 workgroups:
+    # the group-maxima bound leaves over 512 survivors (runs of consecutive
+    # blocks, whose first tiles come early), and stage 2 takes the k-th
+    # largest of all block maxima instead.
+    x = synth.workload("dup1000_1e7")
+    ltk.set_grid(grid)
+    try:
+        check(ltk, x, k)
+    finally:
+        ltk.set_grid(0)
+
+
 def test_pm1000_2p26_floats(ltk):
     # about 33,000 copies of each value: ties by position again
     x = (synth.workload("pm1000_2p26").astype(np.float32) / 8.0)

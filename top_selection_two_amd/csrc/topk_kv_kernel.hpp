@@ -585,41 +585,97 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     if (kv_rank_all(s2.gmax, kBlock, gv) == k - 1) sh.bkey[1] = gv;
   }
   __syncthreads();
-  const uint64_t T2 = umax64(sh.bkey[0], sh.bkey[1]);
+  uint64_t T2 = umax64(sh.bkey[0], sh.bkey[1]);
 
-  // (3) flagged blocks, then their candidate keys >= T2
-  for (int b0 = 0; b0 < G; b0 += kBlock) {
-    const int b = b0 + tid;
-    const bool f = b < G && s2.heads[b] >= T2;
-    wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
-  }
-  __syncthreads();
-  const int nflag = sh.bcast[5];
-  const int total = nflag * k;
-  // Survivors are a prefix of each (descending) list: about one per list
-  // is usual.  Reading whole lists took nflag * k / (8 * kBlock) dependent
-  // round trips.
-  const int pf = min(kPrefix, k);
-  kv_scan_lists(p, s2.blocks, 0, pf, nflag * pf,
-                [&](bool ok, uint64_t c, int b, int e)
-                    __attribute__((always_inline)) {
-                      const bool s = ok && c >= T2;
-                      kv_wave_append(s, c, &sh.bcast[2], s2.surv, kKvSurvCap);
-                      wave_append(s && e == pf - 1 && k > pf, b, &sh.bcast[7],
-                                  s2.longb, kMaxGrid);
-                    });
-  __syncthreads();
-  const int nlong = sh.bcast[7];
-  if (nlong > 0) {
-    kv_scan_lists(p, s2.longb, pf, k - pf, nlong * (k - pf),
-                  [&](bool ok, uint64_t c, int, int)
+  // (3) flagged blocks, then their candidate keys >= T2.  Survivors are a
+  // prefix of each (descending) list: about one per list is usual.
+  // Reading whole lists took nflag * k / (8 * kBlock) dependent round
+  // trips.
+  int nflag = 0, total = 0, m = 0;
+  auto gather = [&]() __attribute__((always_inline)) {
+    if (tid == 0) {
+      sh.bcast[2] = 0;
+      sh.bcast[5] = 0;
+      sh.bcast[7] = 0;
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < G; b0 += kBlock) {
+      const int b = b0 + tid;
+      const bool f = b < G && s2.heads[b] >= T2;
+      wave_append(f, b, &sh.bcast[5], s2.blocks, kMaxGrid);
+    }
+    __syncthreads();
+    nflag = sh.bcast[5];
+    total = nflag * k;
+    const int pf = min(kPrefix, k);
+    kv_scan_lists(p, s2.blocks, 0, pf, nflag * pf,
+                  [&](bool ok, uint64_t c, int b, int e)
                       __attribute__((always_inline)) {
-                        kv_wave_append(ok && c >= T2, c, &sh.bcast[2], s2.surv,
+                        const bool s = ok && c >= T2;
+                        kv_wave_append(s, c, &sh.bcast[2], s2.surv,
                                        kKvSurvCap);
+                        wave_append(s && e == pf - 1 && k > pf, b,
+                                    &sh.bcast[7], s2.longb, kMaxGrid);
                       });
+    __syncthreads();
+    const int nlong = sh.bcast[7];
+    if (nlong > 0) {
+      kv_scan_lists(p, s2.longb, pf, k - pf, nlong * (k - pf),
+                    [&](bool ok, uint64_t c, int, int)
+                        __attribute__((always_inline)) {
+                          kv_wave_append(ok && c >= T2, c, &sh.bcast[2],
+                                         s2.surv, kKvSurvCap);
+                        });
+    }
+    __syncthreads();
+    m = sh.bcast[2];
+  };
+  gather();
+  if (m > 2 * kBlock) {
+    // Ties at the top make group maxima a weak bound: they compare keys by
+    // position, and the groups are runs of consecutive blocks, whose first
+    // tiles are early in the row.  (Key-value top-32 of 1e7 values in
+    // [0, 1000): the 32nd largest of 64 group maxima left 1,025 survivors
+    // and the selection by counting over memory took 240 us.)  The k-th
+    // largest of all G block maxima, each a candidate, is certified too
+    // and much tighter: gather again with it.
+    // Wave 0 holds the G maxima, 16 per lane, and selects the k-th largest
+    // key by ballots: its high word from that of T2a upwards (the group
+    // maxima are block maxima, so at least k of those reach T2a), then its
+    // low word among the maxima with that high word.
+    const uint64_t t2a = sh.bkey[1];
+    __syncthreads();  // every survivor count and bound has been read
+    if (w == 0) {
+      constexpr int V = kMaxGrid / kWave;
+      unsigned hu[V], hl[V];
+      unsigned mx = 0u;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int b = lane() + kWave * j;
+        const uint64_t key = b < G ? s2.heads[b] : 0ull;
+        hu[j] = (unsigned)(key >> 32);
+        hl[j] = (unsigned)key;
+        mx = max(mx, hu[j]);
+      }
+      mx = (unsigned)unbias(wave_max(unbias(mx)));
+      const RegCount<V> cnt{hu};
+      const unsigned lo_hi = (unsigned)(t2a >> 32);
+      const unsigned tv = radix_select(lo_hi, max(mx, lo_hi), k, cnt);
+      const int need = k - (tv == 0xffffffffu ? 0 : cnt(tv + 1u));
+      auto count_lo = [&](unsigned c) __attribute__((always_inline)) -> int {
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) n += popc(ballot(hu[j] == tv && hl[j] >= c));
+        return n;
+      };
+      const unsigned tl = radix_select(tv == lo_hi ? (unsigned)t2a : 0u,
+                                       0xffffffffu, need, count_lo);
+      if (lane() == 0) sh.bkey[1] = ((uint64_t)tv << 32) | tl;
+    }
+    __syncthreads();
+    T2 = umax64(T2, sh.bkey[1]);
+    gather();
   }
-  __syncthreads();
-  int m = sh.bcast[2];
 
   // (4) up to 2 * kBlock survivors are ranked two per thread; more (heavy
   // ties) are first cut to exactly k by selecting the k-th key by counting
