@@ -90,6 +90,35 @@ def test_dup1000_stage2_tie_bound(ltk, k, grid):
         ltk.set_grid(0)
 
 
+@pytest.mark.parametrize("k", [33, 100, 128])
+@pytest.mark.parametrize("grid", [1, 3])
+@pytest.mark.parametrize("f32", [False, True])
+def test_short_lists_one_lane_overflows(ltk, k, grid, f32):
+    # k > 32 runs on lists of 32 keys per lane.  Here one lane of the first
+    # workgroup meets 16 large values in each of its first 4 tiles (its
+    # 16-byte slots at 0, 1 KiB, 2 KiB and 3 KiB of each 16 KiB tile): 64
+    # of the workgroup's top-k, more than its list holds, so the workgroup
+    # finds its top-k again by counting over memory.
+    rng = np.random.default_rng(k + grid)
+    tiles = 64
+    x = rng.integers(0, 1000, tiles * 4096).astype(np.int32)
+    lane0 = np.concatenate([[0, 1, 2, 3], [1024, 1025, 1026, 1027],
+                            [2048, 2049, 2050, 2051], [3072, 3073, 3074, 3075]])
+    big = []
+    for t in range(4):
+        # the first workgroup's t-th tile
+        big.append(lane0 + t * grid * 4096)
+    big = np.concatenate(big)
+    x[big] = 1_000_000 + rng.permutation(big.size).astype(np.int32)
+    if f32:
+        x = x.astype(np.float32)
+    ltk.set_grid(grid)
+    try:
+        check(ltk, x, k)
+    finally:
+        ltk.set_grid(0)
+
+
 def test_pm1000_2p26_floats(ltk):
     # about 33,000 copies of each value: ties by position again
     x = (synth.workload("pm1000_2p26").astype(np.float32) / 8.0)

@@ -282,8 +282,8 @@ const void* topk_kv_fn(int k) {
   if (k <= 16) return (const void*)&topk_kv_kernel<16, true, kTileVec, F32>;
   if (k <= 24) return (const void*)&topk_kv_kernel<24, true, kTileVec, F32>;
   if (k <= 32) return (const void*)&topk_kv_kernel<32, true, kTileVec, F32>;
-  if (k <= 64) return (const void*)&topk_kv_kernel<64, false, kTileVec, F32>;
-  return (const void*)&topk_kv_kernel<128, false, kTileVec, F32>;
+  // k > 32: lists of 32 keys, shorter than k (see kv_lost_check).
+  return (const void*)&topk_kv_kernel<32, false, kTileVec, F32>;
 }
 
 // Both key-value entry points: values are 32-bit words (int32 or float32

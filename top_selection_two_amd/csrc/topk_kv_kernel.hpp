@@ -166,7 +166,7 @@ __device__ __forceinline__ void kv_values(v4i (&d)[U]) {
 template <int KCAP, bool FIT, int U>
 __device__ __forceinline__ void kv_consume(KvList<KCAP>& L, const v4i (&d)[U],
                                            uint32_t pos0, int k, int tsk,
-                                           int& thr) {
+                                           int& thr, uint64_t& lost) {
   constexpr int M = 4 * U;
   static_assert(M <= 16, "slot masks are 16 bits");
   int e[M];
@@ -207,6 +207,9 @@ __device__ __forceinline__ void kv_consume(KvList<KCAP>& L, const v4i (&d)[U],
     // An evicted key bounds every later element of this lane (they come at
     // larger positions).
     thr = max(thr, max(xv, tsk));
+    // Short lists (FIT false: KCAP < k is allowed) may drop a key of the
+    // block's top-k: remember the largest key dropped (see kv_lost).
+    if (!FIT) lost = umax64(lost, kv_key(xv, ~xw));
     pend &= pend - 1;
   } while (ballot(pend != 0));
 }
@@ -733,6 +736,98 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
   }
 }
 
+// Short lists (FIT false: KCAP < k).  A lane keeps its KCAP largest keys,
+// so a key of the block's top-k is dropped when one lane meets more than
+// KCAP of them.  Every key a lane drops is at most the largest key it
+// evicted, `lost` (a key skipped by the lane threshold is below the evicted
+// key that raised it, or below the certified bound).  If no lane evicted a
+// key above the block's k-th key g (sh.bkey[0], written by the result's
+// k-th rank), the lists held every key >= g and the result stands: the
+// common case, at the cost of one block maximum.  Otherwise the block's
+// top-k is found again, exactly, by counting over its elements read back
+// from memory (kv_select: about 65 passes, then one pass gathering the k
+// keys >= the k-th): slow, and only for inputs where one lane of a block
+// meets more than KCAP of the block's top-k.  Barriers inside: call
+// uniformly, after the result has been written.
+template <bool F32, int U, int KCAP>
+__device__ __forceinline__ void kv_lost_check(const TopkKvParams& p, int blk,
+                                           int k, uint64_t lost,
+                                           TopkKvShared<KCAP>& sh,
+                                           uint64_t* dst) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.bkey[1] = 0;
+  __syncthreads();
+  {
+    // wave maximum of a 64-bit key: high words, then the low words of the
+    // lanes holding the top high word
+    const uint32_t lo = (uint32_t)lost, hi = (uint32_t)(lost >> 32);
+    const unsigned whi = (unsigned)unbias(wave_max(unbias(hi)));
+    const unsigned wlo = (unsigned)unbias(wave_max(unbias(hi == whi ? lo : 0u)));
+    if (lane() == 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(&sh.bkey[1]),
+                (unsigned long long)(((uint64_t)whi << 32) | wlo));
+  }
+  __syncthreads();
+  const uint64_t g = sh.bkey[0], worst = sh.bkey[1];
+  if (worst < g) return;
+
+  // Every element of the block as a key, each thread visiting the same
+  // number of times (lanes past the end visit the empty key 0).
+  auto visit = [&](auto&& f) __attribute__((always_inline)) {
+    const v4i* __restrict__ body = reinterpret_cast<const v4i*>(p.in + p.head);
+    const int64_t count = tiles_of(p.ntiles, blk, p.grid);
+    for (int64_t i = 0; i < count; ++i) {
+      const int64_t t = blk + i * p.grid;
+      const v4i* src = body + t * (int64_t)(kBlock * U);
+      v4i d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = src[u * kBlock + tid];
+      kv_values<F32, U>(d);
+      const uint32_t pos0 =
+          (uint32_t)(p.head + t * (int64_t)(4 * kBlock * U)) + 4u * tid;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t q = pos0 + (uint32_t)(4 * kBlock * u);
+        f(kv_key(d[u].x, q));
+        f(kv_key(d[u].y, q + 1));
+        f(kv_key(d[u].z, q + 2));
+        f(kv_key(d[u].w, q + 3));
+      }
+    }
+    if (blk == p.grid - 1) {
+      const int64_t left = p.n - p.covered;
+      for (int64_t base = 0; base < left; base += kBlock) {
+        const int64_t i = base + tid;
+        const int64_t pos = i < p.head ? i : p.covered + i;
+        f(i < left ? kv_key(kv_value<F32>(p.in[pos]), (uint32_t)pos) : 0ull);
+      }
+    }
+  };
+  const uint64_t gk = kv_select(k, sh, visit);
+  __syncthreads();
+  if (tid == 0) sh.bcnt = 0;
+  if (tid < kWave) sh.ranks[tid] = 0;
+  __syncthreads();
+  visit([&](uint64_t key) {
+    kv_wave_append(key >= gk && key != 0ull, key, &sh.bcnt, sh.blist, kBlock);
+  });
+  __syncthreads();
+  const int lb = sh.bcnt;  // == k: keys are distinct
+  uint64_t v;
+  int rk = kBlock;
+  if (lb <= kWave) {
+    v = kv_block_rank64(sh.blist, lb, sh.ranks);
+    if (tid < lb) rk = sh.ranks[tid];
+  } else {
+    rk = kv_rank_all(sh.blist, lb, v);
+  }
+  if (tid < lb && rk < k) {
+    st_agent(dst + rk, v);
+    if (rk == 0) st_agent(p.heads + blk, v);
+    if (rk == k - 1) st_agent(p.kths + blk, v);
+  }
+}
+
 template <int KCAP, bool FIT, int U, bool F32>
 __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   __shared__ TopkKvShared<KCAP> sh;
@@ -750,6 +845,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   }
   int tsh = kI32Min;   // this wave's certified value bound
   int thr = kI32Min;   // skip values <= thr (the first tile skips nothing)
+  uint64_t lost = 0;   // short lists: the largest key this lane dropped
   sh.heads[threadIdx.x] = 0u;
   if (threadIdx.x == 0) sh.bcnt = 0;
   if (threadIdx.x < kWave) sh.ranks[threadIdx.x] = 0;
@@ -839,7 +935,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
       if (i == 0)
         kv_init_list<KCAP, U>(L, d, pos0, thr);
       else
-        kv_consume<KCAP, FIT, U>(L, d, pos0, k, kv_tsk(tsh), thr);
+        kv_consume<KCAP, FIT, U>(L, d, pos0, k, kv_tsk(tsh), thr, lost);
       // After each of the first two tiles every lane publishes its head and
       // the workgroup waits, so that bound refresh sees all 256 fresh
       // heads: the early bounds are much tighter and far fewer elements are
@@ -868,6 +964,7 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
         int xv = q ? s : kI32Min;
         uint32_t xw = q ? ~(uint32_t)pos : 0u;
         kv_list_insert<KCAP, FIT, false>(L, xv, xw, k, kv_tsk(tsh));
+        if (!FIT) lost = umax64(lost, kv_key(xv, ~xw));
       }
     }
   }
@@ -1004,7 +1101,10 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     if ((int)threadIdx.x < lb && rk < k) {
       st_agent(dst + rk, v);
       if (rk == 0) st_agent(p.heads + blk, v);
-      if (rk == k - 1) st_agent(p.kths + blk, v);
+      if (rk == k - 1) {
+        st_agent(p.kths + blk, v);
+        sh.bkey[0] = v;
+      }
     }
   } else {
     // Ties: up to 2 * kBlock keys reach T, ranked two per thread.
@@ -1015,14 +1115,21 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
     if (t < lb && r0 < k) {
       st_agent(dst + r0, v0);
       if (r0 == 0) st_agent(p.heads + blk, v0);
-      if (r0 == k - 1) st_agent(p.kths + blk, v0);
+      if (r0 == k - 1) {
+        st_agent(p.kths + blk, v0);
+        sh.bkey[0] = v0;
+      }
     }
     if (t + kBlock < lb && r1 < k) {
       st_agent(dst + r1, v1);
       if (r1 == 0) st_agent(p.heads + blk, v1);
-      if (r1 == k - 1) st_agent(p.kths + blk, v1);
+      if (r1 == k - 1) {
+        st_agent(p.kths + blk, v1);
+        sh.bkey[0] = v1;
+      }
     }
   }
+  if constexpr (!FIT) kv_lost_check<F32, U>(p, blk, k, lost, sh, dst);
 
   // ---- hand-off: the last workgroup to finish runs stage 2 --------------
   if (!last_to_finish(p.ticket, p.grid, p.epoch, &sh.is_last)) return;
