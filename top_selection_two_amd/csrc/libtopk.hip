@@ -266,14 +266,15 @@ int launch(const void* fn, int grid, P params, hipStream_t stream) {
 }
 
 // List capacity: exactly k rounded up to 8 while that is small (the list
-// then needs no guards), otherwise 64 or 128 slots with chunk guards.
+// then needs no guards); for k > 32, 32 slots (lists shorter than k, with
+// the check of short_list_check).
 const void* topk_fn(int k) {
   if (k <= 8) return (const void*)&topk_kernel<8, true, kTileVec>;
   if (k <= 16) return (const void*)&topk_kernel<16, true, kTileVec>;
   if (k <= 24) return (const void*)&topk_kernel<24, true, kTileVec>;
   if (k <= 32) return (const void*)&topk_kernel<32, true, kTileVec>;
-  if (k <= 64) return (const void*)&topk_kernel<64, false, kTileVec>;
-  return (const void*)&topk_kernel<128, false, kTileVec>;
+  // k > 32: lists of 32 values, shorter than k (see short_list_check).
+  return (const void*)&topk_kernel<32, false, kTileVec>;
 }
 
 template <bool F32>
@@ -462,8 +463,7 @@ const void* seg_long_fn(int k) {
   if (k <= 16) return seg_long_fn_of<16, true>();
   if (k <= 24) return seg_long_fn_of<24, true>();
   if (k <= 32) return seg_long_fn_of<32, true>();
-  if (k <= 64) return seg_long_fn_of<64, false>();
-  return seg_long_fn_of<128, false>();
+  return seg_long_fn_of<32, false>();
 }
 
 // Top-k for LIBTOPK_MAX_K < k <= LIBTOPK_MAX_K_SELECT: four digit passes of

@@ -131,8 +131,9 @@ struct TopkShared {
   alignas(16) int blist[kBlock + 16];
   int ranks[kWave];
   int bcnt;
-  int wave_out[kWaves][KCAP];
+  int wave_out[kWaves][kMaxK];  // each wave's top-k (k <= kMaxK)
   int wave_cnt[kWaves];
+  int kth;                      // the result's k-th value
   int red[2][kWaves];
   int bcast[8];
   int is_last;
@@ -223,12 +224,15 @@ struct ListCount {
   }
 };
 
+// `lost`: with short lists (FIT false: KCAP < k is allowed), the largest
+// value this lane evicted (see short_list_check).
 template <int KCAP, bool FIT>
 __device__ __forceinline__ void admit(int (&L)[KCAP], int x, int k, int tsh,
-                                      int& thr) {
+                                      int& thr, int& lost) {
   if (ballot(x > thr)) {
     const int evicted = list_insert<KCAP, FIT>(L, x, k, tsh);
     thr = max(thr, max(evicted, tsh));
+    if (!FIT) lost = max(lost, evicted);
   }
 }
 
@@ -241,7 +245,7 @@ __device__ __forceinline__ void admit(int (&L)[KCAP], int x, int k, int tsh,
 // slot.
 template <int KCAP, bool FIT, int U>
 __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
-                                        int k, int tsh, int& thr) {
+                                        int k, int tsh, int& thr, int& lost) {
   constexpr int M = 4 * U;
   static_assert(M <= 16, "slot masks are 16 bits");
   int e[M];
@@ -275,6 +279,7 @@ __device__ __forceinline__ void consume(int (&L)[KCAP], const v4i (&d)[U],
     const int x = (pend != 0 && a[0] > thr) ? a[0] : kI32Min;
     const int evicted = list_insert<KCAP, FIT>(L, x, k, tsh);
     thr = max(thr, max(evicted, tsh));
+    if (!FIT) lost = max(lost, evicted);
     pend &= pend - 1;
   } while (ballot(pend != 0));
 }
@@ -865,6 +870,95 @@ __device__ __forceinline__ void topk_stage2(const TopkParams& p, SH& sh,
   stage2_finish(cv, k, r, p.out, sh, s2);
 }
 
+// Short lists (FIT false: KCAP < k).  A lane keeps its KCAP largest values,
+// so a value of the workgroup's top-k is dropped when one lane meets more
+// than KCAP values above the workgroup's k-th largest.  Every value a lane
+// drops is at most the largest value it evicted, `lost` (a value skipped by
+// the lane threshold is below the evicted value that raised it, or below
+// the certified bound).  Equal values are interchangeable here, so if no
+// lane evicted a value above the result's k-th value (sh.kth), the lists
+// held every value above it and the result stands: the common case, at the
+// cost of one block maximum.  Otherwise the workgroup's top-k is found
+// again, exactly, by counting over its elements read back from memory
+// (radix selection of the k-th largest g from the lists' k-th value up,
+// then the values above g ranked and copies of g): slow, and only for
+// inputs where one lane meets more than KCAP of its workgroup's top-k.
+// Barriers inside: call uniformly, after the result has been written.
+template <int KCAP, int U, class SH>
+__device__ __forceinline__ void short_list_check(
+    const int* __restrict__ rin, int64_t n, int blk, int grid, int k,
+    int lost, int head, int* dst, int* head_out, int* kth_out, SH& sh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sh.bcast[2] = kI32Min;
+    sh.bcast[3] = kI32Min;
+  }
+  __syncthreads();  // also publishes sh.kth
+  const int wl = wave_max(lost);
+  const int wh = wave_max(head);
+  if (lane() == 0) {
+    atomicMax(&sh.bcast[2], wl);
+    atomicMax(&sh.bcast[3], wh);
+  }
+  __syncthreads();
+  const int gl = sh.kth, worst = sh.bcast[2], mx = sh.bcast[3];
+  if (worst <= gl) return;
+
+  // Every element of the workgroup, each thread visiting the same number
+  // of times (lanes past the end visit INT_MIN, which counts for nothing
+  // above the lists' k-th value).
+  const RowGeometry geo = row_geometry<U>(rin, n);
+  auto visit = [&](auto&& f) __attribute__((always_inline)) {
+    const v4i* __restrict__ body = reinterpret_cast<const v4i*>(rin + geo.head);
+    const int64_t count = tiles_of(geo.ntiles, blk, grid);
+    for (int64_t i = 0; i < count; ++i) {
+      const v4i* src = body + (blk + i * grid) * (int64_t)(kBlock * U);
+      v4i d[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) d[u] = src[u * kBlock + tid];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        f(d[u].x);
+        f(d[u].y);
+        f(d[u].z);
+        f(d[u].w);
+      }
+    }
+    if (blk == grid - 1) {
+      const int64_t left = n - geo.covered;
+      for (int64_t base = 0; base < left; base += kBlock) {
+        const int64_t i = base + tid;
+        f(i < left ? rin[i < geo.head ? i : geo.covered + i] : kI32Min);
+      }
+    }
+  };
+  int parity = 0;
+  auto count_ge = [&](unsigned c) __attribute__((always_inline)) -> int {
+    const int t = unbias(c);
+    int m = 0;
+    visit([&](int x) { m += x >= t; });
+    return block_sum(m, sh, parity);
+  };
+  // The true k-th largest is >= the lists' (they hold a subset of the
+  // elements), and no element exceeds the largest head (a lane's maximum
+  // is never evicted).
+  const int g = unbias(radix_select(bias(gl), bias(mx), k, count_ge));
+  __syncthreads();
+  if (tid == 0) sh.bcast[0] = 0;
+  __syncthreads();
+  visit([&](int x) { wave_append(x > g, x, &sh.bcast[0], sh.blist, kBlock); });
+  __syncthreads();
+  const int ngt = sh.bcast[0];  // < k
+  int v;
+  const int rk = rank_all(sh.blist, ngt, v);
+  if (tid < ngt) st_agent(dst + rk, v);
+  for (int j = ngt + tid; j < k; j += kBlock) st_agent(dst + j, g);
+  if (head_out && tid == 0) {
+    st_agent(head_out, mx);
+    st_agent(kth_out, g);
+  }
+}
+
 // The k largest of the elements that workgroup `blk` of `grid` owns in one
 // row (rin[0..n): its round-robin tiles, and the head and the tail when it
 // is the row's last workgroup), written in descending order to dst[0..k)
@@ -886,6 +980,8 @@ __device__ __forceinline__ void workgroup_topk(
   for (int i = 0; i < KCAP; ++i) L[i] = kI32Min;
   int tsh = kI32Min;  // this wave's certified bound
   int thr = kI32Min;  // this lane's test: max(its list's last entry, tsh)
+  int lost = kI32Min;  // short lists: the largest value this lane evicted
+  static_assert(FIT || KCAP >= 4 * U, "the first tile fits a short list");
   sh.heads[threadIdx.x] = 0u;  // biased INT_MIN: the weakest valid head
   if (threadIdx.x == 0) sh.bcnt = 0;
   if (threadIdx.x < kWave) sh.ranks[threadIdx.x] = 0;
@@ -932,7 +1028,7 @@ __device__ __forceinline__ void workgroup_topk(
       if (i == 0)
         init_list<KCAP, U>(L, d, thr);
       else
-        consume<KCAP, FIT, U>(L, d, k, tsh, thr);
+        consume<KCAP, FIT, U>(L, d, k, tsh, thr, lost);
       // After each of the first two tiles every lane publishes its head and
       // the workgroup waits, so that bound refresh sees all 256 fresh
       // heads: the early bounds are much tighter and far fewer elements are
@@ -963,7 +1059,7 @@ __device__ __forceinline__ void workgroup_topk(
       const int64_t i = base + threadIdx.x;
       int x = kI32Min;
       if (i < left) x = rin[i < geo.head ? i : geo.covered + i];
-      admit<KCAP, FIT>(L, x, k, tsh, thr);
+      admit<KCAP, FIT>(L, x, k, tsh, thr, lost);
     }
   }
   // One more refresh of this wave's bound from the lane-head snapshot (no
@@ -1017,6 +1113,7 @@ __device__ __forceinline__ void workgroup_topk(
       if (lane() < k) st_agent(dst + lane(), v);
       if (head_out && lane() == 0) st_agent(head_out, v);
       if (head_out && lane() == k - 1) st_agent(kth_out, v);
+      if (lane() == k - 1) sh.kth = v;
     }
   } else if (lb <= kBlock) {
     int v;
@@ -1025,6 +1122,7 @@ __device__ __forceinline__ void workgroup_topk(
       st_agent(dst + rk, v);
       if (head_out && rk == 0) st_agent(head_out, v);
       if (head_out && rk == k - 1) st_agent(kth_out, v);
+      if (rk == k - 1) sh.kth = v;
     }
   } else {
     // Wave merge: each wave's top-k of its entries >= T.
@@ -1032,7 +1130,7 @@ __device__ __forceinline__ void workgroup_topk(
       const int live = list_count_ge<KCAP>(L, k, T);
       int cnt;
       if (live <= k) {
-        list_emit<KCAP>(L, k, T, false, sh.wave_out[w], KCAP);
+        list_emit<KCAP>(L, k, T, false, sh.wave_out[w], kMaxK);
         cnt = live;
       } else {
         const int hi = wave_max(L[0]);
@@ -1040,7 +1138,7 @@ __device__ __forceinline__ void workgroup_topk(
             radix_select(bias(T), bias(hi), k, ListCount<KCAP>{L, k});
         const int gs = unbias(g);
         const int above =
-            list_emit<KCAP>(L, k, gs, true, sh.wave_out[w], KCAP);
+            list_emit<KCAP>(L, k, gs, true, sh.wave_out[w], kMaxK);
         for (int j = lane(); j < k - above; j += kWave)
           sh.wave_out[w][above + j] = gs;
         cnt = k;
@@ -1055,13 +1153,14 @@ __device__ __forceinline__ void workgroup_topk(
     // The values above the k-th (fewer than k) go to LDS, where the whole
     // workgroup ranks them, so the candidates come out in order here too.
     if (w == 0) {
-      constexpr int V = (kWaves * KCAP + kWave - 1) / kWave;
+      constexpr int WO = kMaxK;  // wave_out's row
+      constexpr int V = (kWaves * WO + kWave - 1) / kWave;
       unsigned u[V];
       int mx = kI32Min;
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const int q = lane() + kWave * j;
-        const int ww = q / KCAP, o = q % KCAP;
+        const int ww = q / WO, o = q % WO;
         const int v = (ww < kWaves && o < sh.wave_cnt[ww < kWaves ? ww : 0])
                           ? sh.wave_out[ww][o]
                           : kI32Min;
@@ -1081,6 +1180,7 @@ __device__ __forceinline__ void workgroup_topk(
       if (lane() == 0) {
         sh.bcast[0] = base;
         sh.bcast[1] = unbias(g);
+        sh.kth = unbias(g);
         if (head_out) {
           st_agent(head_out, mx);
           st_agent(kth_out, unbias(g));
@@ -1095,7 +1195,9 @@ __device__ __forceinline__ void workgroup_topk(
     for (int j = ngt + (int)threadIdx.x; j < k; j += kBlock)
       st_agent(dst + j, gv);
   }
-
+  if constexpr (!FIT)
+    short_list_check<KCAP, U>(rin, n, blk, grid, k, lost, L[0], dst,
+                              head_out, kth_out, sh);
 }
 
 template <int KCAP, bool FIT, int U>
