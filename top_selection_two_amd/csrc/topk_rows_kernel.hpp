@@ -17,7 +17,7 @@
 //  1. Lane l loads elements l, l + 64, l + 128, ... of the row: each load
 //     instruction reads 256 consecutive bytes, and any row start and row
 //     stride work (no alignment peel).
-//  2. A certified bound T: for k <= 64, a lower bound on the k-th largest
+//  2. A certified bound T: for k <= 32, a lower bound on the k-th largest
 //     of the 64 lane maxima (k lanes then hold an element >= T); for
 //     larger k, a lower bound on the k-th largest element itself.  Both
 //     come from a short bitwise radix search over ballot counts.
@@ -50,10 +50,11 @@ struct RowsParams {
 
 constexpr int kRowCap = 256;  // candidates per wave held in LDS
 
-// One wave's LDS: kRowCap candidate slots and 16 slots of padding for the
-// ranking reads.
+// One wave's LDS: kRowCap candidate slots, then one slot per lane that
+// takes the compaction's stores with nothing to keep (and the ranking's
+// padding reads).
 struct RowsWaveLds {
-  alignas(16) int buf[kRowCap + 16];
+  alignas(16) int buf[kRowCap + kWave];
 };
 
 // Rank each of the m (<= kRowCap) values in buf by counting and write those
@@ -86,22 +87,22 @@ __device__ __forceinline__ void wave_rank_out(int* buf, int m, int k,
 }
 
 // Append the elements that pass (x[j] > t, or >= t) to buf, one ballot per
-// register slot, at offsets from a wave-uniform count; nothing is written
-// past kRowCap.  Returns the number that pass (it may exceed kRowCap).
-// Slots past n (when not FULL) never pass: callers use t > INT_MIN, or
-// strict.
+// register slot, at offsets from a wave-uniform count; nothing is kept
+// past kRowCap.  Every lane stores in every slot, with no branch: a lane
+// with nothing to keep (or past kRowCap) writes its own slot after
+// kRowCap.  Returns the number that pass (it may exceed kRowCap).  Slots
+// past n (when not FULL) never pass: callers use t > INT_MIN, or strict.
 template <int V, bool STRICT>
 __device__ __forceinline__ int compact(const int (&x)[V], int t, int* buf) {
   int m = 0;  // wave-uniform
+  const int spare = kRowCap + lane();
 #pragma unroll
   for (int j = 0; j < V; ++j) {
     const bool q = STRICT ? x[j] > t : x[j] >= t;
     const uint64_t b = ballot(q);
-    if (b != 0) {
-      const int c = popc(b);
-      if (q && m + c <= kRowCap) buf[m + lanes_below(b)] = x[j];
-      m += c;
-    }
+    const int pos = m + lanes_below(b);
+    buf[min(q ? pos : kI32Max, spare)] = x[j];
+    m += popc(b);
   }
   __builtin_amdgcn_wave_barrier();
   return m;
@@ -146,10 +147,13 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
     return wave_min(mn);
   };
   int T;
-  if (k <= kWave) {
+  if (k <= 32) {
     // 6 steps: a looser bound admits a few more candidates, but the
     // search costs less (A/B on 97,656 x 1,024 rows, top-20: 6 steps
-    // 74.9 us, 8 steps 75.6, 10 steps 76.5).
+    // 74.9 us, 8 steps 75.6, 10 steps 76.5).  Beyond k = 32 the k-th
+    // largest lane maximum falls fast (at k = 64 it is the smallest, and
+    // every element above it is a candidate): the elements are counted
+    // instead.
     const unsigned bm[1] = {bias(mx)};
     T = unbias(radix_lower_bound(bias(wave_min(mx)), bias(hi), k, 6,
                                  RegCount<1>{bm}));
@@ -215,25 +219,36 @@ __global__ __launch_bounds__(kBlock) void topk_rows_kernel(RowsParams p) {
       for (int q = 0; q < Q; ++q)
         d[q] = __builtin_nontemporal_load(src + lane() + kWave * q);
     };
-    v4i cur[Q];
-    if (kPrefetch && r < p.rows) load(r, cur);
-    for (; r < p.rows; r += nwaves) {
-      v4i nxt[Q];
-      const bool more = kPrefetch && r + nwaves < p.rows;
-      if (more) load(r + nwaves, nxt);
-      if (!kPrefetch) load(r, cur);
+    auto run = [&](const v4i (&d)[Q], int64_t row)
+                   __attribute__((always_inline)) {
       int x[V];
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        x[4 * q + 0] = cur[q].x;
-        x[4 * q + 1] = cur[q].y;
-        x[4 * q + 2] = cur[q].z;
-        x[4 * q + 3] = cur[q].w;
+        x[4 * q + 0] = d[q].x;
+        x[4 * q + 1] = d[q].y;
+        x[4 * q + 2] = d[q].z;
+        x[4 * q + 3] = d[q].w;
       }
-      row_topk<V, true>(x, n, k, p.out + r * k, L);
-      if (more) {
-#pragma unroll
-        for (int q = 0; q < Q; ++q) cur[q] = nxt[q];
+      row_topk<V, true>(x, n, k, p.out + row * k, L);
+    };
+    if constexpr (kPrefetch) {
+      // Two buffers in turn (no register copies between rows): each row's
+      // loads are issued before the row before it is processed.
+      v4i a[Q], b[Q];
+      if (r < p.rows) load(r, a);
+      for (; r < p.rows; r += 2 * nwaves) {
+        const int64_t r1 = r + nwaves;
+        if (r1 < p.rows) load(r1, b);
+        run(a, r);
+        if (r1 >= p.rows) break;
+        if (r1 + nwaves < p.rows) load(r1 + nwaves, a);
+        run(b, r1);
+      }
+    } else {
+      for (; r < p.rows; r += nwaves) {
+        v4i a[Q];
+        load(r, a);
+        run(a, r);
       }
     }
   } else {
