@@ -955,8 +955,9 @@ def main():
     if "rows" in P:
         config.update({"rows": P["rows"], "cols": P["cols"], "k": K,
                        "merge": merge})
-    else:
-        config["grid"] = ltk.grid_for(n)
+    elif any(c[1] in ("topk", "kv") and c[2] <= ltk.max_k() for c in calls):
+        # The top-k grid (the other calls size their own grids).
+        config["topk_grid"] = ltk.grid_for(n)
     if P.get("launches_per_call"):
         config["launches_per_call"] = P["launches_per_call"]
     if "segments" in P:

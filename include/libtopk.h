@@ -365,10 +365,14 @@ int libtopk_max_k(void);
 int libtopk_set_grid(int32_t blocks);
 
 /*
- * Workgroups that a call of size n would launch under the current setting
- * (reporting and traffic accounting; no device work).  Returns 0 for n < 1.
- * Key-value calls whose kernel fits only one workgroup per compute unit
- * (k > 64) launch half as many unless a grid is set.
+ * Workgroups that a topk_i32 call of size n (k <= LIBTOPK_MAX_K) would
+ * launch under the current setting (reporting and traffic accounting; no
+ * device work).  Returns 0 for n < 1.  With no grid set, the other calls
+ * choose their own counts: reductions, statistics and selection for
+ * k > LIBTOPK_MAX_K launch at most one workgroup per compute unit,
+ * histograms at most two, all of them fewer on small inputs, and key-value
+ * calls whose kernel fits only one workgroup per compute unit (k > 64) at
+ * most one per unit.
  */
 int32_t libtopk_grid_for(int64_t n);
 

@@ -221,9 +221,33 @@ struct Plan {
   int grid;
 };
 
-// Stage-1 grid: `per_cu` workgroups per CU (two hide each other's
-// latency), capped by the tiles there are.
-Plan plan(const int32_t* in, int64_t n, int cus, int per_cu = 2) {
+// What a launch does with its tiles, for the choice of its grid.
+enum GridKind {
+  kGridTopk,    // top-k and key-value top-k (LDS ring, per-element lists)
+  kGridReduce,  // sum, max, min and the statistics (register pipeline)
+  kGridHist,    // histogram (an LDS atomic per element)
+  kGridSelect,  // the sample, filter and digit passes of k > 128
+};
+
+// Stage-1 grid: up to `per_cu` workgroups per CU, fewer for smaller inputs,
+// capped by the tiles there are.  Every workgroup ends with a device
+// atomic on the launch's one ticket, and those serialise (about 12 ns
+// each under load): on small inputs, where the workgroups finish together,
+// 512 tickets alone take microseconds, so fewer workgroups with more tiles
+// each win until the input is large.  The floors and tile ratios below are
+// the measured best grids on 256 CUs (event-timed, uniform int32, n = 1e6,
+// 4e6, 1.6e7, 3.2e7, 2^26 and 1e8):
+//  * top-k: 192 at 1e6 (9.8 us against 10.5 at 244), 256 at 4e6 (13.3
+//    against 15.5 at 512), 512 from 3.2e7;
+//  * reductions and statistics: 64 at 1e6 (sum 4.5 us against 6.2), 128
+//    at 4e6 (5.6 against 10.0), and never more than one per CU (sum of 1e8
+//    55.9 us against 58.6 at 512; statistics 56.8 against 60.0);
+//  * histogram: 128 at 1e6 (6.8 us against 7.9), 256 at 4e6 (9.6 against
+//    11.8), 512 at 1e8;
+//  * k > 128: 128 up to 4e6 (top-1000 of 4e6 31.8 us against 37.0), one
+//    per CU beyond (top-1000 of 1e8 85.3 us against 87.5 at 512).
+Plan plan(const int32_t* in, int64_t n, int cus, GridKind kind = kGridTopk,
+          int per_cu = 2) {
   Plan pl;
   const uintptr_t a = (uintptr_t)in;
   int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
@@ -233,7 +257,27 @@ Plan plan(const int32_t* in, int64_t n, int cus, int per_cu = 2) {
   pl.ntiles = vecs / (kBlock * kTileVec);
   pl.covered = pl.ntiles * kBlock * kTileVec * 4;
   int g = g_grid_override.load();
-  if (g <= 0) g = per_cu * cus;
+  if (g <= 0) {
+    int64_t lo, hi, want;
+    switch (kind) {
+      case kGridReduce:
+        lo = cus / 4, hi = cus, want = pl.ntiles / 8;
+        break;
+      case kGridHist:
+        lo = cus / 2, hi = 2 * (int64_t)cus, want = pl.ntiles / 4;
+        break;
+      case kGridSelect:
+        lo = cus / 2, hi = cus, want = pl.ntiles / 16;
+        break;
+      default:
+        lo = 3 * (int64_t)cus / 4, hi = (int64_t)per_cu * cus,
+        want = pl.ntiles / 16;
+        break;
+    }
+    if (lo > hi) lo = hi;
+    want = want < lo ? lo : (want > hi ? hi : want);
+    g = (int)(want < 1 ? 1 : want);
+  }
   if (g > kMaxGrid) g = kMaxGrid;
   int64_t cap = pl.ntiles > 0 ? pl.ntiles : 1;
   if (g > cap) g = (int)cap;
@@ -319,7 +363,7 @@ int topk_kv(const int32_t* in, int64_t n, int32_t k, int32_t* out_v,
     cus = compute_units(dev);
     fit = groups_per_cu(fn);
   }
-  const Plan pl = plan(in, n, cus, fit < 2 ? fit : 2);
+  const Plan pl = plan(in, n, cus, kGridTopk, fit < 2 ? fit : 2);
   TopkKvParams p;
   p.in = in;
   p.n = n;
@@ -748,8 +792,10 @@ int topk_i32(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     std::lock_guard<std::mutex> lock(g_mu);
     cus = compute_units(dev);
   }
+  if (k > LIBTOPK_MAX_K)
+    return topk_select(in, n, k, out, s, dev, sc,
+                       plan(in, n, cus, kGridSelect));
   const Plan pl = plan(in, n, cus);
-  if (k > LIBTOPK_MAX_K) return topk_select(in, n, k, out, s, dev, sc, pl);
   TopkParams p;
   p.in = in;
   p.n = n;
@@ -788,7 +834,7 @@ int reduce_i32(const int32_t* in, int64_t n, int32_t op, int64_t* out_i64,
   }
   // n == 0: a one-block launch with nothing to read writes the identity.
   static const int32_t kDummy = 0;
-  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus, kGridReduce);
   ReduceParams p;
   p.in = in;
   p.n = n;
@@ -836,7 +882,7 @@ int reduce_stats_i32(const int32_t* in, int64_t n, int64_t* out,
   }
   // n == 0: a one-block launch with nothing to read writes the identities.
   static const int32_t kDummy = 0;
-  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus, kGridReduce);
   StatsParams p;
   p.in = in;
   p.n = n;
@@ -1048,7 +1094,7 @@ int histogram_i32(const int32_t* in, int64_t n, int32_t lo, int32_t shift,
   }
   // n == 0: a one-block launch with nothing to read writes zero counts.
   static const int32_t kDummy = 0;
-  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus);
+  const Plan pl = plan(n > 0 ? in : &kDummy, n, cus, kGridHist);
   HistParams p;
   p.in = in;
   p.n = n;
