@@ -224,6 +224,22 @@ def test_grid_sweep_gives_identical_results(ltk, grid):
         ltk.set_grid(0)
 
 
+@pytest.mark.parametrize("k", [33, 100, 128])
+def test_stage2_bound_with_fewer_than_256_blocks(ltk, k):
+    # Stage 2 bounds the k-th largest by the group maxima of the blocks;
+    # with fewer than 256 blocks some groups are empty, and with fewer than
+    # k non-empty groups only INT_MIN is certified.  Grids on both sides.
+    x = synth.fill(33, 1_000_003)
+    y = synth.fill(34, 1_000_003, 0, 100)
+    try:
+        for grid in (k - 1, k, k + 1, 200, 244):
+            ltk.set_grid(grid)
+            check_topk(ltk, x, k)
+            check_topk(ltk, y, k)
+    finally:
+        ltk.set_grid(0)
+
+
 def test_repeated_calls_and_two_streams(ltk):
     import torch
     xs = [synth.fill(40 + i, 1_000_000 + 977 * i) for i in range(4)]
