@@ -202,6 +202,21 @@ def test_grid_sweep(ltk, grid):
         ltk.set_grid(0)
 
 
+@pytest.mark.parametrize("k", [33, 100, 128])
+def test_stage2_bound_with_fewer_blocks_than_k(ltk, k):
+    # With fewer block lists than k, stage 2 bounds the result by the k-th
+    # largest of the lists' first ceil(k / G) keys; grids on both sides.
+    x = synth.fill(36, 500_003)
+    y = synth.fill(37, 500_003, 0, 100)
+    try:
+        for grid in (1, 7, k - 1, k, k + 1, 122):
+            ltk.set_grid(grid)
+            check(ltk, x, k)
+            check(ltk, y, k)
+    finally:
+        ltk.set_grid(0)
+
+
 @pytest.mark.parametrize("order", ["ascending", "descending"])
 def test_monotone_input_over_many_tiles(ltk, order):
     # Several tiles per workgroup, the last examined first; with ties, so

@@ -588,6 +588,24 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     if (kv_rank_all(s2.gmax, kBlock, gv) == k - 1) sh.bkey[1] = gv;
   }
   __syncthreads();
+  if (G < k) {
+    // Fewer lists than k: their maxima certify nothing.  The first
+    // j = ceil(k / G) keys of every list are G j >= k candidates, so the
+    // k-th largest of them bounds the result's k-th key (key-value top-128
+    // of 5e5 over 122 blocks took 508 us with no bound).  G j < G + k <
+    // 2 kMaxK = kBlock keys, one per thread, ranked in s2.gmax (free by
+    // now); the bound joins T2b's slot, which stage 2 reads only below.
+    const int j = (k + G - 1) / G;
+    const int cnt = G * j;
+    if (tid < cnt) {
+      const int b = tid / j, e = tid - b * j;
+      s2.gmax[tid] = ld_agent(p.cand + (int64_t)b * k + e);
+    }
+    uint64_t v;
+    const int rk = kv_rank_all(s2.gmax, cnt, v);
+    if (tid < cnt && rk == k - 1) sh.bkey[0] = umax64(sh.bkey[0], v);
+    __syncthreads();
+  }
   uint64_t T2 = umax64(sh.bkey[0], sh.bkey[1]);
 
   // (3) flagged blocks, then their candidate keys >= T2.  Survivors are a
