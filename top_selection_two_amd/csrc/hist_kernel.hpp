@@ -81,12 +81,11 @@ __device__ __forceinline__ void for_each_vector(const int* in, int64_t n,
     if (i < cnt) tile(A);
   }
   if (blk == grid - 1) {
-    const int64_t left = n - covered;
-    for (int64_t base = 0; base < left; base += kBlock) {
-      const int64_t i = base + threadIdx.x;
-      const bool ok = i < left;
-      fe(ok ? in[i < head ? i : covered + i] : kI32Min, ok);
-    }
+    visit_rest<kBlock * U * 4>(in, n, head, covered,
+                               [&](int x, int64_t, bool ok)
+                                   __attribute__((always_inline)) {
+                                     fe(x, ok);
+                                   });
   }
 }
 

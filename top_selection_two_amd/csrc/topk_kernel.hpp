@@ -1085,13 +1085,11 @@ __device__ __forceinline__ void workgroup_topk(
   }
   // Elements outside the full tiles: the unaligned head and the tail.
   if (blk == grid - 1) {
-    const int64_t left = n - geo.covered;
-    for (int64_t base = 0; base < left; base += kBlock) {
-      const int64_t i = base + threadIdx.x;
-      int x = kI32Min;
-      if (i < left) x = rin[i < geo.head ? i : geo.covered + i];
-      admit<KCAP, FIT>(L, x, k, tsh, thr, lost);
-    }
+    visit_rest<kBlock * U * 4>(rin, n, geo.head, geo.covered,
+                               [&](int x, int64_t, bool)
+                                   __attribute__((always_inline)) {
+                                     admit<KCAP, FIT>(L, x, k, tsh, thr, lost);
+                                   });
   }
   // One more refresh of this wave's bound from the lane-head snapshot (no
   // barrier: the bound is certified whatever the other waves are doing).

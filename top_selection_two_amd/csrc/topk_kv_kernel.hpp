@@ -970,21 +970,19 @@ __global__ __launch_bounds__(kBlock) void topk_kv_kernel(TopkKvParams p) {
   // only the shared bound (index-free) filters them; insertion compares
   // whole keys.
   if (blk == p.grid - 1) {
-    const int64_t left = p.n - p.covered;
-    for (int64_t base = 0; base < left; base += kBlock) {
-      const int64_t i = base + threadIdx.x;
-      const bool ok = i < left;
-      const int64_t pos = i < p.head ? i : p.covered + i;
-      const int s = ok ? kv_value<F32>(p.in[pos]) : kI32Min;
-      const bool q = ok && s >= tsh;
-      // Inserting the empty key 0 leaves a list unchanged.
-      if (ballot(q)) {
-        int xv = q ? s : kI32Min;
-        uint32_t xw = q ? ~(uint32_t)pos : 0u;
-        kv_list_insert<KCAP, FIT, false>(L, xv, xw, k, kv_tsk(tsh));
-        if (!FIT) lost = umax64(lost, kv_key(xv, ~xw));
-      }
-    }
+    visit_rest<kBlock * U * 4>(
+        p.in, p.n, p.head, p.covered,
+        [&](int x, int64_t pos, bool ok) __attribute__((always_inline)) {
+          const int s = ok ? kv_value<F32>(x) : kI32Min;
+          const bool q = ok && s >= tsh;
+          // Inserting the empty key 0 leaves a list unchanged.
+          if (ballot(q)) {
+            int xv = q ? s : kI32Min;
+            uint32_t xw = q ? ~(uint32_t)pos : 0u;
+            kv_list_insert<KCAP, FIT, false>(L, xv, xw, k, kv_tsk(tsh));
+            if (!FIT) lost = umax64(lost, kv_key(xv, ~xw));
+          }
+        });
   }
 
   // ---- epilogue: the block's k largest keys ------------------------------

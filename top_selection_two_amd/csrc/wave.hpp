@@ -193,6 +193,39 @@ __device__ __forceinline__ T ld_agent(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
+// The elements outside a stream's full tiles -- the unaligned head (fewer
+// than 4) and the tail (less than one tile of TILE elements) -- one per
+// thread and round, as f(x, pos, ok): x the element at position pos of
+// `in`, ok false (x INT_MIN) past the end.  Every thread takes part in
+// every round that has an element, so f may use wave votes.  The loads of
+// all rounds are issued before the first call: one memory round trip, not
+// one per round (a tail of 3,392 elements took 14 dependent round trips,
+// about 4 us, on the last workgroup's path).
+template <int TILE, class F>
+__device__ __forceinline__ void visit_rest(const int* in, int64_t n,
+                                           int64_t head, int64_t covered,
+                                           F&& f) {
+  constexpr int R = (3 + TILE + kBlock - 1) / kBlock;
+  const int64_t left = n - covered;
+  int x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = (int64_t)r * kBlock + threadIdx.x;
+    x[r] = i < left ? in[i < head ? i : covered + i] : kI32Min;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = (int64_t)r * kBlock + threadIdx.x;
+    if ((int64_t)r * kBlock < left) f(x[r], i < head ? i : covered + i, i < left);
+  }
+  // The stream geometry leaves fewer; any more go round by round.
+  for (int64_t base = (int64_t)R * kBlock; base < left; base += kBlock) {
+    const int64_t i = base + threadIdx.x;
+    const int64_t pos = i < head ? i : covered + i;
+    f(i < left ? in[pos] : kI32Min, pos, i < left);
+  }
+}
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void drain_memory_ops() {
   __builtin_amdgcn_s_waitcnt(0);
