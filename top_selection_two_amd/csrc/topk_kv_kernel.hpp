@@ -397,31 +397,55 @@ __device__ __forceinline__ int kv_wave_append(bool p, uint64_t v,
 }
 
 // The k-th largest of a set of distinct keys spread over the workgroup, by
-// counting: a 32-bit radix pass on the high words, then one on the low
-// words among the keys with that high word.  visit(f) calls f(key) for
-// each key this thread holds (a fixed, uniform loop structure); at least k
-// keys must exist.  Barriers inside: call uniformly.
+// radix selection with 8-bit digits ([Radix] §3.2's digits, used to select
+// instead of sort): eight passes, each counting into a 256-bin LDS
+// histogram the digit of every key whose higher digits equal those chosen
+// so far, then taking the bin that holds the k-th largest.  (Counting bit
+// by bit took 65 passes: key-value top-128 of 1e6 values in [0, 1000),
+// which then selected over 521 tied survivors in memory, took 488 us so,
+// 107 us with digits.)
+// visit(f) calls f(key) for each key this thread holds (a fixed, uniform
+// loop structure); at least k keys must exist.  The histogram lives in
+// sh.hkeys, free wherever this is called (after the epilogue's use of it).
+// Barriers inside: call uniformly.
 template <class SH, class Visit>
 __device__ __forceinline__ uint64_t kv_select(int k, SH& sh, Visit&& visit) {
-  int parity = 0;
-  auto count_hi = [&](unsigned c) __attribute__((always_inline)) -> int {
-    int m = 0;
-    visit([&](uint64_t key) { m += (unsigned)(key >> 32) >= c; });
-    return block_sum(m, sh, parity);
-  };
-  const unsigned ghi = radix_select(0u, 0xffffffffu, k, count_hi);
-  int above = 0;
-  visit([&](uint64_t key) { above += (unsigned)(key >> 32) > ghi; });
-  above = block_sum(above, sh, parity);
-  auto count_lo = [&](unsigned c) __attribute__((always_inline)) -> int {
-    int m = 0;
-    visit([&](uint64_t key) {
-      m += ((unsigned)(key >> 32) == ghi) & ((unsigned)key >= c);
+  constexpr int kBins = 256;  // one per thread
+  static_assert(kBlock == kBins, "one bin per thread");
+  unsigned* h = reinterpret_cast<unsigned*>(sh.hkeys);
+  const int t = threadIdx.x, w = t / kWave;
+  uint64_t prefix = 0ull;
+  int kleft = k;
+  for (int d = 7; d >= 0; --d) {
+    const unsigned shift = 8u * (unsigned)d;
+    // The bits above this digit (none for the first).
+    const uint64_t high = d == 7 ? 0ull : ~0ull << (shift + 8u);
+    h[t] = 0u;
+    __syncthreads();
+    visit([&](uint64_t key) __attribute__((always_inline)) {
+      if ((key & high) == prefix)
+        atomicAdd(&h[(unsigned)(key >> shift) & 0xffu], 1u);
     });
-    return block_sum(m, sh, parity);
-  };
-  const unsigned glo = radix_select(0u, 0xffffffffu, k - above, count_lo);
-  return ((uint64_t)ghi << 32) | glo;
+    __syncthreads();
+    // Thread t looks at bin 255 - t: its inclusive scan is the count of
+    // keys in the bucket at or above that bin.
+    const int c = (int)h[kBins - 1 - t];
+    const int incl_w = wave_scan_incl(c);
+    if (lane() == kWave - 1) sh.red[0][w] = incl_w;
+    __syncthreads();
+    int incl = incl_w;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) incl += j < w ? sh.red[0][j] : 0;
+    if (incl >= kleft && incl - c < kleft) {
+      sh.bcast[0] = kBins - 1 - t;
+      sh.bcast[1] = incl - c;
+    }
+    __syncthreads();
+    prefix |= (uint64_t)(unsigned)sh.bcast[0] << shift;
+    kleft -= sh.bcast[1];
+    __syncthreads();  // h, red and bcast are written again next pass
+  }
+  return prefix;
 }
 
 // ---- LDS layouts ----------------------------------------------------------
@@ -666,7 +690,26 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     // low word among the maxima with that high word.
     const uint64_t t2a = sh.bkey[1];
     __syncthreads();  // every survivor count and bound has been read
-    if (w == 0) {
+    const int jl = min(k, 2 * kBlock / G);  // list entries that fit a ranking
+    if (jl >= 2) {
+      // Up to 256 blocks: the first jl keys of every list, ranked two per
+      // thread (G jl <= 512 keys, at least k).  Under ties a list's first
+      // keys are its earliest copies of the top value, so their k-th
+      // largest reaches further into the ties than the k-th largest block
+      // maximum.  (Key-value top-128 of 1e6 values in [0, 1000) over 192
+      // blocks: the k-th block maximum left 521 survivors, more than the
+      // ranking holds.)
+      const int cnt = G * jl;
+      for (int i = tid; i < cnt; i += kBlock) {
+        const int b = i / jl, e = i - b * jl;
+        s2.surv[i] = ld_agent(p.cand + (int64_t)b * k + e);
+      }
+      uint64_t v0, v1;
+      int r0, r1;
+      kv_rank_all2(s2.surv, cnt, v0, r0, v1, r1);
+      if (tid < cnt && r0 == k - 1) sh.bkey[1] = v0;
+      if (tid + kBlock < cnt && r1 == k - 1) sh.bkey[1] = v1;
+    } else if (w == 0) {
       constexpr int V = kMaxGrid / kWave;
       unsigned hu[V], hl[V];
       unsigned mx = 0u;
@@ -763,8 +806,8 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
 // k-th rank), the lists held every key >= g and the result stands: the
 // common case, at the cost of one block maximum.  Otherwise the block's
 // top-k is found again, exactly, by counting over its elements read back
-// from memory (kv_select: about 65 passes, then one pass gathering the k
-// keys >= the k-th): slow, and only for inputs where one lane of a block
+// from memory (kv_select: eight passes, then one pass gathering the k
+// keys >= the k-th): slower, and only for inputs where one lane of a block
 // meets more than KCAP of the block's top-k.  Barriers inside: call
 // uniformly, after the result has been written.
 template <bool F32, int U, int KCAP>
