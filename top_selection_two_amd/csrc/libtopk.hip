@@ -559,7 +559,9 @@ int topk_select(const int32_t* in, int64_t n, int32_t k, int32_t* out,
     q.nvec = nvec;
     q.grid = grid;
     q.need = need;
-    q.stride = nvec / ((int64_t)grid * kSampleThreads);
+    // nvec < 2^31 and S >= kSampleThreads, so i * step < nvec * 2^32 fits.
+    q.step = (uint64_t)(((unsigned __int128)nvec << 32) /
+                        (uint64_t)((int64_t)grid * kSampleThreads));
     q.st = sc.rstate;
     q.samp = rcand + kCandCap;
     q.samp_cnt = q.samp + kSampleGridMax * kNeedMax;

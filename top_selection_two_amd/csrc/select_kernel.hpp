@@ -280,7 +280,8 @@ constexpr int kUnionSlots = 4 * kSampleThreads;  // grid * need <= this
 struct SampleParams {
   const v4i* body;   // the 16-byte-aligned body of the input
   int64_t nvec;      // vectors in it
-  int64_t stride;    // vectors between consecutive samples
+  uint64_t step;     // vectors between consecutive samples, 32.32 fixed
+                     // point: sample i reads vector (i * step) >> 32
   int grid;          // workgroups, <= kSampleGridMax
   int need;          // 1 <= need <= kNeedMax, grid * need <= kUnionSlots
   RadixState* st;
@@ -363,8 +364,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleParams p) 
   if (t == 0) sh.cnt = 0;
   unsigned u[4];
   {
-    const int64_t v = ((int64_t)blockIdx.x * kSampleThreads + t) * p.stride;
-    // Vectors past the end (none while S * stride <= nvec) count as
+    // Spread over the whole body: a whole-vector stride (nvec / S rounded
+    // down) left up to S vectors at the end unread, the top of a sorted
+    // input (top-1000 of 3e6 sorted values then copied 117,063 candidates
+    // aside instead of about 1,700).
+    const int64_t v = (int64_t)(
+        ((uint64_t)blockIdx.x * kSampleThreads + (uint64_t)t) * p.step >> 32);
+    // Vectors past the end (none: i < S gives v < nvec) count as
     // INT_MIN, never above a real threshold's rank.
     const v4i d = v < p.nvec ? __builtin_nontemporal_load(p.body + v)
                              : v4i{kI32Min, kI32Min, kI32Min, kI32Min};
@@ -1118,12 +1124,13 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   }
   const int m = s.bucket;
   if (m < k) {
-    // Fewer than k values above t: all of them, then copies of t.
+    // Fewer than k values above t: all of them, sorted, then copies of t
+    // (only the m values are sorted: under heavy ties m is small, often 0).
     const int* cand = p.cand;
     for (int i = t; i < m; i += kFinThreads) sh.top[i] = cand[i];
-    for (int i = m + t; i < k; i += kFinThreads) sh.top[i] = s.thresh;
+    for (int i = m + t; i < k; i += kFinThreads) p.out[i] = s.thresh;
     __syncthreads();
-    sort_desc(sh.top, p.out, k, sh.top);
+    if (m > 0) sort_desc(sh.top, p.out, m, sh.top);
     if (t == 0) p.st->fast = 0;
     return;
   }
