@@ -174,6 +174,10 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
   } else if (m <= kWave) {
     const int v = wave_sort_desc<kWave>(lane() < m ? L.buf[lane()] : kI32Min);
     if (lane() < k) out[lane()] = v;
+  } else if (T == hi) {
+    // The bound is the row maximum: at least k elements equal it, and they
+    // are the result (a row of ties would otherwise rank all of them).
+    for (int j = lane(); j < k; j += kWave) out[j] = hi;
   } else if (m <= kRowCap) {
     // 4'. Up to kRowCap candidates: rank by counting.
     wave_rank_out(L.buf, m, k, out);
