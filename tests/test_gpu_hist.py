@@ -134,6 +134,11 @@ def test_hot_bins(ltk, nbins):
         check_hist(ltk, x, min(v, 0), 0 if nbins > 1 else 31, nbins)
     alt = np.tile(np.array([3, 250], np.int32), 600_000)
     check_hist(ltk, alt, 0, 0, nbins)
+    # A whole wave's elements in one bin add with one atomic; below the
+    # range they add nowhere.
+    check_hist(ltk, np.full(1_000_003, -7, np.int32), 0, 0, nbins)
+    runs = np.repeat(np.arange(40, dtype=np.int32), 50_000)
+    check_hist(ltk, runs, 0, 2, nbins)
 
 
 @pytest.mark.parametrize("grid", [1, 7, 64, 1024])

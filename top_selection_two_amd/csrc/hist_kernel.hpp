@@ -169,13 +169,35 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
   __syncthreads();
   unsigned* hw = per_wave ? h + w * kWaveHistBins : h;
 
-  for_each_element<U>(p.in, p.n, p.head, p.ntiles, p.covered, p.grid,
-                      [&](int x, bool ok) __attribute__((always_inline)) {
-                        // x >= lo makes x - lo exact in 32 unsigned bits.
-                        const unsigned d = ((unsigned)x - (unsigned)lo) >> shift;
-                        if (ok && x >= lo && d < (unsigned)nb)
-                          atomicAdd(&hw[d], 1u);
-                      });
+  // An element's bin, or nb and more when it has none (x >= lo makes
+  // x - lo exact in 32 unsigned bits).
+  auto bin_of = [&](int x) __attribute__((always_inline)) -> unsigned {
+    return x >= lo ? ((unsigned)x - (unsigned)lo) >> shift : 0xffffffffu;
+  };
+  // Same-address LDS atomics serialise, so a wave whose 256 elements of
+  // one vector slot all share a bin adds 256 with one atomic (a histogram
+  // of 1e8 equal values, or of values that all fall into one bin, took
+  // 333 us with an atomic per element, against 61 us for spread values).
+  for_each_vector<U>(
+      p.in, p.n, p.head, p.ntiles, p.covered, p.grid, (int)blockIdx.x,
+      [&](const v4i& v) __attribute__((always_inline)) {
+        const unsigned b0 = bin_of(v.x), b1 = bin_of(v.y), b2 = bin_of(v.z),
+                       b3 = bin_of(v.w);
+        const unsigned bu = (unsigned)uni((int)b0);
+        // Tiles keep every lane active.
+        if (ballot((b0 == bu) & (b1 == bu) & (b2 == bu) & (b3 == bu)) == ~0ull) {
+          if (lane() == 0 && bu < (unsigned)nb) atomicAdd(&hw[bu], 4u * kWave);
+        } else {
+          if (b0 < (unsigned)nb) atomicAdd(&hw[b0], 1u);
+          if (b1 < (unsigned)nb) atomicAdd(&hw[b1], 1u);
+          if (b2 < (unsigned)nb) atomicAdd(&hw[b2], 1u);
+          if (b3 < (unsigned)nb) atomicAdd(&hw[b3], 1u);
+        }
+      },
+      [&](int x, bool ok) __attribute__((always_inline)) {
+        const unsigned d = bin_of(x);
+        if (ok && d < (unsigned)nb) atomicAdd(&hw[d], 1u);
+      });
   __syncthreads();
 
   // This workgroup's counts into the device counters.
