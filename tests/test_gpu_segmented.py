@@ -65,7 +65,8 @@ def test_mixed_lengths(k):
         [255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 2048, 2049,
          4095, 4096, 4097, 4098],                     # bucket edges
         rng.integers(4097, 40_000, 40),               # medium
-        [262_143, 262_144, 262_145],                  # medium / huge edge
+        [131_071, 131_072, 131_073],                  # medium / huge edge
+        [262_143, 262_144, 262_145],                  # one / two units
         [700_001, 2_500_003],                         # huge
     ]).astype(np.int64)
     rng.shuffle(lengths)

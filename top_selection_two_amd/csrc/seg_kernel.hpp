@@ -46,8 +46,8 @@
 namespace ltk {
 
 constexpr int64_t kSegShort = 4096;         // one wave, in registers
-constexpr int64_t kSegWhole = 1 << 16;      // one workgroup, whole segment
-constexpr int64_t kSegUnit = 1 << 16;       // a huge segment's units
+constexpr int64_t kSegWhole = 1 << 17;      // one workgroup, whole segment
+constexpr int64_t kSegUnit = 1 << 18;       // a huge segment's units
 constexpr int kSegStageMed = 64;            // per-wave LDS staging of the
 constexpr int kSegStageHuge = 16;           // listed segments
 constexpr int64_t kSegTile = kBlock * 16;   // elements in one stage-1 tile
