@@ -103,7 +103,7 @@ def test_row_lengths(ltk, rng, cols):
 
 @pytest.mark.parametrize("pad,offset", [(1, 0), (3, 1), (17, 2), (0, 3),
                                         (4, 0), (1000, 1)])
-@pytest.mark.parametrize("cols", [100, 1024, 3001, 4096, 5000, 70_001])
+@pytest.mark.parametrize("cols", [30, 64, 100, 1024, 3001, 4096, 5000, 70_001])
 def test_strided_and_misaligned_rows(ltk, rng, cols, pad, offset):
     x = rand_rows(rng, 9, cols)
     check_batched(ltk, x, 20, pad=pad, offset=offset)

@@ -76,6 +76,28 @@ def test_mixed_lengths(k):
     check(x, offsets, k)
 
 
+@pytest.mark.parametrize("k", [1, 20, 100, 128])
+def test_many_short_segments(k):
+    # An average length below 1024 takes the lean short kernel, which lists
+    # segments of 1025 .. 4096 elements for one wave each of the long
+    # kernel; a few medium and huge ones ride along.
+    rng = np.random.default_rng(200 + k)
+    lengths = np.concatenate([
+        rng.integers(0, 100, 30_000),                 # tiny (and empty)
+        rng.integers(100, 1025, 2_000),               # short
+        [1024, 1025, 2048, 2049, 4096, 4097],         # mid-length edges
+        rng.integers(1025, 4097, 300),                # mid-length
+        rng.integers(4097, 100_000, 5),               # medium
+        [300_001],                                    # huge
+    ]).astype(np.int64)
+    rng.shuffle(lengths)
+    offsets = cuts_from_lengths(lengths, start=1)
+    x = synth.fill(50 + k, int(offsets[-1]) + 3)
+    assert x.size < 1024 * lengths.size  # the lean kernel
+    print("many short k=%d nseg=%d n=%d" % (k, lengths.size, x.size), flush=True)
+    check(x, offsets, k)
+
+
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
 def test_misaligned_array_and_starts(offset):
     rng = np.random.default_rng(offset)

@@ -414,14 +414,16 @@ int get_rcand(int dev, hipStream_t stream, int** out) {
 }
 
 // The segmented top-k's scratch for inputs of up to n elements: lists of
-// the medium and huge segments, the units of the huge ones with their
-// candidates, maxima and k-th values, three counters, one ticket per huge
-// segment plus one, and the plan.  Sized from n (valid offsets list at
-// most n / (kSegShort + 1) medium and n / (kSegWhole + 1) huge segments,
-// and at most n / kSegUnit + huge units); grown on demand, the stream
+// the mid-length, medium and huge segments, the units of the huge ones
+// with their candidates, maxima and k-th values, four counters, one ticket
+// per huge segment plus one, and the plan.  Sized from n (valid offsets
+// list at most n / (kSegReg + 1) mid-length, n / (kSegShort + 1) medium
+// and n / (kSegWhole + 1) huge segments, and at most n / kSegUnit + huge
+// units); grown on demand, the stream
 // synchronised before the old area is freed.
 struct SegScratch {
   int* med;
+  int* mid;
   SegHuge* huge;
   SegUnit* units;
   int* cand;
@@ -430,12 +432,13 @@ struct SegScratch {
   uint64_t* ctr;
   uint64_t* ticket;
   SegPlan* plan;
-  int med_cap, huge_cap, unit_cap;
+  int med_cap, mid_cap, huge_cap, unit_cap;
 };
 
 void seg_layout(void* base, int64_t n, SegScratch* s, size_t* bytes) {
   const int64_t nn = n < ((int64_t)1 << 20) ? ((int64_t)1 << 20) : n;
   s->med_cap = (int)(nn / (kSegShort + 1) + 1);
+  s->mid_cap = (int)(nn / (kSegReg + 1) + 1);
   s->huge_cap = (int)(nn / (kSegWhole + 1) + 1);
   s->unit_cap = (int)(nn / kSegUnit + s->huge_cap + 1);
   size_t off = 0;
@@ -452,6 +455,7 @@ void seg_layout(void* base, int64_t n, SegScratch* s, size_t* bytes) {
   s->units = (SegUnit*)take((size_t)s->unit_cap * sizeof(SegUnit));
   s->huge = (SegHuge*)take((size_t)s->huge_cap * sizeof(SegHuge));
   s->med = (int*)take((size_t)s->med_cap * 4);
+  s->mid = (int*)take((size_t)s->mid_cap * 4);
   s->plan = (SegPlan*)take(sizeof(SegPlan));
   s->ctr = (uint64_t*)take(4 * 8 + (size_t)(1 + s->huge_cap) * 8);
   s->ticket = s->ctr + 4;
@@ -630,6 +634,8 @@ const void* rows_fn_v(bool full) {
 }
 
 const void* rows_fn(const int32_t* in, int64_t n, int64_t ld) {
+  // Rows of at most 64 elements: one per lane, sorted across the wave.
+  if (n <= kWave) return (const void*)&topk_rows_kernel<1, false>;
   const int v = n <= 256 ? 4 : n <= 512 ? 8 : n <= 1024 ? 16 : n <= 2048 ? 32
                                                                         : 64;
   const bool full = n == 64 * v && ((uintptr_t)in & 15u) == 0 && ld % 4 == 0;
@@ -1048,6 +1054,8 @@ int topk_segmented_i32(const int32_t* in, int64_t n, const int64_t* offsets,
   p.counts = counts;
   p.med = ss.med;
   p.med_cap = ss.med_cap;
+  p.mid = ss.mid;
+  p.mid_cap = ss.mid_cap;
   p.huge = ss.huge;
   p.huge_cap = ss.huge_cap;
   p.units = ss.units;
@@ -1061,7 +1069,11 @@ int topk_segmented_i32(const int32_t* in, int64_t n, const int64_t* offsets,
   p.seg_tag = next_epoch(*sc.seg_calls);
   // 1. One wave per segment: the short ones done, the others listed and
   // planned.
-  const void* sfn = (const void*)&seg_short_kernel;
+  // Many short segments on average: the lean short kernel (see
+  // seg_short_kernel).
+  const bool lean = n < kSegReg * nseg;
+  const void* sfn = lean ? (const void*)&seg_short_kernel<true>
+                         : (const void*)&seg_short_kernel<false>;
   const int64_t want = (nseg + kWaves - 1) / kWaves;
   const int64_t slots = (int64_t)resident_blocks(sfn) * cus;
   p.epoch = next_epoch(*sc.epochs);

@@ -17,17 +17,21 @@
 // gfx950 design.  The offsets live on the device, so the host cannot plan
 // per segment; two launches plan and work on the device instead:
 //  1. seg_short_kernel, one wave per segment (segments dealt to the waves
-//     in order).  A segment of at most kSegShort elements is read into the
+//     in order).  A segment of at most kSegReg elements is read into the
 //     wave's registers (V elements per lane, V picked by its length) and
-//     finished there by the short-row machinery of topk_rows_kernel.hpp.
-//     Longer segments are only listed: up to kSegWhole elements as
+//     finished there by the short-row machinery of topk_rows_kernel.hpp;
+//     so are segments up to kSegShort elements, unless the segments are
+//     many and short on average: then those are listed as "mid-length" for
+//     a wave of the next kernel each (see seg_short_kernel).  Longer
+//     segments are only listed: up to kSegWhole elements as
 //     "medium" (one workgroup will stream the whole segment), beyond that
 //     as "huge".  The last workgroup to finish (epoch-tagged ticket) cuts
 //     each huge segment into units of about kSegUnit elements (whole tiles,
 //     16-byte aligned from the second unit on, at most kMaxGrid of them)
 //     and writes the work plan.
-//  2. seg_long_kernel, persistent workgroups taking work items from an
-//     epoch-tagged counter: first the huge units, then the medium segments.
+//  2. seg_long_kernel, persistent workgroups: first the mid-length
+//     segments, one wave each, then work items from an epoch-tagged
+//     counter: the huge units, then the medium segments.
 //     A workgroup streams its item with the stage-1 machinery of
 //     topk_kernel (workgroup_topk).  A medium segment's top-k is its
 //     result.  A huge unit's top-k goes to scratch with its max and k-th;
@@ -46,6 +50,7 @@
 namespace ltk {
 
 constexpr int64_t kSegShort = 4096;         // one wave, in registers
+constexpr int64_t kSegReg = 1024;           // ... in seg_short_kernel<true>
 constexpr int64_t kSegWhole = 1 << 17;      // one workgroup, whole segment
 constexpr int64_t kSegUnit = 1 << 18;       // a huge segment's units
 constexpr int kSegStageMed = 64;            // per-wave LDS staging of the
@@ -67,7 +72,7 @@ struct SegPlan {   // written by seg_short_kernel's last workgroup
   int32_t m_med;   // medium segments listed
   int32_t units;   // units of the huge segments
   int32_t total;   // work items of seg_long_kernel: units + m_med
-  int32_t pad;
+  int32_t m_mid;   // mid-length segments listed (one wave each)
 };
 
 struct SegParams {
@@ -82,6 +87,8 @@ struct SegParams {
   int* counts;              // [nseg] or null
   int* med;                 // [med_cap] medium segment indices
   int med_cap;
+  int* mid;                 // [mid_cap] mid-length segment indices
+  int mid_cap;
   SegHuge* huge;            // [huge_cap]
   int huge_cap;
   SegUnit* units;           // [unit_cap]
@@ -89,7 +96,8 @@ struct SegParams {
   int* cand;                // [unit_cap * k] per unit: its top-k
   int* heads;               // [unit_cap] per unit: its max
   int* kths;                // [unit_cap] per unit: its k-th
-  uint64_t* ctr;            // [3] tagged with seg_tag: medium, huge, work
+  uint64_t* ctr;            // [4] tagged with seg_tag: medium, huge,
+                            // work, mid-length
   uint32_t seg_tag;         // this call's: one more than the previous
                             // segmented call's on the same scratch
   uint64_t* ticket;         // [1 + huge_cap]: seg_short_kernel's, then one
@@ -126,6 +134,28 @@ __device__ __forceinline__ void seg_short_topk(const int* src, int len,
   row_topk<V, false>(x, len, kk, dst, L);
 }
 
+// Issue the loads of a segment of at most 256 elements (four per lane,
+// clamped to the segment) without waiting for them: x holds the raw
+// values, to be masked (seg_mask4) where they are used.  Nothing is read
+// for an empty or longer segment.
+__device__ __forceinline__ void seg_prefetch4(const int* in, int64_t a,
+                                              int64_t b, int (&x)[4]) {
+  const int64_t len = b - a;
+  if (len > 0 && len <= 4 * kWave) {
+    const int nn = (int)len;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = lane() + kWave * j;
+      x[j] = __builtin_nontemporal_load(in + a + (idx < nn ? idx : nn - 1));
+    }
+  }
+}
+
+__device__ __forceinline__ void seg_mask4(int (&x)[4], int n) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = lane() + kWave * j < n ? x[j] : kI32Min;
+}
+
 typedef Tagged<32> SegCount;
 
 // Append a wave's n staged segment indices to a device list (entry i at
@@ -143,23 +173,46 @@ __device__ __forceinline__ void seg_flush(uint64_t* ctr, uint32_t tag,
   __builtin_amdgcn_wave_barrier();
 }
 
+// LEAN (chosen by the host for inputs of many short segments: an average
+// below kSegReg elements): segments of kSegReg .. kSegShort elements are
+// listed for seg_long_kernel instead of held in registers here, and this
+// kernel keeps a third of the registers, so that more waves hide the
+// memory latency of the many segments each one visits in turn (1e6
+// segments of 30 elements: 992 -> 567 us).  Otherwise every segment up to
+// kSegShort elements is finished here.
+template <bool LEAN>
 __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
   __shared__ RowsWaveLds lds[kWaves];
   __shared__ int mstage[kWaves][kSegStageMed];
   __shared__ int hstage[kWaves][kSegStageHuge];
+  __shared__ int dstage[kWaves][kSegStageMed];
   __shared__ int scan[kWaves];
-  __shared__ int staged[2][kWaves];
-  __shared__ uint64_t lbase[2];
+  __shared__ int staged[3][kWaves];
+  __shared__ uint64_t lbase[3];
   __shared__ int is_last;
   const int w = threadIdx.x / kWave;
   RowsWaveLds& L = lds[w];
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   const int k = p.k;
-  int mcnt = 0, hcnt = 0;  // staged medium and huge segments (uniform)
-  for (int64_t s = uni((int)(blockIdx.x * kWaves + w)); s < p.nseg;
-       s += nwaves) {
-    int64_t a, b;
-    seg_bounds(p, s, a, b);
+  // Staged medium, huge and mid-length segments (uniform).
+  int mcnt = 0, hcnt = 0, dcnt = 0;
+  // Software pipeline over the wave's segments s, s + W, s + 2W, ...: while
+  // segment s is worked on, the bounds of s + 2W and, when it has at most
+  // 256 elements, the data of s + W are in flight.  (One segment at a time,
+  // each paying its bounds' and its data's memory latency in turn, 1e6
+  // segments of 30 elements took 988 us.)
+  int64_t s = uni((int)(blockIdx.x * kWaves + w));
+  int64_t a0 = 0, b0 = 0, a1 = 0, b1 = 0;
+  if (s < p.nseg) seg_bounds(p, s, a0, b0);
+  if (s + nwaves < p.nseg) seg_bounds(p, s + nwaves, a1, b1);
+  int x0[4] = {kI32Min, kI32Min, kI32Min, kI32Min};
+  seg_prefetch4(p.in, a0, b0, x0);
+  for (; s < p.nseg; s += nwaves) {
+    int64_t a2 = 0, b2 = 0;
+    if (s + 2 * nwaves < p.nseg) seg_bounds(p, s + 2 * nwaves, a2, b2);
+    int x1[4] = {kI32Min, kI32Min, kI32Min, kI32Min};
+    seg_prefetch4(p.in, a1, b1, x1);
+    const int64_t a = a0, b = b0;
     const int64_t len = b - a;
     if (len > kSegShort) {
       // Listed in the wave's LDS stage; a full stage goes out at once.
@@ -177,52 +230,78 @@ __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
           mcnt = 0;
         }
       }
-      continue;
+    } else if (LEAN && len > kSegReg) {
+      // Mid-length: one wave of seg_long_kernel takes it (this kernel keeps
+      // the registers of segments up to kSegReg only, for occupancy).
+      if (lane() == 0) dstage[w][dcnt] = (int)s;
+      if (++dcnt == kSegStageMed) {
+        seg_flush(p.ctr + 3, p.seg_tag, dstage[w], dcnt, p.mid, 1, p.mid_cap);
+        dcnt = 0;
+      }
+    } else {
+      const int n = (int)len;
+      const int kk = n < k ? n : k;
+      int* dst = p.out + s * k;
+      if (n > 0) {
+        const int* src = p.in + a;
+        if (n <= 256) {
+          seg_mask4(x0, n);
+          if (LEAN && n <= kWave)
+            tiny_row_topk(x0[0], n, kk, dst);
+          else
+            row_topk<4, false>(x0, n, kk, dst, L);
+        } else if (n <= 512) {
+          seg_short_topk<8>(src, n, kk, dst, L);
+        } else if (LEAN || n <= 1024) {
+          seg_short_topk<16>(src, n, kk, dst, L);
+        } else if (n <= 2048) {
+          seg_short_topk<32>(src, n, kk, dst, L);
+        } else {
+          seg_short_topk<64>(src, n, kk, dst, L);
+        }
+      }
+      for (int i = kk + lane(); i < k; i += kWave) dst[i] = kI32Min;
+      if (p.counts && lane() == 0) p.counts[s] = kk;
     }
-    const int n = (int)len;
-    const int kk = n < k ? n : k;
-    int* dst = p.out + s * k;
-    if (n > 0) {
-      const int* src = p.in + a;
-      if (n <= 256)
-        seg_short_topk<4>(src, n, kk, dst, L);
-      else if (n <= 512)
-        seg_short_topk<8>(src, n, kk, dst, L);
-      else if (n <= 1024)
-        seg_short_topk<16>(src, n, kk, dst, L);
-      else if (n <= 2048)
-        seg_short_topk<32>(src, n, kk, dst, L);
-      else
-        seg_short_topk<64>(src, n, kk, dst, L);
-    }
-    for (int i = kk + lane(); i < k; i += kWave) dst[i] = kI32Min;
-    if (p.counts && lane() == 0) p.counts[s] = kk;
+    a0 = a1;
+    b0 = b1;
+    a1 = a2;
+    b1 = b2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x0[j] = x1[j];
   }
   // What the waves still hold goes out with one atomic per list for the
   // whole workgroup.
   if (lane() == 0) {
     staged[0][w] = mcnt;
     staged[1][w] = hcnt;
+    staged[2][w] = dcnt;
   }
   __syncthreads();
-  if (threadIdx.x < 2) {
+  if (threadIdx.x < 3) {
+    // List 0 counts in ctr[0], list 1 in ctr[1], list 2 in ctr[3].
+    const int l = threadIdx.x;
     int tot = 0;
-    for (int v = 0; v < kWaves; ++v) tot += staged[threadIdx.x][v];
-    lbase[threadIdx.x] =
-        tot ? SegCount::add(p.ctr + threadIdx.x, (uint64_t)tot, p.seg_tag) : 0;
+    for (int v = 0; v < kWaves; ++v) tot += staged[l][v];
+    lbase[l] = tot ? SegCount::add(p.ctr + (l == 2 ? 3 : l), (uint64_t)tot,
+                                   p.seg_tag)
+                   : 0;
   }
   __syncthreads();
   {
-    uint64_t mb = lbase[0], hb = lbase[1];
+    uint64_t mb = lbase[0], hb = lbase[1], db = lbase[2];
     for (int v = 0; v < w; ++v) {
       mb += staged[0][v];
       hb += staged[1][v];
+      db += staged[2][v];
     }
     for (int i = lane(); i < mcnt; i += kWave)
       if (mb + i < (uint64_t)p.med_cap) st_agent(p.med + mb + i, mstage[w][i]);
     for (int i = lane(); i < hcnt; i += kWave)
       if (hb + i < (uint64_t)p.huge_cap)
         st_agent(&p.huge[hb + i].seg, hstage[w][i]);
+    for (int i = lane(); i < dcnt; i += kWave)
+      if (db + i < (uint64_t)p.mid_cap) st_agent(p.mid + db + i, dstage[w][i]);
   }
 
   // ---- the last workgroup plans the long segments -----------------------
@@ -232,10 +311,13 @@ __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
                        (uint64_t)p.med_cap);
   int m_huge = (int)min(SegCount::count(ld_agent(p.ctr + 1), p.seg_tag),
                         (uint64_t)p.huge_cap);
+  const int m_mid = (int)min(SegCount::count(ld_agent(p.ctr + 3), p.seg_tag),
+                             (uint64_t)p.mid_cap);
   __syncthreads();  // every thread has read the counts
   if (tid == 0) {
     st_agent(p.ctr, SegCount::armed(p.seg_tag + 1u));
     st_agent(p.ctr + 1, SegCount::armed(p.seg_tag + 1u));
+    st_agent(p.ctr + 3, SegCount::armed(p.seg_tag + 1u));
   }
   // Units of each huge segment: c0 = ceil(len / kSegUnit) capped at
   // kMaxGrid, chunk = len / c0 rounded up to whole tiles.  Unit 0 starts
@@ -297,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
     pl.m_med = m_med;
     pl.units = base < p.unit_cap ? base : p.unit_cap;
     pl.total = pl.units + m_med;
-    pl.pad = 0;
+    pl.m_mid = m_mid;
     *p.plan = pl;
   }
 }
@@ -310,11 +392,35 @@ __global__ __launch_bounds__(kBlock) void seg_long_kernel(SegParams p) {
   static_assert(sizeof(ring_lds) >= sizeof(Stage2Lds), "ring too small");
   const SegPlan plan = *p.plan;
   const int k = p.k;
+  const int G = gridDim.x;
+  // Mid-length segments first, one wave each, in registers as in the short
+  // kernel; the ring's LDS holds the waves' candidate buffers meanwhile.
+  static_assert(sizeof(ring_lds) >= kWaves * sizeof(RowsWaveLds),
+                "ring holds the waves' buffers");
+  if (plan.m_mid > 0) {
+    RowsWaveLds* rl = reinterpret_cast<RowsWaveLds*>(&ring_lds[0][0][0][0]);
+    const int w = uni((int)(threadIdx.x / kWave));
+    for (int64_t i = (int64_t)blockIdx.x * kWaves + w; i < plan.m_mid;
+         i += (int64_t)G * kWaves) {
+      const int s = uni(p.mid[i]);
+      int64_t a, b;
+      seg_bounds(p, s, a, b);
+      const int n = uni((int)(b - a));  // in (kSegReg, kSegShort]
+      const int kk = n < k ? n : k;
+      int* dst = p.out + (int64_t)s * k;
+      if (n <= 2048)
+        seg_short_topk<32>(p.in + a, n, kk, dst, rl[w]);
+      else
+        seg_short_topk<64>(p.in + a, n, kk, dst, rl[w]);
+      for (int j = kk + lane(); j < k; j += kWave) dst[j] = kI32Min;
+      if (p.counts && lane() == 0) p.counts[s] = kk;
+    }
+    __syncthreads();  // the ring is the items' again
+  }
   // Work items: workgroup b starts with item b, then takes items G, G + 1,
   // ... from a counter (G = gridDim.x).  Every workgroup that started ends
   // with one grab past the end; the last grab of all arms the counter for
   // the next call.
-  const int G = gridDim.x;
   const int64_t started = min((int64_t)G, (int64_t)plan.total);
   const uint64_t grabs =
       (uint64_t)(plan.total > G ? plan.total - G : 0) + (uint64_t)started;

