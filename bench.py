@@ -257,8 +257,8 @@ PATHS = {
         "calls": [("seg20", "segmented", 20)],
         # One call is two launches; summaries and traffic are per call.
         "groups": [("ltk::seg_long_kernel<", ["seg20"])],
-        "call_kernels": ["ltk::seg_short_kernel(", "ltk::seg_long_kernel<"],
-        "once_per_call": "ltk::seg_short_kernel(",
+        "call_kernels": ["ltk::seg_short_kernel<", "ltk::seg_long_kernel<"],
+        "once_per_call": "ltk::seg_short_kernel<",
         "launches_per_call": 2,
         "sources": ["wave.hpp", "topk_kernel.hpp", "topk_rows_kernel.hpp",
                     "seg_kernel.hpp", "libtopk.hip"],
