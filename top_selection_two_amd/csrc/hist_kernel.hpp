@@ -178,6 +178,8 @@ __global__ __launch_bounds__(kBlock) void hist_kernel(HistParams p) {
   // one vector slot all share a bin adds 256 with one atomic (a histogram
   // of 1e8 equal values, or of values that all fall into one bin, took
   // 333 us with an atomic per element, against 61 us for spread values).
+  // The check costs spread values about 2 % (60.7 -> 62.0 us); checking
+  // only every 16th slot until one passes cost more (63.5 us).
   for_each_vector<U>(
       p.in, p.n, p.head, p.ntiles, p.covered, p.grid, (int)blockIdx.x,
       [&](const v4i& v) __attribute__((always_inline)) {
