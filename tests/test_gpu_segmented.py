@@ -96,6 +96,9 @@ def test_many_short_segments(k):
     assert x.size < 1024 * lengths.size  # the lean kernel
     print("many short k=%d nseg=%d n=%d" % (k, lengths.size, x.size), flush=True)
     check(x, offsets, k)
+    # ties: few distinct values, and one value throughout
+    check(synth.fill(60 + k, x.size, 0, 7), offsets, k)
+    check(np.full(x.size, -5, np.int32), offsets, k, with_counts=False)
 
 
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
