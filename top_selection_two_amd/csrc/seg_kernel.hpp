@@ -175,11 +175,13 @@ __device__ __forceinline__ void seg_flush(uint64_t* ctr, uint32_t tag,
 
 // LEAN (chosen by the host for inputs of many short segments: an average
 // below kSegReg elements): segments of kSegReg .. kSegShort elements are
-// listed for seg_long_kernel instead of held in registers here, and this
-// kernel keeps a third of the registers, so that more waves hide the
-// memory latency of the many segments each one visits in turn (1e6
-// segments of 30 elements: 992 -> 567 us).  Otherwise every segment up to
-// kSegShort elements is finished here.
+// listed for seg_long_kernel instead of held in registers here, so this
+// kernel needs less than half the registers and runs 5 waves per SIMD
+// instead of 2, which hide the memory latency of the many segments each
+// wave visits in turn; segments of at most 64 elements are sorted across
+// the wave directly (1e6 segments of 30 elements: 992 us, 567 with the
+// lean instance, 404 with the direct sort).  Otherwise every segment up
+// to kSegShort elements is finished here.
 template <bool LEAN>
 __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
   __shared__ RowsWaveLds lds[kWaves];
@@ -198,9 +200,7 @@ __global__ __launch_bounds__(kBlock) void seg_short_kernel(SegParams p) {
   int mcnt = 0, hcnt = 0, dcnt = 0;
   // Software pipeline over the wave's segments s, s + W, s + 2W, ...: while
   // segment s is worked on, the bounds of s + 2W and, when it has at most
-  // 256 elements, the data of s + W are in flight.  (One segment at a time,
-  // each paying its bounds' and its data's memory latency in turn, 1e6
-  // segments of 30 elements took 988 us.)
+  // 256 elements, the data of s + W are in flight.
   int64_t s = uni((int)(blockIdx.x * kWaves + w));
   int64_t a0 = 0, b0 = 0, a1 = 0, b1 = 0;
   if (s < p.nseg) seg_bounds(p, s, a0, b0);
