@@ -681,13 +681,13 @@ __device__ __forceinline__ void topk_kv_stage2(const TopkKvParams& p,
     // position, and the groups are runs of consecutive blocks, whose first
     // tiles are early in the row.  (Key-value top-32 of 1e7 values in
     // [0, 1000): the 32nd largest of 64 group maxima left 1,025 survivors
-    // and the selection by counting over memory took 240 us.)  The k-th
-    // largest of all G block maxima, each a candidate, is certified too
-    // and much tighter: gather again with it.
-    // Wave 0 holds the G maxima, 16 per lane, and selects the k-th largest
-    // key by ballots: its high word from that of T2a upwards (the group
-    // maxima are block maxima, so at least k of those reach T2a), then its
-    // low word among the maxima with that high word.
+    // and the selection by counting over memory took 240 us.)  A tighter
+    // certified bound from the lists' first keys (below), then gather again
+    // with it.  Over 256 blocks, the k-th largest of all G block maxima,
+    // each a candidate: wave 0 holds the G maxima, 16 per lane, and selects
+    // the k-th largest key by ballots: its high word from that of T2a
+    // upwards (the group maxima are block maxima, so at least k of those
+    // reach T2a), then its low word among the maxima with that high word.
     const uint64_t t2a = sh.bkey[1];
     __syncthreads();  // every survivor count and bound has been read
     const int jl = min(k, 2 * kBlock / G);  // list entries that fit a ranking
