@@ -86,6 +86,25 @@ __device__ __forceinline__ void wave_rank_out(int* buf, int m, int k,
   }
 }
 
+// Sort buf[0..m) (m <= 64 R) descending across the wave, R values per
+// lane, and write the first k to out.
+template <int R>
+__device__ __forceinline__ void sort_out(const int* buf, int m, int k,
+                                         int* out) {
+  int v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = j * kWave + lane();
+    v[j] = i < m ? buf[i] : kI32Min;
+  }
+  wave_sort_desc_regs<R>(v);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int i = j * kWave + lane();
+    if (i < k) out[i] = v[j];
+  }
+}
+
 // Append the elements that pass (x[j] > t, or >= t) to buf, one ballot per
 // register slot, at offsets from a wave-uniform count; nothing is kept
 // past kRowCap.  Every lane stores in every slot, with no branch: a lane
@@ -186,9 +205,18 @@ __device__ __forceinline__ void row_topk(const int (&x)[V], int n, int k,
     // The bound is the row maximum: at least k elements equal it, and they
     // are the result (a row of ties would otherwise rank all of them).
     for (int j = lane(); j < k; j += kWave) out[j] = hi;
-  } else if (m <= kRowCap) {
-    // 4'. Up to kRowCap candidates: rank by counting.
-    wave_rank_out(L.buf, m, k, out);
+  } else if (m <= 4 * kWave) {
+    // 4'. Up to 256 candidates: two or four per lane, sorted across the
+    // wave by a bitonic network (ranking them by counting took O(m^2):
+    // 100,000 rows of 100, top-64, 89 us).
+    // Rows of up to 512 elements, where k is often large for the row,
+    // carry a network for up to 128 too; longer rows one network only (a
+    // second made the common path of 97,656 rows of 1,024 about 1 %
+    // slower: longer code).
+    if (V <= 8 && m <= 2 * kWave)
+      sort_out<2>(L.buf, m, k, out);
+    else
+      sort_out<4>(L.buf, m, k, out);
   } else {
     // Exact path: the k-th largest g by radix selection over the row, the
     // elements above g (fewer than k) ranked, then copies of g.

@@ -531,4 +531,36 @@ __device__ __forceinline__ int wave_sort_desc(int v) {
   return bitonic_sort<2, W>(v);
 }
 
+// Bitonic sort of 64 R values held R per lane (value j * 64 + lane in
+// v[j]), descending: runs of one register sorted across the lanes in
+// alternating directions (ascending as the complement of a descending
+// sort: ~x reverses the order of int32 with no overflow), then each
+// longer run merged by compare-exchanges between registers (partners 64
+// and more apart) and lane exchanges (32 .. 1).  Afterwards v[0] holds the
+// 64 largest, lane 0 the largest of all.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc_regs(int (&v)[R]) {
+  static_assert(R >= 1 && (R & (R - 1)) == 0, "R a power of two");
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    v[j] = (j & 1) ? ~wave_sort_desc<kWave>(~v[j]) : wave_sort_desc<kWave>(v[j]);
+#pragma unroll
+  for (int size = 2; size <= R; size <<= 1) {  // runs of `size` registers
+#pragma unroll
+    for (int js = size / 2; js >= 1; js >>= 1) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if ((j & js) == 0) {
+          const bool desc = (j & size) == 0;
+          const int a = v[j], b = v[j | js];
+          v[j] = desc ? max(a, b) : min(a, b);
+          v[j | js] = desc ? min(a, b) : max(a, b);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = merge_dir<32>(v[j], (j & size) == 0);
+  }
+}
+
 }  // namespace ltk
